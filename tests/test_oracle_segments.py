@@ -1,0 +1,82 @@
+"""Pins for the oracle's segment table (Ascend walkthrough, section 2.3).
+
+The oracle sorts with numpy's stable argsort; these tests pin it against a
+hand-worked fixture, a second definition built from Python dict grouping,
+brute force over every id map of small size, and invariants.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import lora as O
+
+
+def grouping_definition(ids, L):
+    """Independent definition: collect token lists per valid id in a dict,
+    concatenate them by ascending id, then the tokens with no adapter."""
+    groups = {}
+    rest = []
+    for m, v in enumerate(ids):
+        if 0 <= v < L:
+            groups.setdefault(v, []).append(m)
+        else:
+            rest.append(m)
+    keys = sorted(groups)
+    sorted_idx = [m for k in keys for m in groups[k]] + rest
+    seg = [0]
+    for k in keys:
+        seg.append(seg[-1] + len(groups[k]))
+    seg += [seg[-1]] * (L + 1 - len(seg))
+    req = keys + [-1] * (L - len(keys))
+    return sorted_idx, seg, req, len(keys)
+
+
+@pytest.mark.parametrize("name", ["segments_example.json", "decode_example_small.json"])
+def test_golden(golden, name):
+    g = golden(name)
+    si, seg, req, n = O.build_segments(g["ids"], g["L"])
+    assert si.tolist() == g["sorted_idx"]
+    assert seg.tolist() == g["seg_indptr"]
+    assert req.tolist() == g["req_to_lora"]
+    assert n == g["num_segments"]
+
+
+@pytest.mark.parametrize("L", [1, 2, 3])
+@pytest.mark.parametrize("M", [0, 1, 2, 3, 4])
+def test_brute_force_all_maps(M, L):
+    # every map over {-1, 0..L-1} plus one out-of-range id (treated as -1)
+    values = list(range(-1, L)) + [L]
+    for ids in itertools.product(values, repeat=M):
+        ids = list(ids)
+        si, seg, req, n = O.build_segments(np.array(ids, np.int32), L)
+        e_si, e_seg, e_req, e_n = grouping_definition(ids, L)
+        assert si.tolist() == e_si, ids
+        assert seg.tolist() == e_seg, ids
+        assert req.tolist() == e_req, ids
+        assert n == e_n
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(1, 64))
+    M = int(rng.integers(0, 3000))
+    ids = rng.integers(-1, L, size=M).astype(np.int32)
+    si, seg, req, n = O.build_segments(ids, L)
+    # permutation
+    assert sorted(si.tolist()) == list(range(M))
+    hist = np.bincount(ids[ids >= 0], minlength=L)
+    assert n == int(np.count_nonzero(hist))
+    # req_to_lora strictly increasing; segment sizes equal the histogram
+    assert all(req[s] < req[s + 1] for s in range(n - 1))
+    for s in range(n):
+        a, b = seg[s], seg[s + 1]
+        assert b - a == hist[req[s]]
+        assert np.all(ids[si[a:b]] == req[s])
+        assert np.all(np.diff(si[a:b]) > 0)        # stable
+    mv = int(np.count_nonzero(ids >= 0))
+    assert np.all(seg[n:] == mv)
+    assert np.all(req[n:] == -1)
+    assert np.all(ids[si[mv:]] < 0)
+    assert np.all(np.diff(si[mv:]) > 0)
