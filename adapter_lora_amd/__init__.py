@@ -1,0 +1,304 @@
+"""Python binding of libmlora (dynamic multi-LoRA on MI355X / gfx950).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the path runs in the library's kernels.
+The names match the C ABI in include/mlora.h.  There is no fallback: if the
+library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+from ._abi import (LORA_BF16, LORA_F32, LORA_MAX_ADAPTERS, LORA_MAX_RANK,
+                   LORA_MAX_SLICES, LORA_DECODE_MAX_M, LoraError, lib, lora_weights_t,
+                   lora_segments_t, lora_moe_weights_t, lora_moe_align_t, check)
+
+__all__ = [
+    "LORA_BF16", "LORA_F32", "LoraError", "LoraTable", "Segments", "Workspace",
+    "MoeWeights", "MoeAlign",
+    "lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
+    "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
+    "lora_table_plan", "lora_pack_adapter",
+    "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
+    "lora_moe_gate_up_add", "lora_moe_silu_and_mul", "lora_moe_down_add",
+    "lora_moe_topk_reduce", "stream_handle",
+]
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return LORA_BF16
+    if t == torch.float32:
+        return LORA_F32
+    raise LoraError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a row-major 2-D device tensor."""
+    if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+        raise LoraError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise LoraError(f"{name} must live on the GPU")
+    return max(t.stride(0), t.shape[1])
+
+
+# ------------------------------------------------------------------------- table
+def lora_table_plan(ranks: Sequence[int], n_slices: int, K: int, N_total: int):
+    L = len(ranks)
+    r = (ctypes.c_int32 * L)(*ranks)
+    rp = (ctypes.c_int32 * L)()
+    ao = (ctypes.c_int64 * L)()
+    bo = (ctypes.c_int64 * L)()
+    na, nb = ctypes.c_int64(), ctypes.c_int64()
+    check(lib.lora_table_plan(L, r, n_slices, K, N_total, rp, ao, bo, ctypes.byref(na),
+                              ctypes.byref(nb)), "lora_table_plan")
+    return list(rp), list(ao), list(bo), na.value, nb.value
+
+
+def lora_pack_adapter(A_src: torch.Tensor, B_src: torch.Tensor, K: int, N_total: int,
+                      n_slices: int, rank: int, rank_pad: int, A_dst: torch.Tensor,
+                      B_dst: torch.Tensor, stream=None) -> None:
+    check(lib.lora_pack_adapter(_dtype_code(A_src.dtype), K, N_total, n_slices, rank, rank_pad,
+                                _ptr(A_src), _ptr(B_src), _ptr(A_dst), _ptr(B_dst),
+                                stream_handle(stream)), "lora_pack_adapter")
+
+
+class LoraTable:
+    """Rank-grouped packed adapter table on the device (load time).
+
+    A[i]: [n_slices * r_i, K] (slice s = rows [s*r_i, (s+1)*r_i)),
+    B[i]: [N_total, r_i]; rank 0 (or None) marks an empty slot.
+    """
+
+    def __init__(self, A: Sequence[Optional[torch.Tensor]], B: Sequence[Optional[torch.Tensor]],
+                 ranks: Sequence[int], slice_sizes: Sequence[int], K: int,
+                 dtype: torch.dtype, device="cuda", stream=None):
+        self.L = len(ranks)
+        if not (1 <= self.L <= LORA_MAX_ADAPTERS):
+            raise LoraError("adapter count out of range")
+        if not (1 <= len(slice_sizes) <= LORA_MAX_SLICES):
+            raise LoraError("slice count out of range")
+        self.K = int(K)
+        self.n_slices = len(slice_sizes)
+        self.slice_sizes = [int(n) for n in slice_sizes]
+        self.N = int(sum(self.slice_sizes))
+        self.dtype = dtype
+        self.ranks = [int(r) for r in ranks]
+        rp, ao, bo, na, nb = lora_table_plan(self.ranks, self.n_slices, self.K, self.N)
+        self.rank_pad = rp
+        self.r_max = max([16] + rp)
+        self.A_table = torch.zeros(max(na, 8), dtype=dtype, device=device)
+        self.B_table = torch.zeros(max(nb, 8), dtype=dtype, device=device)
+        for i, r in enumerate(self.ranks):
+            if r == 0:
+                continue
+            a = A[i].to(device=device, dtype=dtype).contiguous()
+            b = B[i].to(device=device, dtype=dtype).contiguous()
+            if tuple(a.shape) != (self.n_slices * r, self.K) or tuple(b.shape) != (self.N, r):
+                raise LoraError(f"adapter {i}: bad A/B shape {tuple(a.shape)} {tuple(b.shape)}")
+            lora_pack_adapter(a, b, self.K, self.N, self.n_slices, r, rp[i],
+                              self.A_table[ao[i]:], self.B_table[bo[i]:], stream)
+        self.a_off = torch.tensor(ao, dtype=torch.int64, device=device)
+        self.b_off = torch.tensor(bo, dtype=torch.int64, device=device)
+        self.rank_dev = torch.tensor(rp, dtype=torch.int32, device=device)
+        off = [0]
+        for n in self.slice_sizes:
+            off.append(off[-1] + n)
+        so = (ctypes.c_int64 * (LORA_MAX_SLICES + 1))(*(off + [0] * (LORA_MAX_SLICES + 1 - len(off))))
+        self.c = lora_weights_t(_dtype_code(dtype), self.K, self.n_slices, self.L, self.r_max, 0,
+                                so, _ptr(self.A_table), _ptr(self.B_table),
+                                ctypes.cast(_ptr(self.a_off), ctypes.POINTER(ctypes.c_int64)),
+                                ctypes.cast(_ptr(self.b_off), ctypes.POINTER(ctypes.c_int64)),
+                                ctypes.cast(_ptr(self.rank_dev), ctypes.POINTER(ctypes.c_int32)))
+
+    @property
+    def cols(self) -> int:
+        return self.n_slices * self.r_max
+
+
+# ------------------------------------------------------------------------- segments
+class Segments:
+    """Device buffers of a segment table for up to M_cap tokens and L slots."""
+
+    def __init__(self, M_cap: int, L: int, device="cuda"):
+        self.L = int(L)
+        self.sorted_idx = torch.empty(max(M_cap, 1), dtype=torch.int32, device=device)
+        self.seg_indptr = torch.empty(L + 1, dtype=torch.int32, device=device)
+        self.req_to_lora = torch.empty(L, dtype=torch.int32, device=device)
+        self.num_segments = torch.empty(1, dtype=torch.int32, device=device)
+        self.c = lora_segments_t(
+            *(ctypes.cast(_ptr(t), ctypes.POINTER(ctypes.c_int32))
+              for t in (self.sorted_idx, self.seg_indptr, self.req_to_lora, self.num_segments)),
+            self.L, 0)
+
+
+def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None) -> None:
+    if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1:
+        raise LoraError("ids must be a 1-D int32 device tensor")
+    M = ids.shape[0]
+    if M > seg.sorted_idx.shape[0]:
+        raise LoraError("segment buffers too small")
+    check(lib.lora_build_segments(_ptr(ids), M, seg.L, _ptr(seg.sorted_idx), _ptr(seg.seg_indptr),
+                                  _ptr(seg.req_to_lora), _ptr(seg.num_segments),
+                                  stream_handle(stream)), "lora_build_segments")
+
+
+# ------------------------------------------------------------------------- workspace
+def lora_workspace_size(table: LoraTable, M: int) -> int:
+    return int(lib.lora_workspace_size(ctypes.byref(table.c), M))
+
+
+def lora_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    check(lib.lora_workspace_init(_ptr(ws), ws.numel(), stream_handle(stream)),
+          "lora_workspace_init")
+
+
+def lora_read_device_error(ws: torch.Tensor, stream=None) -> int:
+    out = ctypes.c_int32()
+    check(lib.lora_read_device_error(_ptr(ws), ctypes.byref(out), stream_handle(stream)),
+          "lora_read_device_error")
+    return out.value
+
+
+class Workspace:
+    """Zero-initialised device workspace (uint8) for a table and up to M tokens."""
+
+    def __init__(self, nbytes: int, device="cuda", stream=None):
+        self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        lora_workspace_init(self.buf, stream)
+
+    @classmethod
+    def for_table(cls, table: LoraTable, M: int, device="cuda", stream=None):
+        return cls(lora_workspace_size(table, M), device, stream)
+
+
+# ------------------------------------------------------------------------- dense calls
+def lora_shrink(table: LoraTable, x: torch.Tensor, seg: Segments, S: torch.Tensor,
+                ws: Workspace, stream=None) -> None:
+    ldx = _rows(x, "x")
+    if S.dtype != torch.float32 or not S.is_contiguous() or S.numel() < x.shape[0] * table.cols:
+        raise LoraError("S must be a contiguous fp32 [M, n_slices, r_max] tensor")
+    check(lib.lora_shrink(ctypes.byref(table.c), _ptr(x), ldx, x.shape[0], ctypes.byref(seg.c),
+                          _ptr(S), _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
+          "lora_shrink")
+
+
+def lora_expand_add(table: LoraTable, S: torch.Tensor, seg: Segments, y: torch.Tensor,
+                    stream=None) -> None:
+    ldy = _rows(y, "y")
+    if S.dtype != torch.float32 or not S.is_contiguous():
+        raise LoraError("S must be a contiguous fp32 tensor")
+    check(lib.lora_expand_add(ctypes.byref(table.c), _ptr(S), y.shape[0], ctypes.byref(seg.c),
+                              _ptr(y), ldy, stream_handle(stream)), "lora_expand_add")
+
+
+def lora_shrink_expand_add(table: LoraTable, x: torch.Tensor, seg: Segments, y: torch.Tensor,
+                           ws: Workspace, stream=None) -> None:
+    ldx, ldy = _rows(x, "x"), _rows(y, "y")
+    if x.shape[0] != y.shape[0]:
+        raise LoraError("x and y must have the same number of rows")
+    check(lib.lora_shrink_expand_add(ctypes.byref(table.c), _ptr(x), ldx, x.shape[0],
+                                     ctypes.byref(seg.c), _ptr(y), ldy, _ptr(ws.buf),
+                                     ws.buf.numel(), stream_handle(stream)),
+          "lora_shrink_expand_add")
+
+
+# ------------------------------------------------------------------------- MoE
+class MoeWeights:
+    """Dense per-expert LoRA stacks [L, E, r, H] / [L, E, 2I, r] / [L, E, r, I] / [L, E, H, r]."""
+
+    def __init__(self, A_gu, B_gu, A_d, B_d, adapter_enabled):
+        self.A_gu, self.B_gu = A_gu.contiguous(), B_gu.contiguous()
+        self.A_d, self.B_d = A_d.contiguous(), B_d.contiguous()
+        self.enabled = adapter_enabled.to(torch.int32).contiguous()
+        L, E, r, H = self.A_gu.shape
+        I = self.A_d.shape[3]
+        if tuple(self.B_gu.shape) != (L, E, 2 * I, r) or tuple(self.A_d.shape) != (L, E, r, I) \
+                or tuple(self.B_d.shape) != (L, E, H, r):
+            raise LoraError("inconsistent MoE LoRA shapes")
+        self.L, self.E, self.r, self.H, self.I = L, E, r, H, I
+        self.dtype = self.A_gu.dtype
+        self.c = lora_moe_weights_t(_dtype_code(self.dtype), L, E, H, I, r, _ptr(self.A_gu),
+                                    _ptr(self.B_gu), _ptr(self.A_d), _ptr(self.B_d),
+                                    ctypes.cast(_ptr(self.enabled), ctypes.POINTER(ctypes.c_int32)))
+
+
+def lora_moe_align_capacity(M: int, topk: int, E: int, block_size_m: int) -> int:
+    return int(lib.lora_moe_align_capacity(M, topk, E, block_size_m))
+
+
+class MoeAlign:
+    def __init__(self, L: int, max_tokens_padded: int, block_size_m: int, device="cuda"):
+        self.sorted_token_ids = torch.empty(L * max_tokens_padded, dtype=torch.int32, device=device)
+        self.expert_ids = torch.empty(L * (max_tokens_padded // block_size_m), dtype=torch.int32,
+                                      device=device)
+        self.ntpp = torch.empty(L, dtype=torch.int32, device=device)
+        self.L = L
+        self.max_tokens_padded = max_tokens_padded
+        self.block_size_m = block_size_m
+        self.c = lora_moe_align_t(
+            ctypes.cast(_ptr(self.sorted_token_ids), ctypes.POINTER(ctypes.c_int32)),
+            ctypes.cast(_ptr(self.expert_ids), ctypes.POINTER(ctypes.c_int32)),
+            ctypes.cast(_ptr(self.ntpp), ctypes.POINTER(ctypes.c_int32)),
+            max_tokens_padded, block_size_m)
+
+
+def lora_moe_align_run(topk_ids: torch.Tensor, ids: torch.Tensor, adapter_enabled: torch.Tensor,
+                       E: int, out: MoeAlign, stream=None) -> None:
+    M, topk = topk_ids.shape
+    for t, n in ((topk_ids, "topk_ids"), (ids, "ids"), (adapter_enabled, "adapter_enabled")):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise LoraError(f"{n} must be a contiguous int32 device tensor")
+    check(lib.lora_moe_align_run(_ptr(topk_ids), _ptr(ids), _ptr(adapter_enabled), M, topk, E,
+                                 out.L, ctypes.byref(out.c), stream_handle(stream)),
+          "lora_moe_align_run")
+
+
+def lora_moe_workspace_size(w: MoeWeights, max_tokens_padded: int) -> int:
+    return int(lib.lora_moe_workspace_size(ctypes.byref(w.c), max_tokens_padded))
+
+
+def lora_moe_gate_up_add(w: MoeWeights, x: torch.Tensor, topk: int, align: MoeAlign,
+                         cache1: torch.Tensor, ws: Workspace, stream=None) -> None:
+    check(lib.lora_moe_gate_up_add(ctypes.byref(w.c), _ptr(x), _rows(x, "x"), x.shape[0], topk,
+                                   ctypes.byref(align.c), _ptr(cache1), _rows(cache1, "cache1"),
+                                   _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
+          "lora_moe_gate_up_add")
+
+
+def lora_moe_silu_and_mul(cache1: torch.Tensor, cache2: torch.Tensor, stream=None) -> None:
+    P, I = cache2.shape
+    check(lib.lora_moe_silu_and_mul(_dtype_code(cache1.dtype), _ptr(cache1), _rows(cache1, "cache1"),
+                                    _ptr(cache2), _rows(cache2, "cache2"), P, I,
+                                    stream_handle(stream)), "lora_moe_silu_and_mul")
+
+
+def lora_moe_down_add(w: MoeWeights, cache2: torch.Tensor, M: int, topk: int, align: MoeAlign,
+                      cache3: torch.Tensor, ws: Workspace, stream=None) -> None:
+    check(lib.lora_moe_down_add(ctypes.byref(w.c), _ptr(cache2), _rows(cache2, "cache2"), M, topk,
+                                ctypes.byref(align.c), _ptr(cache3), _rows(cache3, "cache3"),
+                                _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
+          "lora_moe_down_add")
+
+
+def lora_moe_topk_reduce(cache3: torch.Tensor, topk_weights: torch.Tensor, out: torch.Tensor,
+                         stream=None) -> None:
+    M, topk = topk_weights.shape
+    if topk_weights.dtype != torch.float32 or not topk_weights.is_contiguous():
+        raise LoraError("topk_weights must be contiguous fp32")
+    check(lib.lora_moe_topk_reduce(_dtype_code(cache3.dtype), _ptr(cache3), _rows(cache3, "cache3"),
+                                   _ptr(topk_weights), _ptr(out), _rows(out, "out"), M, topk,
+                                   out.shape[1], stream_handle(stream)), "lora_moe_topk_reduce")

@@ -1,0 +1,121 @@
+// Device helpers shared by the gfx950 kernels: storage conversion, 16-byte
+// vector loads, wavefront reductions, and the tagged fp32 exchange slots
+// through which workgroups of one launch hand partial sums to each other.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlora {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------
+// storage types: float (fp32) and uint16_t holding bfloat16 bits
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even.  NaNs stay NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <typename T> struct Io;
+
+template <> struct Io<float> {
+    static constexpr int kPer16B = 4;
+    __device__ static float ld(const float* p) { return *p; }
+    __device__ static void st(float* p, float v) { *p = v; }
+    // 8 consecutive elements -> floats
+    __device__ static void ld8(const float* p, float* o) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+
+template <> struct Io<uint16_t> {
+    static constexpr int kPer16B = 8;
+    __device__ static float ld(const uint16_t* p) { return bf16_to_f32(*p); }
+    __device__ static void st(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16(v); }
+    __device__ static void ld8(const uint16_t* p, float* o) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------
+// wavefront reductions
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// ----------------------------------------------------------------------------
+// tagged exchange slots
+//
+// A slot is one 64-bit word {fp32 value (low), tag (high)} written and read
+// with single 64-bit relaxed atomics at agent scope, so the value and its tag
+// always travel together: no fence is needed to order data before a flag.
+// Tag 1 = full, 0 = empty.  The consumer that reads a group of slots last
+// (decided by a per-group counter) empties them again, so a workspace stays
+// ready for the next launch.
+// ----------------------------------------------------------------------------
+typedef unsigned long long slot_t;
+
+__device__ __forceinline__ void slot_put(slot_t* s, float v) {
+    const slot_t w = (1ull << 32) | (slot_t)__float_as_uint(v);
+    __hip_atomic_store(s, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void slot_clear(slot_t* s) {
+    __hip_atomic_store(s, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until the slot is full.  Gives up after `max_spin` polls (then
+// returns false and the caller reports a device error): every wave exits.
+__device__ __forceinline__ bool slot_get(const slot_t* s, float* out, int max_spin) {
+    for (int i = 0;; ++i) {
+        const slot_t w = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == 1u) {
+            *out = __uint_as_float((uint32_t)w);
+            return true;
+        }
+        if (i >= max_spin) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+__device__ __forceinline__ int atomic_add_agent(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workspace header shared by every kernel that uses a workspace.
+struct WsHeader {
+    int error;        // sticky error bits (bit 0: gave up waiting)
+    int pad[63];      // keeps counters that follow on their own 256-byte line
+};
+
+constexpr int kErrSpin = 1;
+constexpr int kMaxSpin = 1 << 20;
+
+}  // namespace mlora

@@ -1,0 +1,450 @@
+// Fused decode: y[m] += (x[m] A_i^T) B_i^T for a small batch (M <= 64) in a
+// single launch ("vLLM-Ascend dynamic LoRA operator" walkthrough: section 2.1
+// fused operator — look up A/B by id, two low-rank products, add to the base
+// rows; section 2.2 — S accumulated in fp32; section 1.2 — at decode every
+// token may use a different adapter, so the work is a gather-GEMV whose cost
+// is reading each touched adapter's A and B once).
+//
+// The launch has two groups of workgroups:
+//   producers  (blockIdx <  grid1): unit = (segment, 16 rows of A, 512-wide K
+//              chunk).  Lanes stream one row of A chunk each 1 KB at a time
+//              (coalesced 16-byte loads), dot it with the segment's token rows
+//              and reduce across the wavefront.  Each partial sum goes into a
+//              tagged 64-bit exchange slot.
+//   consumers  (blockIdx >= grid1): unit = (segment, 256 output columns of a
+//              slice).  They first issue the loads of their B tile (coalesced:
+//              consecutive lanes read consecutive 16-byte chunks of the
+//              row-major [N, rp] block) and only then wait for the segment's
+//              slots, sum the K chunks in a fixed order into LDS (S stays on
+//              chip), and finish with a lane-group reduce-scatter so that each
+//              lane ends up owning one output column for the read-modify-write
+//              of y.
+// Consumers only wait on producers, which never wait, and producers have the
+// lower workgroup ids, so they are dispatched first; every wait is also
+// bounded (kMaxSpin) and reports a device error instead of hanging.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mlora {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / kWave;
+
+struct DecodeParams {
+    LinearArgs a;
+    const void* x;
+    int64_t ldx;
+    void* y;
+    int64_t ldy;
+    int* err;
+    int* counters;     // [s_max][n_sl]
+    slot_t* slots;     // [C][M][cols]
+    int C;
+    int jb_max;        // n_sl * r_max / 16
+    int grid1;
+    int n_tiles;
+    int tile_start[LORA_MAX_SLICES + 1];
+};
+
+// ---------------------------------------------------------------- shared view
+// Everything a workgroup needs to know about segment s, fetched with
+// independent loads so that the index lookups cost one memory round trip:
+// the segment bounds, its adapter id, the whole sorted token list (M <= 64,
+// one entry per lane) and, for tables of up to 256 slots, every slot's rank
+// and weight offset (picked by lane shuffle once the id is known).
+struct SegView {
+    int nseg, id, rp, p0, ms, my_idx;
+    int64_t off;
+};
+
+__device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a_side) {
+    const LinearArgs& a = p.a;
+    const int lane = lane_id();
+    const int64_t* offs = a_side ? a.a_off : a.b_off;
+    SegView v;
+    v.nseg = a.num_segments[0];
+    v.id = a.req_to_lora[s];
+    v.p0 = a.seg_indptr[s];
+    const int p1 = a.seg_indptr[s + 1];
+    v.my_idx = lane < a.M ? a.sorted_idx[lane] : 0;
+    if (a.L <= 4 * kWave) {
+        int rk[4];
+        int64_t of[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = q * kWave + lane;
+            rk[q] = j < a.L ? a.rank[j] : 0;
+            of[q] = j < a.L ? offs[j] : 0;
+        }
+        const int id = v.id < 0 ? 0 : v.id;
+        const int q = id / kWave, src = id % kWave;
+        const int r_sel = q == 0 ? rk[0] : q == 1 ? rk[1] : q == 2 ? rk[2] : rk[3];
+        const int64_t o_sel = q == 0 ? of[0] : q == 1 ? of[1] : q == 2 ? of[2] : of[3];
+        v.rp = __shfl(r_sel, src, kWave);
+        v.off = __shfl(o_sel, src, kWave);
+    } else {
+        const int id = v.id < 0 ? 0 : v.id;
+        v.rp = a.rank[id];
+        v.off = offs[id];
+    }
+    v.ms = p1 - v.p0;
+    return v;
+}
+
+// Reduce-scatter of N partials over groups of N lanes (N a power of two):
+// afterwards v[0] on the lane with (lane % N) == g holds the group's sum of
+// partial index g.
+template <int N>
+__device__ __forceinline__ void reduce_scatter(float* v, int g) {
+#pragma unroll
+    for (int h = N / 2; h >= 1; h /= 2) {
+        const bool upper = (g & h) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const float send = upper ? v[i] : v[i + h];
+            const float keep = upper ? v[i + h] : v[i];
+            v[i] = keep + __shfl_xor(send, h, kWave);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- producers
+// Unit = (segment, 16 rows of A, K chunk of 512 x dec_steps values).  Wave w owns rows
+// 4w..4w+3; per step a lane loads 8 consecutive K values of each row (one
+// 16-byte load, 1 KB contiguous per row and wave) and of each token row, and
+// accumulates row x token partial dot products in fp32.  One wavefront
+// reduction per (row, token) at the end.
+constexpr int kTokGroup = 4;                    // token rows accumulated together
+
+// 8 consecutive elements kept in their storage form (one or two 16-byte words)
+template <typename T> struct Raw8 { uint4 q[sizeof(T) / 2]; };
+
+template <typename T>
+__device__ __forceinline__ Raw8<T> ld_raw8(const T* p) {
+    Raw8<T> r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.q[i] = reinterpret_cast<const uint4*>(p)[i];
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void raw_to_f(const Raw8<T>& r, float* o) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        o[0] = __uint_as_float(r.q[0].x); o[1] = __uint_as_float(r.q[0].y);
+        o[2] = __uint_as_float(r.q[0].z); o[3] = __uint_as_float(r.q[0].w);
+        o[4] = __uint_as_float(r.q[1].x); o[5] = __uint_as_float(r.q[1].y);
+        o[6] = __uint_as_float(r.q[1].z); o[7] = __uint_as_float(r.q[1].w);
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// c + sum of 8 products; bf16 pairs go through v_dot2_f32_bf16 (products of
+// two bf16 values are exact in fp32, the sums are fp32)
+template <typename T>
+__device__ __forceinline__ float dot8(const Raw8<T>& a, const Raw8<T>& b, float c) {
+    if constexpr (sizeof(T) == 2) {
+        c = dot2_bf16(a.q[0].x, b.q[0].x, c);
+        c = dot2_bf16(a.q[0].y, b.q[0].y, c);
+        c = dot2_bf16(a.q[0].z, b.q[0].z, c);
+        c = dot2_bf16(a.q[0].w, b.q[0].w, c);
+        return c;
+    } else {
+        float af[8], bf[8];
+        raw_to_f(a, af);
+        raw_to_f(b, bf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c += af[e] * bf[e];
+        return c;
+    }
+}
+
+// wave steps of 512 K values per producer unit (1024 K values)
+// K values; A stays in registers for the whole unit
+template <typename T> constexpr int dec_steps() { return 2; }
+
+template <typename T>
+__device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
+    constexpr int ST = dec_steps<T>();
+    const LinearArgs& a = p.a;
+    const int per_s = p.jb_max * p.C;
+    const int s = unit / per_s;
+    const int jb = (unit % per_s) / p.C;
+    const int c = unit % p.C;
+    const SegView v = seg_view(p, s, true);
+    if (s >= v.nseg || v.id < 0) return;
+    const int nb = v.rp / 16;
+    if (nb == 0 || jb >= nb * a.n_sl) return;
+    const int sl = jb / nb, jj = jb % nb;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int kbase = c * ST * 512 + lane * 8;
+    const T* A = reinterpret_cast<const T*>(a.A) + v.off +
+                 (int64_t)(sl * v.rp + jj * 16 + wave * 4) * a.K;
+    // A rows of every step, issued together
+    Raw8<T> ar[ST][4];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+        const int k = kbase + st * 512;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (k < a.K) {
+                ar[st][i] = ld_raw8(A + (int64_t)i * a.K + k);
+            } else {
+#pragma unroll
+                for (int q = 0; q < (int)(sizeof(T) / 2); ++q) ar[st][i].q[q] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+    const T* X = reinterpret_cast<const T*>(p.x);
+    slot_t* out = p.slots + ((int64_t)c * a.M + v.p0) * a.cols + sl * a.r_max + jj * 16 + wave * 4;
+    for (int t0 = 0; t0 < v.ms; t0 += kTokGroup) {
+        float acc[kTokGroup][4];
+#pragma unroll
+        for (int u = 0; u < kTokGroup; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[u][i] = 0.f;
+        int mrow[kTokGroup];
+#pragma unroll
+        for (int u = 0; u < kTokGroup; ++u) mrow[u] = __shfl(v.my_idx, v.p0 + t0 + u, kWave);
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+            const int k = kbase + st * 512;
+            Raw8<T> xr[kTokGroup];
+#pragma unroll
+            for (int u = 0; u < kTokGroup; ++u) {
+                if (k < a.K && t0 + u < v.ms) {
+                    xr[u] = ld_raw8(X + (int64_t)mrow[u] * p.ldx + k);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < (int)(sizeof(T) / 2); ++q) xr[u].q[q] = make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int u = 0; u < kTokGroup; ++u) acc[u][i] = dot8<T>(ar[st][i], xr[u], acc[u][i]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kTokGroup; ++u) {
+            if (t0 + u >= v.ms) break;
+            // rows 0..3 summed over the wavefront: reduce-scatter inside groups
+            // of 4 lanes, then a butterfly over the 16 groups
+            reduce_scatter<4>(acc[u], lane & 3);
+            float tot = acc[u][0];
+#pragma unroll
+            for (int o = 4; o < kWave; o <<= 1) tot += __shfl_xor(tot, o, kWave);
+            if (lane < 4) slot_put(out + (int64_t)(t0 + u) * a.cols + lane, tot);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- consumers
+constexpr int kPollBatch = 8;    // exchange slots polled together
+
+template <typename T, int RCAP>
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView& v, int s, int sl,
+                                            int n0, int n1, float* sS, int* sFlag) {
+    constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+    constexpr int CPR = RCAP / EPC;            // chunks per (capacity) row
+    constexpr int RPI = kWave / CPR;           // B rows per load instruction
+    const LinearArgs& a = p.a;
+    const int rp = v.rp;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int g = lane % CPR;
+    const int rsub = lane / CPR;
+    const int nw = n0 + wave * 64;
+    const bool gin = g * EPC < rp;
+    const T* B = reinterpret_cast<const T*>(a.B) + v.off;
+    T* Y = reinterpret_cast<T*>(p.y);
+    const int n_out = nw + g * RPI + rsub;
+    const bool nin = n_out < n1;
+    // 1. B tile and the y values this lane will update, issued before any wait
+    uint4 braw[CPR];
+#pragma unroll
+    for (int q = 0; q < CPR; ++q) {
+        const int n = nw + q * RPI + rsub;
+        braw[q] = (gin && n < n1) ? *reinterpret_cast<const uint4*>(B + (int64_t)n * rp + g * EPC)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+    float yv[kTokGroup];
+#pragma unroll
+    for (int u = 0; u < kTokGroup; ++u) {
+        const int m = __shfl(v.my_idx, v.p0 + u, kWave);
+        yv[u] = (u < v.ms && nin) ? Io<T>::ld(Y + (int64_t)m * p.ldy + n_out) : 0.f;
+    }
+    // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
+    //    polled kPollBatch slots at a time
+    bool ok = true;
+    const int64_t cstride = (int64_t)a.M * a.cols;
+    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
+        const int t = e / rp, j = e % rp;
+        const slot_t* sp = p.slots + (int64_t)(v.p0 + t) * a.cols + sl * a.r_max + j;
+        float acc = 0.f;
+        for (int c0 = 0; c0 < p.C; c0 += kPollBatch) {
+            slot_t w[kPollBatch];
+            for (int spin = 0;; ++spin) {
+                bool all = true;
+#pragma unroll
+                for (int q = 0; q < kPollBatch; ++q) {
+                    if (c0 + q < p.C) {
+                        w[q] = __hip_atomic_load(sp + (c0 + q) * cstride, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        w[q] = 1ull << 32;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kPollBatch; ++q) all = all && (uint32_t)(w[q] >> 32) == 1u;
+                if (all) break;
+                if (!ok || spin >= kMaxSpin) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int q = 0; q < kPollBatch; ++q)
+                if (c0 + q < p.C && (uint32_t)(w[q] >> 32) == 1u)
+                    acc += __uint_as_float((uint32_t)w[q]);
+        }
+        sS[t * RCAP + j] = acc;
+    }
+    if (!ok) atomicOr(p.err, kErrSpin);
+    __syncthreads();
+    // 3. delta rows: lane (rsub, g) dots its chunk with S, then the CPR lanes
+    //    of a row group reduce-scatter so lane g owns row q = g of the group.
+    if (nw < n1) {
+        for (int t = 0; t < v.ms; ++t) {
+            float sv[EPC];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) sv[e] = gin ? sS[t * RCAP + g * EPC + e] : 0.f;
+            float part[CPR];
+#pragma unroll
+            for (int q = 0; q < CPR; ++q) {
+                float bv[EPC];
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t w[4] = {braw[q].x, braw[q].y, braw[q].z, braw[q].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bv[2 * i] = __uint_as_float(w[i] << 16);
+                        bv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+                    }
+                } else {
+                    bv[0] = __uint_as_float(braw[q].x);
+                    bv[1] = __uint_as_float(braw[q].y);
+                    bv[2] = __uint_as_float(braw[q].z);
+                    bv[3] = __uint_as_float(braw[q].w);
+                }
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc += sv[e] * bv[e];
+                part[q] = acc;
+            }
+            reduce_scatter<CPR>(part, g);
+            const int m = __shfl(v.my_idx, v.p0 + t, kWave);   // all lanes take part
+            if (nin) {
+                T* yp = Y + (int64_t)m * p.ldy + n_out;
+                float old = 0.f;
+#pragma unroll
+                for (int u = 0; u < kTokGroup; ++u)
+                    if (u == t) old = yv[u];
+                if (t >= kTokGroup) old = Io<T>::ld(yp);
+                Io<T>::st(yp, old + part[0]);
+            }
+        }
+    }
+    // 4. the last consumer of (segment, slice) empties the slots it shared
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int tiles = p.tile_start[sl + 1] - p.tile_start[sl];
+        int* cnt = p.counters + s * a.n_sl + sl;
+        const int old = atomic_add_agent(cnt, 1);
+        *sFlag = (old == tiles - 1);
+        if (*sFlag) atomic_store_agent(cnt, 0);
+    }
+    __syncthreads();
+    if (*sFlag) {
+        for (int e = threadIdx.x; e < v.ms * rp * p.C; e += kDecThreads) {
+            const int c = e / (v.ms * rp);
+            const int r = e % (v.ms * rp);
+            const int t = r / rp, j = r % rp;
+            slot_clear(p.slots + ((int64_t)c * a.M + v.p0 + t) * a.cols + sl * a.r_max + j);
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
+    __shared__ float sS[LORA_DECODE_MAX_M * LORA_MAX_RANK];
+    __shared__ int sFlag;
+    if ((int)blockIdx.x < p.grid1) {
+        dec_produce<T>(p, blockIdx.x);
+        return;
+    }
+    const LinearArgs& a = p.a;
+    const int u = blockIdx.x - p.grid1;
+    const int s = u / p.n_tiles;
+    const int t = u % p.n_tiles;
+    const SegView v = seg_view(p, s, false);
+    if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
+    int sl = 0;
+    while (sl + 1 < a.n_sl && t >= p.tile_start[sl + 1]) ++sl;
+    const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
+    const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
+    if (v.rp <= 16)
+        dec_consume<T, 16>(p, v, s, sl, n0, n1, sS, &sFlag);
+    else if (v.rp <= 32)
+        dec_consume<T, 32>(p, v, s, sl, n0, n1, sS, &sFlag);
+    else
+        dec_consume<T, 64>(p, v, s, sl, n0, n1, sS, &sFlag);
+}
+
+hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, void* y,
+                               int64_t ldy, void* ws, hipStream_t st) {
+    DecodeParams p{};
+    p.a = a;
+    p.x = x;
+    p.ldx = ldx;
+    p.y = y;
+    p.ldy = ldy;
+    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.L, a.n_sl);
+    char* base = reinterpret_cast<char*>(ws);
+    p.err = reinterpret_cast<int*>(base + L.header);
+    p.counters = reinterpret_cast<int*>(base + L.counters);
+    p.slots = reinterpret_cast<slot_t*>(base + L.slots);
+    const int kc = 512 * (a.dtype == LORA_BF16 ? dec_steps<uint16_t>() : dec_steps<float>());
+    p.C = (a.K + kc - 1) / kc;
+    p.jb_max = a.cols / 16;
+    p.grid1 = a.s_max * p.jb_max * p.C;
+    int t = 0;
+    for (int s = 0; s < a.n_sl; ++s) {
+        p.tile_start[s] = t;
+        t += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+    }
+    p.tile_start[a.n_sl] = t;
+    p.n_tiles = t;
+    const unsigned grid = (unsigned)(p.grid1 + a.s_max * p.n_tiles);
+    if (a.dtype == LORA_BF16) {
+        hipLaunchKernelGGL(k_decode_fused<uint16_t>, dim3(grid), dim3(kDecThreads), 0, st, p);
+    } else {
+        hipLaunchKernelGGL(k_decode_fused<float>, dim3(grid), dim3(kDecThreads), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mlora

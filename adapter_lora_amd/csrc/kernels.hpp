@@ -1,0 +1,123 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the
+// kernels.  Host and device visible; no HIP types beyond hipStream_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mlora.h"
+
+namespace mlora {
+
+// Dense multi-LoRA call description (validated by api.cpp).
+struct LinearArgs {
+    int dtype;
+    int K;
+    int n_sl;
+    int L;
+    int r_max;      // padded rank bound (multiple of 16)
+    int M;
+    int s_max;      // segment bound: min(L, M)
+    int cols;       // n_sl * r_max: width of one S row
+    int64_t slice_off[LORA_MAX_SLICES + 1];
+    const void* A;
+    const void* B;
+    const int64_t* a_off;
+    const int64_t* b_off;
+    const int32_t* rank;
+    const int32_t* sorted_idx;
+    const int32_t* seg_indptr;
+    const int32_t* req_to_lora;
+    const int32_t* num_segments;
+};
+
+// K columns handled by one shrink work unit (fused decode and MFMA shrink).
+constexpr int kKChunk = 512;
+// Output columns handled by one expand work unit.
+constexpr int kNTile = 256;
+
+inline int kchunks(int K) { return (K + kKChunk - 1) / kKChunk; }
+
+inline int ntiles_total(const LinearArgs& a) {
+    int t = 0;
+    for (int s = 0; s < a.n_sl; ++s) {
+        const int64_t n = a.slice_off[s + 1] - a.slice_off[s];
+        t += (int)((n + kNTile - 1) / kNTile);
+    }
+    return t;
+}
+
+// Workspace layout (bytes from the start), see api.cpp.
+struct LinearWs {
+    size_t header;      // WsHeader
+    size_t counters;    // int[s_max * n_sl] (decode consumer counters)
+    size_t slots;       // slot_t[C][M][cols] (decode exchange)
+    size_t partial;     // float[C][M][cols]   (MFMA shrink partial sums)
+    size_t S;           // float[M][cols]      (S between shrink and expand)
+    size_t total;
+};
+
+LinearWs linear_ws_layout(int M, int K, int cols, int L, int n_sl);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
+                                 int32_t* seg_indptr, int32_t* req_to_lora,
+                                 int32_t* num_segments, hipStream_t st);
+
+hipError_t launch_pack_adapter(int dtype, int K, int64_t N, int n_sl, int rank, int rank_pad,
+                               const void* A_src, const void* B_src, void* A_dst, void* B_dst,
+                               hipStream_t st);
+
+hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, void* y,
+                               int64_t ldy, void* ws, hipStream_t st);
+
+// S (fp32 [M][cols], sorted rows) from x; `ws` holds the partial sums.
+hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float* S, void* ws,
+                         hipStream_t st);
+
+hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
+                         hipStream_t st);
+
+// MoE
+struct MoeArgs {
+    int dtype;
+    int L, E, H, I, r;
+    int M, topk;
+    int max_tokens_padded, block_size_m;
+    const void* A_gu;
+    const void* B_gu;
+    const void* A_d;
+    const void* B_d;
+    const int32_t* adapter_enabled;
+    const int32_t* sorted_token_ids;
+    const int32_t* expert_ids;
+    const int32_t* ntpp;
+};
+
+struct MoeWs {
+    size_t header;
+    size_t partial;     // float[C][L*max_tokens_padded][r]
+    size_t S;           // float[L*max_tokens_padded][r]
+    size_t total;
+};
+
+MoeWs moe_ws_layout(int L, int max_tokens_padded, int r, int Kmax);
+
+hipError_t launch_moe_align(const int32_t* topk_ids, const int32_t* ids,
+                            const int32_t* adapter_enabled, int M, int topk, int E, int L,
+                            int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
+                            int max_tokens_padded, int block_size_m, hipStream_t st);
+
+// which = 0: gate/up (x rows = f / topk, K = H, N = 2I); 1: down (rows = f, K = I, N = H)
+hipError_t launch_moe_delta(const MoeArgs& a, int which, const void* in, int64_t ld_in,
+                            void* out, int64_t ld_out, void* ws, hipStream_t st);
+
+hipError_t launch_silu_and_mul(int dtype, const void* c1, int64_t ld1, void* c2, int64_t ld2,
+                               int P, int I, hipStream_t st);
+
+hipError_t launch_topk_reduce(int dtype, const void* c3, int64_t ld3, const float* w, void* out,
+                              int64_t ldo, int M, int topk, int H, hipStream_t st);
+
+}  // namespace mlora

@@ -1,0 +1,366 @@
+// LoRA on a Mixture-of-Experts MLP (SGLang "LoRA + MoE" page):
+//   * alignment: one padded list of (token, expert) pairs per adapter, sorted
+//     by expert ("MoE LoRA Alignment");
+//   * stage 1.5: cache1 += gate/up delta, before the activation;
+//   * stage 2: silu_and_mul;
+//   * stage 3.5: cache3 += down delta, before the reduce;
+//   * the final top-k weighted reduce.
+// The deltas run the same MFMA shrink / expand tiles as the dense path, with
+// a unit = (adapter, block of block_size_m aligned pairs) that reads the
+// weights of the block's expert.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace mlora {
+
+// ---------------------------------------------------------------- alignment
+constexpr int kAlignThreads = 256;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+constexpr int kMaxExperts = 256;
+
+__global__ __launch_bounds__(kAlignThreads) void k_moe_align(
+    const int32_t* __restrict__ topk_ids, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ adapter_enabled, int M, int topk, int E,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ ntpp, int mtp, int bs) {
+    __shared__ int cnt[kMaxExperts];
+    __shared__ int base[kMaxExperts];
+    __shared__ int wcnt[kAlignWaves][kMaxExperts];
+    __shared__ int total_sh;
+    const int l = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int P = M * topk;
+    const int nblk = mtp / bs;
+    int32_t* row = sorted_ids + (int64_t)l * mtp;
+    int32_t* erow = expert_ids + (int64_t)l * nblk;
+    const bool on = adapter_enabled[l] != 0;
+
+    for (int e = tid; e < kMaxExperts; e += kAlignThreads) {
+        cnt[e] = 0;
+        for (int w = 0; w < kAlignWaves; ++w) wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    if (on) {
+        for (int f = tid; f < P; f += kAlignThreads) {
+            const int e = topk_ids[f];
+            if (ids[f / topk] == l && e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int run = 0;
+        for (int e0 = 0; e0 < E; e0 += kWave) {
+            const int e = e0 + lane;
+            const int c = (e < E) ? cnt[e] : 0;
+            const int pad = (c + bs - 1) / bs * bs;
+            int inc = pad;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int v = __shfl_up(inc, o, kWave);
+                if (lane >= o) inc += v;
+            }
+            if (e < E) base[e] = run + inc - pad;
+            run += __shfl(inc, kWave - 1, kWave);
+        }
+        if (lane == 0) {
+            total_sh = run;
+            ntpp[l] = run;
+        }
+    }
+    __syncthreads();
+    const int total = total_sh;
+    // expert id per block; sentinels in padding slots and the tail
+    for (int b = tid; b < nblk; b += kAlignThreads) erow[b] = -1;
+    __syncthreads();
+    for (int e = 0; e < E; ++e) {
+        const int c = cnt[e];
+        if (c == 0) continue;
+        const int pad = (c + bs - 1) / bs * bs;
+        for (int b = base[e] / bs + tid; b < (base[e] + pad) / bs; b += kAlignThreads) erow[b] = e;
+        for (int i = base[e] + c + tid; i < base[e] + pad; i += kAlignThreads) row[i] = P;
+    }
+    for (int i = total + tid; i < mtp; i += kAlignThreads) row[i] = P;
+    if (!on) return;
+    // stable scatter of the adapter's pairs, in increasing f, into their bucket
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int f0 = 0; f0 < P; f0 += kAlignThreads) {
+        const int f = f0 + tid;
+        int e = 0;
+        bool act = false;
+        if (f < P) {
+            e = topk_ids[f];
+            act = ids[f / topk] == l && e >= 0 && e < E;
+        }
+        unsigned long long peers = __ballot(act);
+        for (int i = 0; i < nbits; ++i) {
+            const bool bit = (e >> i) & 1;
+            const unsigned long long bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank_w = __popcll(peers & lt);
+        const bool leader = act && rank_w == 0;
+        if (leader) wcnt[wave][e] = __popcll(peers);
+        __syncthreads();
+        if (act) {
+            int pos = base[e] + rank_w;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+            row[pos] = f;
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&base[e], __popcll(peers));   // one leader per wave and expert
+            wcnt[wave][e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_moe_align(const int32_t* topk_ids, const int32_t* ids,
+                            const int32_t* adapter_enabled, int M, int topk, int E, int L,
+                            int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
+                            int max_tokens_padded, int block_size_m, hipStream_t st) {
+    hipLaunchKernelGGL(k_moe_align, dim3(L), dim3(kAlignThreads), 0, st, topk_ids, ids,
+                       adapter_enabled, M, topk, E, sorted_token_ids, expert_ids, ntpp,
+                       max_tokens_padded, block_size_m);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- deltas
+struct MoeUnit {
+    bool ok;
+    int e;
+};
+
+// Stage the rows of block b of adapter l.  `shrink` selects the row roles:
+// shrink: in = source row of the activation, out = P/S row (l*mtp + pos);
+// expand: in = S row, out = cache row f.
+__device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool shrink, int l, int b,
+                                            int* s_in, int* s_out) {
+    const int bs = a.block_size_m;
+    if (!a.adapter_enabled[l] || b * bs >= a.ntpp[l]) return MoeUnit{false, -1};
+    const int e = a.expert_ids[(int64_t)l * (a.max_tokens_padded / bs) + b];
+    if (e < 0 || e >= a.E) return MoeUnit{false, -1};
+    const int P = a.M * a.topk;
+    for (int i = threadIdx.x; i < bs; i += kTileThreads) {
+        const int pos = b * bs + i;
+        const int f = a.sorted_token_ids[(int64_t)l * a.max_tokens_padded + pos];
+        const bool real = f >= 0 && f < P;
+        const int srow = l * a.max_tokens_padded + pos;
+        const int src = which == 0 ? f / a.topk : f;
+        if (shrink) {
+            s_in[i] = real ? src : -1;
+            s_out[i] = real ? srow : -1;
+        } else {
+            s_in[i] = real ? srow : -1;
+            s_out[i] = real ? f : -1;
+        }
+    }
+    __syncthreads();
+    return MoeUnit{true, e};
+}
+
+template <typename T, int NCB>
+__global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int which,
+                                                              const T* __restrict__ in,
+                                                              int64_t ld_in, float* __restrict__ P,
+                                                              int C, int K) {
+    __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
+    const int nblk = a.max_tokens_padded / a.block_size_m;
+    const int unit = blockIdx.x / C;
+    const int c = blockIdx.x % C;
+    const int l = unit / nblk, b = unit % nblk;
+    const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out);
+    if (!mu.ok) return;
+    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const T* A = reinterpret_cast<const T*>(which == 0 ? a.A_gu : a.A_d) + ew * a.r * K;
+    const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
+    const int k0 = c * kKChunk;
+    const int k1 = min(K, k0 + kKChunk);
+    const int rows = a.L * a.max_tokens_padded;
+    float* Pc = P + (int64_t)c * rows * a.r;
+    if constexpr (sizeof(T) == 2) {
+        shrink_tile_bf16<NCB>(rs, reinterpret_cast<const uint16_t*>(in), ld_in,
+                              reinterpret_cast<const uint16_t*>(A), K, a.r, a.r, k0, k1, Pc, a.r);
+    } else {
+        shrink_tile_simple<T>(rs, in, ld_in, A, K, 1, a.r, a.r, k0, k1, Pc, a.r);
+    }
+}
+
+// S rows of the aligned positions that exist (pos < ntpp[l]).
+__global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride,
+                             float* __restrict__ S, int r, int mtp,
+                             const int32_t* __restrict__ ntpp, int L) {
+    const int l = blockIdx.y;
+    const int n = ntpp[l];
+    const int64_t row0 = (int64_t)l * mtp;
+    const int total4 = n * r / 4;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += gridDim.x * blockDim.x) {
+        const int64_t idx = row0 * r / 4 + i;
+        float4 acc = reinterpret_cast<const float4*>(P)[idx];
+        for (int c = 1; c < C; ++c) {
+            const float4 v = reinterpret_cast<const float4*>(P + c * cstride)[idx];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        reinterpret_cast<float4*>(S)[idx] = acc;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kTileThreads) void k_moe_expand(MoeArgs a, int which,
+                                                              const float* __restrict__ S,
+                                                              T* __restrict__ out, int64_t ld_out,
+                                                              int N, int n_tiles) {
+    __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
+    const int nblk = a.max_tokens_padded / a.block_size_m;
+    const int unit = blockIdx.x / n_tiles;
+    const int t = blockIdx.x % n_tiles;
+    const int l = unit / nblk, b = unit % nblk;
+    const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out);
+    if (!mu.ok) return;
+    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const T* B = reinterpret_cast<const T*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
+    const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
+    const int n0 = t * kNTile;
+    const int n1 = min(N, n0 + kNTile);
+    if constexpr (sizeof(T) == 2) {
+        expand_tile_bf16(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n0, n1,
+                         reinterpret_cast<uint16_t*>(out), ld_out);
+    } else {
+        expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, n1, out, ld_out);
+    }
+}
+
+template <typename T>
+static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64_t ld_in,
+                              void* out, int64_t ld_out, void* ws, hipStream_t st) {
+    const int K = which == 0 ? a.H : a.I;
+    const int N = which == 0 ? 2 * a.I : a.H;
+    const int C = kchunks(K);
+    const int nblk = a.max_tokens_padded / a.block_size_m;
+    const MoeWs W = moe_ws_layout(a.L, a.max_tokens_padded, a.r, a.H > a.I ? a.H : a.I);
+    float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.partial);
+    float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
+    const unsigned g1 = (unsigned)(a.L * nblk * C);
+    switch (a.r / 16) {
+#define MLORA_MOE_NCB(n)                                                                          \
+    case n:                                                                                       \
+        hipLaunchKernelGGL((k_moe_shrink<T, n>), dim3(g1), dim3(kTileThreads), 0, st, a, which,   \
+                           reinterpret_cast<const T*>(in), ld_in, P, C, K);                       \
+        break;
+        MLORA_MOE_NCB(1) MLORA_MOE_NCB(2) MLORA_MOE_NCB(3) MLORA_MOE_NCB(4)
+#undef MLORA_MOE_NCB
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
+    int rb = (a.max_tokens_padded * a.r / 4 + 255) / 256;
+    if (rb < 1) rb = 1;
+    hipLaunchKernelGGL(k_moe_reduce, dim3((unsigned)rb, (unsigned)a.L), dim3(256), 0, st, P, C,
+                       cstride, S, a.r, a.max_tokens_padded, a.ntpp, a.L);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_tiles = (N + kNTile - 1) / kNTile;
+    const unsigned g2 = (unsigned)(a.L * nblk * n_tiles);
+    hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
+                       reinterpret_cast<T*>(out), ld_out, N, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_delta(const MoeArgs& a, int which, const void* in, int64_t ld_in,
+                            void* out, int64_t ld_out, void* ws, hipStream_t st) {
+    return a.dtype == LORA_BF16 ? moe_delta_t<uint16_t>(a, which, in, ld_in, out, ld_out, ws, st)
+                                : moe_delta_t<float>(a, which, in, ld_in, out, ld_out, ws, st);
+}
+
+// ---------------------------------------------------------------- silu_and_mul
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+__global__ void k_silu_mul_bf16(const uint16_t* __restrict__ c1, int64_t ld1,
+                                uint16_t* __restrict__ c2, int64_t ld2, int P, int I) {
+    const int per_row = I / 8;
+    const int64_t total = (int64_t)P * per_row;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t f = i / per_row;
+        const int j = (int)(i - f * per_row) * 8;
+        float g[8], u[8];
+        Io<uint16_t>::ld8(c1 + f * ld1 + j, g);
+        Io<uint16_t>::ld8(c1 + f * ld1 + I + j, u);
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = f32_to_bf16(silu_f(g[2 * q]) * u[2 * q]) |
+                   (f32_to_bf16(silu_f(g[2 * q + 1]) * u[2 * q + 1]) << 16);
+        *reinterpret_cast<uint4*>(c2 + f * ld2 + j) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+__global__ void k_silu_mul_f32(const float* __restrict__ c1, int64_t ld1, float* __restrict__ c2,
+                               int64_t ld2, int P, int I) {
+    const int64_t total = (int64_t)P * I;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t f = i / I;
+        const int j = (int)(i - f * I);
+        c2[f * ld2 + j] = silu_f(c1[f * ld1 + j]) * c1[f * ld1 + I + j];
+    }
+}
+
+hipError_t launch_silu_and_mul(int dtype, const void* c1, int64_t ld1, void* c2, int64_t ld2,
+                               int P, int I, hipStream_t st) {
+    const int64_t work = dtype == LORA_BF16 ? (int64_t)P * I / 8 : (int64_t)P * I;
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    if (dtype == LORA_BF16)
+        hipLaunchKernelGGL(k_silu_mul_bf16, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const uint16_t*)c1, ld1, (uint16_t*)c2, ld2, P, I);
+    else
+        hipLaunchKernelGGL(k_silu_mul_f32, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const float*)c1, ld1, (float*)c2, ld2, P, I);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- top-k reduce
+template <typename T>
+__global__ void k_topk_reduce(const T* __restrict__ c3, int64_t ld3, const float* __restrict__ w,
+                              T* __restrict__ out, int64_t ldo, int M, int topk, int H) {
+    const int per_row = H / 8;
+    const int64_t total = (int64_t)M * per_row;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t m = i / per_row;
+        const int h = (int)(i - m * per_row) * 8;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < topk; ++k) {
+            const float wk = w[m * topk + k];
+            float v[8];
+            Io<T>::ld8(c3 + (m * topk + k) * ld3 + h, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += wk * v[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Io<T>::st(out + m * ldo + h + e, acc[e]);
+    }
+}
+
+hipError_t launch_topk_reduce(int dtype, const void* c3, int64_t ld3, const float* w, void* out,
+                              int64_t ldo, int M, int topk, int H, hipStream_t st) {
+    int64_t blocks = ((int64_t)M * H / 8 + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    if (dtype == LORA_BF16)
+        hipLaunchKernelGGL(k_topk_reduce<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const uint16_t*)c3, ld3, w, (uint16_t*)out, ldo, M, topk, H);
+    else
+        hipLaunchKernelGGL(k_topk_reduce<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const float*)c3, ld3, w, (float*)out, ldo, M, topk, H);
+    return hipGetLastError();
+}
+
+}  // namespace mlora

@@ -1,0 +1,169 @@
+// lora_build_segments: token clustering by adapter id into a segment table
+// ("vLLM-Ascend dynamic LoRA operator" walkthrough, section 2.3: equal ids
+// made contiguous; a segment is an id plus a contiguous range of tokens).
+//
+// One workgroup runs a stable counting sort:
+//   1. histogram of bucket ids in LDS (bucket L = no adapter);
+//   2. one wavefront scans the histogram into bucket bases and compacts the
+//      non-empty adapter buckets into (req_to_lora, seg_indptr);
+//   3. tokens are scattered tile by tile in token order: inside a wavefront
+//      equal buckets are found with one ballot per id bit, so a token's rank
+//      among its equals is a popcount; earlier wavefronts' counts per bucket
+//      come from a small LDS table.  Order inside a bucket is token order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mlora {
+
+constexpr int kSegThreads = 512;
+constexpr int kSegWaves = kSegThreads / kWave;
+constexpr int kCachedTiles = 8;
+
+__global__ __launch_bounds__(kSegThreads) void k_build_segments(
+    const int32_t* __restrict__ ids, int M, int L, int32_t* __restrict__ sorted_idx,
+    int32_t* __restrict__ seg_indptr, int32_t* __restrict__ req_to_lora,
+    int32_t* __restrict__ num_segments) {
+    extern __shared__ int lds[];
+    const int NB = L + 1;
+    int* count = lds;               // [NB]
+    int* base = lds + NB;           // [NB]   running output position per bucket
+    int* wcnt = lds + 2 * NB;       // [kSegWaves][NB] per-tile, per-wave bucket counts
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+
+    for (int i = tid; i < NB * (2 + kSegWaves); i += kSegThreads) lds[i] = 0;
+    __syncthreads();
+
+    // bucket of each of this thread's tokens; the first kCachedTiles tiles stay
+    // in registers for the scatter (their loads are issued together)
+    int bk[kCachedTiles];
+#pragma unroll
+    for (int i = 0; i < kCachedTiles; ++i) {
+        const int m = i * kSegThreads + tid;
+        int b = L;
+        if (m < M) {
+            const int v = ids[m];
+            b = (v >= 0 && v < L) ? v : L;
+        }
+        bk[i] = b;
+    }
+#pragma unroll
+    for (int i = 0; i < kCachedTiles; ++i)
+        if (i * kSegThreads + tid < M) atomicAdd(&count[bk[i]], 1);
+    for (int m = kCachedTiles * kSegThreads + tid; m < M; m += kSegThreads) {
+        const int v = ids[m];
+        atomicAdd(&count[(v >= 0 && v < L) ? v : L], 1);
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        int run = 0, segs = 0;
+        for (int b0 = 0; b0 < NB; b0 += kWave) {
+            const int b = b0 + lane;
+            const int c = (b < NB) ? count[b] : 0;
+            int inc = c;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int t = __shfl_up(inc, o, kWave);
+                if (lane >= o) inc += t;
+            }
+            const int excl = run + inc - c;
+            if (b < NB) base[b] = excl;
+            const bool present = (b < L) && (c > 0);
+            const unsigned long long bal = __ballot(present);
+            const int s = segs + __popcll(bal & ((1ull << lane) - 1ull));
+            if (present) {
+                req_to_lora[s] = b;
+                seg_indptr[s + 1] = excl + c;
+            }
+            run += __shfl(inc, kWave - 1, kWave);
+            segs += __popcll(bal);
+        }
+        const int m_valid = run - count[L];
+        if (lane == 0) {
+            seg_indptr[0] = 0;
+            num_segments[0] = segs;
+        }
+        for (int s = segs + 1 + lane; s <= L; s += kWave) seg_indptr[s] = m_valid;
+        for (int s = segs + lane; s < L; s += kWave) req_to_lora[s] = -1;
+    }
+    __syncthreads();
+
+    const int nbits = 32 - __clz(L);          // enough bits for buckets 0..L
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    // one tile of kSegThreads tokens in token order; b = this thread's bucket
+    auto scatter_tile = [&](int t0, int b) {
+        const int m = t0 + tid;
+        const bool act = m < M;
+        unsigned long long peers = __ballot(act);
+        for (int i = 0; i < nbits; ++i) {
+            const bool bit = (b >> i) & 1;
+            const unsigned long long bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank_w = __popcll(peers & lt);
+        const bool leader = act && rank_w == 0;
+        if (leader) wcnt[wave * NB + b] = __popcll(peers);
+        __syncthreads();
+        if (act) {
+            int pos = base[b] + rank_w;
+            for (int w = 0; w < wave; ++w) pos += wcnt[w * NB + b];
+            sorted_idx[pos] = m;
+        }
+        __syncthreads();
+        if (leader) {
+            atomicAdd(&base[b], __popcll(peers));
+            wcnt[wave * NB + b] = 0;
+        }
+        __syncthreads();
+    };
+#pragma unroll
+    for (int i = 0; i < kCachedTiles; ++i) {
+        if (i * kSegThreads >= M) break;
+        scatter_tile(i * kSegThreads, bk[i]);
+    }
+    for (int t0 = kCachedTiles * kSegThreads; t0 < M; t0 += kSegThreads) {
+        int b = L;
+        if (t0 + tid < M) {
+            const int v = ids[t0 + tid];
+            b = (v >= 0 && v < L) ? v : L;
+        }
+        scatter_tile(t0, b);
+    }
+}
+
+hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
+                                 int32_t* seg_indptr, int32_t* req_to_lora,
+                                 int32_t* num_segments, hipStream_t st) {
+    const size_t lds = (size_t)(L + 1) * (2 + kSegWaves) * sizeof(int);
+    hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kSegThreads), lds, st, ids, M, L,
+                       sorted_idx, seg_indptr, req_to_lora, num_segments);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// zero fill (workspace initialisation; a kernel rather than a memset so that
+// it can sit inside a captured graph)
+// ---------------------------------------------------------------------------
+__global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                            size_t ntail) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0, 0, 0, 0);
+    if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+    if (bytes == 0) return hipSuccess;
+    const size_t n16 = bytes / 16;
+    const size_t ntail = bytes - n16 * 16;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, st, (uint4*)p, n16,
+                       (uint8_t*)p + n16 * 16, ntail);
+    return hipGetLastError();
+}
+
+}  // namespace mlora

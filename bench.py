@@ -1,0 +1,304 @@
+"""Benchmark of the dynamic multi-LoRA hot path on one MI355X.
+
+Headline workload: decode, bf16, M=32 tokens (one per sequence), K=N=4096,
+20 adapters with ranks drawn from {16,32,64}, 10% of tokens without an
+adapter.  One step = lora_build_segments + lora_shrink_expand_add (the fused
+decode kernel) on one batch.  Inputs are synthetic and seeded (workloads.py).
+
+Protocol:
+  * R copies of every input (packed weight table, x, y, ids, segment table)
+    sized so that R copies exceed twice the 256 MB Infinity Cache; step i uses
+    copy i % R, so each step reads its weights from HBM (cold MALL);
+  * W warmup steps, then K timed steps between two device synchronisations;
+    ms_per_step is the wall time of the K steps (launch gaps included);
+  * the dominant kernel is bracketed by HIP events on the stream it runs on,
+    every step, and its mean duration gives the roofline figure:
+    algorithmic bytes per launch / mean duration, against 8 TB/s;
+  * the oracle (fp64 CPU) is timed on the host on a bounded sample.
+Other configurations (prefill, stacked QKV / gate-up, MoE) are measured the
+same way and reported under "extra" as context; the headline line is the
+decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+METRIC = "LoRA-delta tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s vs peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--only", default="", help="comma list: decode,prefill,qkv,gate_up,moe")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- helpers
+def dev_tensor(t):
+    import torch
+    import workloads as W
+    if t.dtype == W.BF16:
+        return torch.from_numpy(t.storage.astype(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(t.storage).cuda()
+
+
+def linear_bytes_flops(case):
+    """Algorithmic bytes and FLOPs of one pass: each touched adapter's A and B
+    read once, x rows of tokens with an adapter read once, their y rows read
+    and written once (element size 2 for bf16)."""
+    es = 2 if case.dtype == "bf16" else 4
+    touched = sorted(set(int(i) for i in case.ids if 0 <= i < case.L and case.ranks[i] > 0))
+    m_valid = int(sum(1 for i in case.ids if 0 <= i < case.L and case.ranks[i] > 0))
+    w_bytes = sum(case.ranks[i] * (case.n_slices * case.K + case.N) * es for i in touched)
+    act = m_valid * case.K * es + 2 * m_valid * case.N * es
+    flops = sum(2 * case.ranks[int(i)] * (case.n_slices * case.K + case.N)
+                for i in case.ids if 0 <= i < case.L and case.ranks[int(i)] > 0)
+    return w_bytes + act, flops, m_valid, len(touched)
+
+
+class Timer:
+    """Event pairs around one kernel launch per step, on the launching stream."""
+
+    def __init__(self, n):
+        import torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        self.i = 0
+
+    def start(self):
+        self.ev[self.i][0].record()
+
+    def stop(self):
+        self.ev[self.i][1].record()
+        self.i += 1
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[:self.i]]))
+
+
+def run_timed(step, steps, warmup, timer_slots):
+    import torch
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    timer = Timer(steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(warmup + i, timer)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, timer.mean_ms(), wall / steps * 1e3
+
+
+# ----------------------------------------------------------------------------- dense
+def bench_linear(case, steps, warmup, fused_kernel_name):
+    import torch
+    import adapter_lora_amd as ml
+    nbytes, flops, m_valid, touched = linear_bytes_flops(case)
+    per_copy = nbytes + case.M * case.K * 2
+    R = max(2, int(np.ceil(2 * MALL_BYTES / max(per_copy, 1))))
+    A = [dev_tensor(a) for a in case.A]
+    B = [dev_tensor(b) for b in case.B]
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    copies = []
+    for r in range(R):
+        table = ml.LoraTable(A, B, case.ranks, case.slice_sizes, case.K, dt)
+        ids = torch.from_numpy(case.ids).cuda()
+        seg = ml.Segments(case.M, case.L)
+        copies.append((table, ids, seg, dev_tensor(case.x), dev_tensor(case.y_base)))
+    ws = ml.Workspace.for_table(copies[0][0], case.M)
+    del A, B
+    torch.cuda.synchronize()
+
+    def step(i, timer):
+        table, ids, seg, x, y = copies[i % R]
+        ml.lora_build_segments(ids, seg)
+        if timer:
+            timer.start()
+        ml.lora_shrink_expand_add(table, x, seg, y, ws)
+        if timer:
+            timer.stop()
+
+    ms_step, ms_kernel, ms_wall = run_timed(step, steps, warmup, 1)
+    assert ml.lora_read_device_error(ws.buf) == 0, "device error during the bench"
+    res = {
+        "ms_per_step": ms_step, "ms_kernel_events": ms_kernel, "ms_wall_host": ms_wall,
+        "tokens_per_s": m_valid / (ms_step * 1e-3), "m_valid": m_valid, "M": case.M,
+        "adapters_touched": touched, "alg_bytes": nbytes, "alg_flops": flops,
+        "kernel": fused_kernel_name, "rotation_copies": R,
+        "hbm_gbs": nbytes / (ms_kernel * 1e-3) / 1e9,
+        "tflops": flops / (ms_kernel * 1e-3) / 1e12,
+    }
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    res["mfma_frac"] = res["tflops"] / BF16_MFMA_PEAK_TFLOPS
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- MoE
+def bench_moe(case, steps, warmup):
+    import torch
+    import adapter_lora_amd as ml
+    es = 2
+    P = case.M * case.topk
+    pairs = [(int(case.ids[m]), int(case.topk_ids[m, k])) for m in range(case.M)
+             for k in range(case.topk) if case.ids[m] >= 0 and case.adapter_enabled[case.ids[m]]]
+    buckets = set(pairs)
+    r, H, I = case.rank, case.H, case.I
+    w_bytes = len(buckets) * r * (H + 2 * I + I + H) * es
+    act = len(pairs) * (H + 2 * 2 * I + I + 2 * H) * es
+    nbytes = w_bytes + act
+    flops = len(pairs) * 2 * r * (H + 2 * I + I + H)
+    R = max(2, int(np.ceil(2 * MALL_BYTES / (w_bytes + act))))
+    R = min(R, 12)
+    en = torch.from_numpy(case.adapter_enabled).cuda()
+    base = [dev_tensor(t) for t in (case.A_gu, case.B_gu, case.A_d, case.B_d)]
+    copies = []
+    for _ in range(R):
+        w = ml.MoeWeights(*[t.clone() for t in base], en)
+        copies.append((w, dev_tensor(case.x), dev_tensor(case.cache1), dev_tensor(case.cache3)))
+    cap = ml.lora_moe_align_capacity(case.M, case.topk, case.E, case.block_size_m)
+    al = ml.MoeAlign(case.L, cap, case.block_size_m)
+    tid = torch.from_numpy(case.topk_ids).cuda()
+    ids = torch.from_numpy(case.ids).cuda()
+    wts = torch.from_numpy(case.topk_weights).cuda()
+    c2 = torch.empty(P, I, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(case.M, H, dtype=torch.bfloat16, device="cuda")
+    ws = ml.Workspace(ml.lora_moe_workspace_size(copies[0][0], cap))
+    torch.cuda.synchronize()
+
+    def step(i, timer):
+        w, x, c1, c3 = copies[i % R]
+        ml.lora_moe_align_run(tid, ids, en, case.E, al)
+        if timer:
+            timer.start()
+        ml.lora_moe_gate_up_add(w, x, case.topk, al, c1, ws)
+        ml.lora_moe_silu_and_mul(c1, c2)
+        ml.lora_moe_down_add(w, c2, case.M, case.topk, al, c3, ws)
+        if timer:
+            timer.stop()
+        ml.lora_moe_topk_reduce(c3, wts, out)
+
+    ms_step, ms_deltas, ms_wall = run_timed(step, steps, warmup, 1)
+    silu_bytes = P * 3 * I * es
+    res = {
+        "ms_per_step": ms_step, "ms_deltas_and_silu_events": ms_deltas, "ms_wall_host": ms_wall,
+        "tokens_per_s": case.M / (ms_step * 1e-3), "pairs": len(pairs), "buckets": len(buckets),
+        "alg_bytes_deltas": nbytes, "alg_bytes_silu": silu_bytes, "alg_flops": flops,
+        "rotation_copies": R,
+        "hbm_gbs": (nbytes + silu_bytes) / (ms_deltas * 1e-3) / 1e9,
+    }
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- oracle
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, on the host: whole decode batches repeated
+    until about `seconds` of CPU time have been spent."""
+    from threadpoolctl import threadpool_info
+    from oracle import lora as O
+    A = [a.values for a in case.A]
+    B = [b.values for b in case.B]
+    m_valid = int(sum(1 for i in case.ids if i >= 0))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.lora_linear(case.x.values, case.ids, A, B, case.ranks, case.slice_sizes,
+                      case.y_base.values)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": m_valid * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full decode batches (M=32, {m_valid} tokens with an adapter) "
+                      f"in {el:.1f} s, fp64 numpy per-token loop",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    only = set(s for s in args.only.split(",") if s)
+    want = lambda k: not only or k in only
+
+    results = {}
+    dec_case = W.decode_bf16(0)
+    if want("decode"):
+        results["decode_bf16"] = bench_linear(dec_case, args.steps, args.warmup,
+                                              "k_decode_fused<uint16_t>")
+    if want("prefill"):
+        results["prefill_bf16"] = bench_linear(W.prefill_bf16(0), args.steps, args.warmup,
+                                               "k_shrink_dense + k_reduce_partials + k_expand_dense")
+    if want("qkv"):
+        results["stacked_qkv_bf16"] = bench_linear(W.stacked_bf16("qkv", 0), args.steps,
+                                                   args.warmup, "shrink + reduce + expand")
+    if want("gate_up"):
+        results["stacked_gate_up_bf16"] = bench_linear(W.stacked_bf16("gate_up", 0), args.steps,
+                                                       args.warmup, "shrink + reduce + expand")
+    if want("moe"):
+        results["moe_bf16"] = bench_moe(W.moe_case(0), args.steps, args.warmup)
+
+    head = results.get("decode_bf16")
+    cpu = None if args.no_cpu or head is None else cpu_baseline(dec_case, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"] if head else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"] if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bf16: M=32 tokens, K=4096, N=4096, 20 adapters, ranks "
+                               "from {16,32,64}, 10% tokens without adapter, seed 0",
+                   "step": "lora_build_segments + lora_shrink_expand_add",
+                   "cold_mall_rotation": head["rotation_copies"] if head else None},
+        "roofline": None if head is None else {
+            "bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": head["hbm_frac"], "traffic": None,
+            "kernel": head["kernel"], "kernel_ms": head["ms_kernel_events"],
+            "alg_bytes_per_launch": head["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "extra": {k: v for k, v in results.items() if k != "decode_bf16"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

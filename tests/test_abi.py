@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every symbol include/mlora.h declares;
+host-only entry points and argument checks work without a GPU (no compute
+call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlora.h")
+LIB = os.path.join(ROOT, "adapter_lora_amd", "libmlora.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
+              "lora_moe_align_run", "lora_moe_gate_up_add", "lora_moe_silu_and_mul",
+              "lora_moe_down_add", "lora_moe_topk_reduce", "lora_workspace_size",
+              "lora_status_string", "lora_read_device_error", "lora_table_plan",
+              "lora_pack_adapter"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "run __graft_entry__.build() first"
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (lora_\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_binding_signature_table_matches_header():
+    from adapter_lora_amd import _abi
+    assert sorted(_abi.SIGNATURES) == declared_functions()
+
+
+def test_host_only_calls():
+    from adapter_lora_amd import _abi
+    import adapter_lora_amd as ml
+    lib = _abi.lib
+    assert lib.lora_abi_version() == _abi.MLORA_ABI_VERSION
+    assert lib.lora_status_string(1) == b"invalid argument"
+    rp, ao, bo, na, nb = ml.lora_table_plan([20, 16, 0, 64, 8], 2, 64, 96)
+    assert rp == [32, 16, 0, 64, 16]
+    # rank-group major: padded 16 slots first (1, then 4), then 32 (0), then 64 (3)
+    assert ao[1] == 0 and ao[4] == 2 * 16 * 64 and ao[0] == 4 * 16 * 64
+    assert ao[3] == ao[0] + 2 * 32 * 64
+    assert na == ao[3] + 2 * 64 * 64
+    assert bo[1] == 0 and bo[4] == 96 * 16 and bo[0] == 2 * 96 * 16 and nb == bo[3] + 96 * 64
+    assert ml.lora_moe_align_capacity(256, 2, 8, 64) == 1024
+    assert ml.lora_moe_align_capacity(3, 2, 2, 2) == 8
+
+
+def test_argument_checks_fail_before_any_launch():
+    from adapter_lora_amd import _abi
+    lib = _abi.lib
+    INV = _abi.LORA_INVALID_ARG
+    null = ctypes.c_void_p(0)
+    assert lib.lora_build_segments(null, -1, 4, null, null, null, null, null) == INV
+    assert lib.lora_build_segments(null, 4, 0, null, null, null, null, null) == INV
+    assert lib.lora_build_segments(null, 4, 4, null, null, null, null, null) == INV
+    w = _abi.lora_weights_t()
+    w.dtype, w.K, w.n_slices, w.L, w.r_max = 1, 100, 1, 4, 16     # K not a multiple of 8
+    assert lib.lora_shrink_expand_add(ctypes.byref(w), null, 0, 1, None, null, 0, null, 0,
+                                      null) == INV
+    w.K = 128
+    w.slice_offsets[0], w.slice_offsets[1] = 0, 128              # pointers still null
+    assert lib.lora_expand_add(ctypes.byref(w), null, 1, None, null, 0, null) == INV
+    assert lib.lora_workspace_size(ctypes.byref(w), 8) == 0      # invalid table -> 0
+    ma = _abi.lora_moe_align_t()
+    ma.max_tokens_padded, ma.block_size_m = 100, 64               # not a multiple of the block
+    assert lib.lora_moe_align_run(null, null, null, 4, 2, 8, 2, ctypes.byref(ma), null) == INV
+    assert lib.lora_moe_silu_and_mul(1, null, 0, null, 0, 4, 12, null) == INV   # I % 8
+    assert lib.lora_moe_topk_reduce(1, null, 0, null, null, 0, 4, 0, 64, null) == INV
+    assert lib.lora_table_plan(2, (ctypes.c_int32 * 2)(8, 65), 1, 64, 64,
+                               (ctypes.c_int32 * 2)(), (ctypes.c_int64 * 2)(),
+                               (ctypes.c_int64 * 2)(), ctypes.byref(ctypes.c_int64()),
+                               ctypes.byref(ctypes.c_int64())) == INV           # rank > 64
