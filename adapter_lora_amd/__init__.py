@@ -14,13 +14,13 @@ from typing import List, Optional, Sequence
 import torch
 
 from ._abi import (LORA_BF16, LORA_F32, LORA_MAX_ADAPTERS, LORA_MAX_RANK,
-                   LORA_MAX_SLICES, LORA_DECODE_MAX_M, LoraError, lib, lora_weights_t,
+                   LORA_MAX_SLICES, LORA_DECODE_MAX_M, LORA_TILE_ROWS, LoraError, lib, lora_weights_t,
                    lora_segments_t, lora_moe_weights_t, lora_moe_align_t, check)
 
 __all__ = [
     "LORA_BF16", "LORA_F32", "LoraError", "LoraTable", "Segments", "Workspace",
     "MoeWeights", "MoeAlign",
-    "lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
+    "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
     "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
@@ -131,18 +131,24 @@ class LoraTable:
 
 # ------------------------------------------------------------------------- segments
 class Segments:
-    """Device buffers of a segment table for up to M_cap tokens and L slots."""
+    """Device buffers of a segment table and its tile schedule for up to
+    M_cap tokens and L slots."""
 
     def __init__(self, M_cap: int, L: int, device="cuda"):
         self.L = int(L)
+        self.max_tiles = max(int(lib.lora_tile_capacity(M_cap, L)), 1)
         self.sorted_idx = torch.empty(max(M_cap, 1), dtype=torch.int32, device=device)
         self.seg_indptr = torch.empty(L + 1, dtype=torch.int32, device=device)
         self.req_to_lora = torch.empty(L, dtype=torch.int32, device=device)
         self.num_segments = torch.empty(1, dtype=torch.int32, device=device)
-        self.c = lora_segments_t(
-            *(ctypes.cast(_ptr(t), ctypes.POINTER(ctypes.c_int32))
-              for t in (self.sorted_idx, self.seg_indptr, self.req_to_lora, self.num_segments)),
-            self.L, 0)
+        self.tile_info = torch.empty(self.max_tiles * 4, dtype=torch.int32, device=device)
+        self.tile_rows = torch.empty(self.max_tiles * LORA_TILE_ROWS, dtype=torch.int32,
+                                     device=device)
+        self.num_tiles = torch.empty(1, dtype=torch.int32, device=device)
+        p32 = lambda t: ctypes.cast(_ptr(t), ctypes.POINTER(ctypes.c_int32))
+        self.c = lora_segments_t(p32(self.sorted_idx), p32(self.seg_indptr), p32(self.req_to_lora),
+                                 p32(self.num_segments), p32(self.tile_info), p32(self.tile_rows),
+                                 p32(self.num_tiles), self.L, self.max_tiles)
 
 
 def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None) -> None:
@@ -153,7 +159,12 @@ def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None) -> None:
         raise LoraError("segment buffers too small")
     check(lib.lora_build_segments(_ptr(ids), M, seg.L, _ptr(seg.sorted_idx), _ptr(seg.seg_indptr),
                                   _ptr(seg.req_to_lora), _ptr(seg.num_segments),
-                                  stream_handle(stream)), "lora_build_segments")
+                                  _ptr(seg.tile_info), _ptr(seg.tile_rows), _ptr(seg.num_tiles),
+                                  seg.max_tiles, stream_handle(stream)), "lora_build_segments")
+
+
+def lora_tile_capacity(M: int, L: int) -> int:
+    return int(lib.lora_tile_capacity(M, L))
 
 
 # ------------------------------------------------------------------------- workspace

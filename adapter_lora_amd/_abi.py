@@ -16,6 +16,7 @@ LORA_RANK_ALIGN = 16
 LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
+LORA_TILE_ROWS = 64
 MLORA_ABI_VERSION = 1
 
 
@@ -46,7 +47,8 @@ class lora_weights_t(ctypes.Structure):
 
 class lora_segments_t(ctypes.Structure):
     _fields_ = [("sorted_idx", PI32), ("seg_indptr", PI32), ("req_to_lora", PI32),
-                ("num_segments", PI32), ("L", I32), ("reserved", I32)]
+                ("num_segments", PI32), ("tile_info", PI32), ("tile_rows", PI32),
+                ("num_tiles", PI32), ("L", I32), ("max_tiles", I32)]
 
 
 class lora_moe_weights_t(ctypes.Structure):
@@ -73,7 +75,8 @@ SIGNATURES = {
     "lora_read_device_error": (I32, [P, PI32, P]),
     "lora_table_plan": (I32, [I32, PI32, I32, I32, I64, PI32, PI64, PI64, PI64, PI64]),
     "lora_pack_adapter": (I32, [I32, I32, I64, I32, I32, I32, P, P, P, P, P]),
-    "lora_build_segments": (I32, [P, I32, I32, P, P, P, P, P]),
+    "lora_tile_capacity": (I32, [I32, I32]),
+    "lora_build_segments": (I32, [P, I32, I32, P, P, P, P, P, P, P, I32, P]),
     "lora_shrink": (I32, [PW, P, I64, I32, PS, P, P, SZ, P]),
     "lora_expand_add": (I32, [PW, P, I32, PS, P, I64, P]),
     "lora_shrink_expand_add": (I32, [PW, P, I64, I32, PS, P, I64, P, SZ, P]),

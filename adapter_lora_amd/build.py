@@ -2,7 +2,8 @@
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled, then linked into adapter_lora_amd/libmlora.so next to
-this file.  Run `python -m adapter_lora_amd.build` or call build().
+this file.  Run `python adapter_lora_amd/build.py` (not `-m`: importing the
+package loads the library) or __graft_entry__.build().
 """
 from __future__ import annotations
 

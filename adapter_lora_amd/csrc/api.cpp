@@ -44,10 +44,12 @@ lora_status check_weights(const lora_weights_t* w) {
     return LORA_OK;
 }
 
-lora_status check_segments(const lora_segments_t* seg, const lora_weights_t* w) {
-    if (!seg || !seg->sorted_idx || !seg->seg_indptr || !seg->req_to_lora || !seg->num_segments)
+lora_status check_segments(const lora_segments_t* seg, const lora_weights_t* w, int M) {
+    if (!seg || !seg->sorted_idx || !seg->seg_indptr || !seg->req_to_lora || !seg->num_segments ||
+        !seg->tile_info || !seg->tile_rows || !seg->num_tiles)
         return LORA_INVALID_ARG;
     if (seg->L != w->L) return LORA_INVALID_ARG;
+    if (seg->max_tiles < lora_tile_capacity(M, w->L)) return LORA_INVALID_ARG;
     return LORA_OK;
 }
 
@@ -77,6 +79,10 @@ LinearArgs make_args(const lora_weights_t* w, const lora_segments_t* seg, int M)
     a.seg_indptr = seg->seg_indptr;
     a.req_to_lora = seg->req_to_lora;
     a.num_segments = seg->num_segments;
+    a.tile_info = seg->tile_info;
+    a.tile_rows = seg->tile_rows;
+    a.num_tiles = seg->num_tiles;
+    a.max_tiles = seg->max_tiles;
     return a;
 }
 
@@ -211,14 +217,22 @@ lora_status lora_pack_adapter(int32_t dtype, int32_t K, int64_t N_total, int32_t
                                         A_dst, B_dst, stream));
 }
 
+int32_t lora_tile_capacity(int32_t M, int32_t L) {
+    if (M < 0 || L < 1) return 0;
+    return M / LORA_TILE_ROWS + std::min(L, M);
+}
+
 lora_status lora_build_segments(const int32_t* ids, int32_t M, int32_t L, int32_t* sorted_idx,
                                 int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
-                                hipStream_t stream) {
+                                int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
+                                int32_t max_tiles, hipStream_t stream) {
     if (M < 0 || M > (1 << 24) || L < 1 || L > LORA_MAX_ADAPTERS) return LORA_INVALID_ARG;
-    if (!seg_indptr || !req_to_lora || !num_segments) return LORA_INVALID_ARG;
-    if (M > 0 && (!ids || !sorted_idx)) return LORA_INVALID_ARG;
+    if (!seg_indptr || !req_to_lora || !num_segments || !num_tiles) return LORA_INVALID_ARG;
+    if (max_tiles < lora_tile_capacity(M, L)) return LORA_INVALID_ARG;
+    if (M > 0 && (!ids || !sorted_idx || !tile_info || !tile_rows)) return LORA_INVALID_ARG;
     return from_hip(launch_build_segments(ids, M, L, sorted_idx, seg_indptr, req_to_lora,
-                                          num_segments, stream));
+                                          num_segments, tile_info, tile_rows, num_tiles,
+                                          max_tiles, stream));
 }
 
 lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int32_t M,
@@ -227,7 +241,7 @@ lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
-    if ((st = check_segments(seg, w)) != LORA_OK) return st;
+    if ((st = check_segments(seg, w, M)) != LORA_OK) return st;
     if (M == 0) return LORA_OK;
     if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
     if (!S || !aligned16(S)) return LORA_INVALID_ARG;
@@ -244,7 +258,7 @@ lora_status lora_expand_add(const lora_weights_t* w, const float* S, int32_t M,
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
-    if ((st = check_segments(seg, w)) != LORA_OK) return st;
+    if ((st = check_segments(seg, w, M)) != LORA_OK) return st;
     if (M == 0) return LORA_OK;
     if (!S || !aligned16(S)) return LORA_INVALID_ARG;
     if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;
@@ -258,7 +272,7 @@ lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
-    if ((st = check_segments(seg, w)) != LORA_OK) return st;
+    if ((st = check_segments(seg, w, M)) != LORA_OK) return st;
     if (M == 0) return LORA_OK;
     if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
     if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;

@@ -56,6 +56,28 @@ template <> struct Io<uint16_t> {
 };
 
 // ----------------------------------------------------------------------------
+// masked vector loads without branches: the load always happens, from `p`
+// when `ok` and otherwise from `safe` (any readable address, e.g. the start
+// of the same tensor), and the result is zeroed by a select.  A conditional
+// load (`ok ? *p : 0`) is compiled into per-dword loads under exec-mask
+// branches; this form stays one dwordx4 / dwordx2 load.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16_if(const void* p, bool ok, const void* safe) {
+    const uint4 v = *reinterpret_cast<const uint4*>(ok ? p : safe);
+    return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 ld8_if(const void* p, bool ok, const void* safe) {
+    const uint2 v = *reinterpret_cast<const uint2*>(ok ? p : safe);
+    return ok ? v : make_uint2(0, 0);
+}
+
+__device__ __forceinline__ float4 ldf4_if(const float* p, bool ok, const float* safe) {
+    const float4 v = *reinterpret_cast<const float4*>(ok ? p : safe);
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ----------------------------------------------------------------------------
 // wavefront reductions
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

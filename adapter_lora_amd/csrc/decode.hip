@@ -120,10 +120,10 @@ constexpr int kTokGroup = 4;                    // token rows accumulated togeth
 template <typename T> struct Raw8 { uint4 q[sizeof(T) / 2]; };
 
 template <typename T>
-__device__ __forceinline__ Raw8<T> ld_raw8(const T* p) {
+__device__ __forceinline__ Raw8<T> ld_raw8_if(const T* p, bool ok, const T* safe) {
     Raw8<T> r;
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.q[i] = reinterpret_cast<const uint4*>(p)[i];
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.q[i] = ld16_if(p + i * (16 / (int)sizeof(T)), ok, safe);
     return r;
 }
 
@@ -200,12 +200,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
         const int k = kbase + st * 512;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (k < a.K) {
-                ar[st][i] = ld_raw8(A + (int64_t)i * a.K + k);
-            } else {
-#pragma unroll
-                for (int q = 0; q < (int)(sizeof(T) / 2); ++q) ar[st][i].q[q] = make_uint4(0, 0, 0, 0);
-            }
+            ar[st][i] = ld_raw8_if(A + (int64_t)i * a.K + k, k < a.K, A);
         }
     }
     const T* X = reinterpret_cast<const T*>(p.x);
@@ -225,12 +220,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
             Raw8<T> xr[kTokGroup];
 #pragma unroll
             for (int u = 0; u < kTokGroup; ++u) {
-                if (k < a.K && t0 + u < v.ms) {
-                    xr[u] = ld_raw8(X + (int64_t)mrow[u] * p.ldx + k);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < (int)(sizeof(T) / 2); ++q) xr[u].q[q] = make_uint4(0, 0, 0, 0);
-                }
+                xr[u] = ld_raw8_if(X + (int64_t)mrow[u] * p.ldx + k, k < a.K && t0 + u < v.ms, X);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -278,8 +268,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
 #pragma unroll
     for (int q = 0; q < CPR; ++q) {
         const int n = nw + q * RPI + rsub;
-        braw[q] = (gin && n < n1) ? *reinterpret_cast<const uint4*>(B + (int64_t)n * rp + g * EPC)
-                                  : make_uint4(0, 0, 0, 0);
+        braw[q] = ld16_if(B + (int64_t)n * rp + g * EPC, gin && n < n1, B);
     }
     float yv[kTokGroup];
 #pragma unroll

@@ -30,6 +30,10 @@ struct LinearArgs {
     const int32_t* seg_indptr;
     const int32_t* req_to_lora;
     const int32_t* num_segments;
+    const int32_t* tile_info;   // [max_tiles][4]: segment, adapter, first position, rows
+    const int32_t* tile_rows;   // [max_tiles][64]: token index per row, -1 past the rows
+    const int32_t* num_tiles;
+    int max_tiles;
 };
 
 // K columns handled by one shrink work unit (fused decode and MFMA shrink).
@@ -62,9 +66,13 @@ LinearWs linear_ws_layout(int M, int K, int cols, int L, int n_sl);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
+// rows per tile of the tile schedule
+constexpr int kRowTileRows = 64;
+
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
                                  int32_t* seg_indptr, int32_t* req_to_lora,
-                                 int32_t* num_segments, hipStream_t st);
+                                 int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
+                                 int32_t* num_tiles, int max_tiles, hipStream_t st);
 
 hipError_t launch_pack_adapter(int dtype, int K, int64_t N, int n_sl, int rank, int rank_pad,
                                const void* A_src, const void* B_src, void* A_dst, void* B_dst,

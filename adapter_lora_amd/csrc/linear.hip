@@ -1,102 +1,105 @@
-// Dense multi-LoRA shrink and expand over a segment table
+// Dense multi-LoRA shrink and expand over the tile schedule
 // ("vLLM-Ascend dynamic LoRA operator" walkthrough, section 2.3: per segment
 // X_seg A_i^T, then S B_i^T added to the y_base rows of the segment's tokens;
-// every segment is served by one launch).
+// every segment is served by one launch; section 2.4: the block -> segment ->
+// rank mapping is settled before the product kernels run).
 //
-// Work units never straddle a segment: a segment of m_s tokens is cut into
-// ceil(m_s / 64) row tiles, and each launch's grid enumerates
-// (row tile, K chunk) for the shrink or (row tile, 256-column tile) for the
-// expand.  Which segment a row tile belongs to is found on the device from
-// seg_indptr by a wavefront prefix scan (section 2.4 asks for the "which
-// block, which segment, which rank" mapping to be settled outside the inner
-// loops; here it is settled once per workgroup, before any data moves).
+// A work unit is one 64-row tile of the schedule (tiles never straddle a
+// segment) and either a (K chunk, S column group) for the shrink or a run of
+// 256-column output tiles inside one slice for the expand.  A workgroup
+// learns everything about its tile with independent loads issued together
+// (tile descriptor, the tile's 64 token indices, and for tables of up to 256
+// slots every slot's rank and weight offset), so its data loads start after
+// one memory round trip.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
 
 namespace mlora {
 
-constexpr int kRowTile = 64;
+constexpr int kRowTile = kRowTileRows;
+static_assert(kRowTile == 64, "tile functions assume 64-row tiles");
 
-struct UnitInfo {
-    int seg;      // segment index, -1 if the unit does not exist
-    int pbeg;     // first sorted position of the tile
-    int n;        // rows in the tile
+struct TileView {
+    int seg;       // -1 when the tile does not exist
+    int id;
+    int pbeg;
+    int n;
+    int rp;
+    int64_t off;
+    int row;       // lane i: token index of row i (-1 past n)
 };
 
-// Wave 0 finds row tile u; result broadcast through LDS.
-__device__ __forceinline__ UnitInfo find_row_tile(const LinearArgs& a, int u, int* sh) {
-    if (threadIdx.x < kWave) {
-        const int lane = lane_id();
-        const int nseg = a.num_segments[0];
-        int run = 0, found = -1, pbeg = 0, nr = 0;
-        for (int s0 = 0; s0 < nseg && found < 0; s0 += kWave) {
-            const int s = s0 + lane;
-            int b = 0, e = 0, t = 0;
-            if (s < nseg) {
-                b = a.seg_indptr[s];
-                e = a.seg_indptr[s + 1];
-                t = (e - b + kRowTile - 1) / kRowTile;
-            }
-            int inc = t;
+__device__ __forceinline__ TileView tile_view(const LinearArgs& a, int t, bool a_side) {
+    const int lane = lane_id();
+    const int64_t* offs = a_side ? a.a_off : a.b_off;
+    TileView v;
+    const int nt = a.num_tiles[0];
+    const int tt = t < a.max_tiles ? t : 0;
+    v.seg = a.tile_info[tt * 4 + 0];
+    v.id = a.tile_info[tt * 4 + 1];
+    v.pbeg = a.tile_info[tt * 4 + 2];
+    v.n = a.tile_info[tt * 4 + 3];
+    v.row = a.tile_rows[(int64_t)tt * kRowTile + lane];
+    if (a.L <= 4 * kWave) {
+        int rk[4];
+        int64_t of[4];
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int v = __shfl_up(inc, o, kWave);
-                if (lane >= o) inc += v;
-            }
-            const int excl = run + inc - t;
-            const bool mine = (s < nseg) && u >= excl && u < excl + t;
-            const unsigned long long bal = __ballot(mine);
-            if (bal) {
-                const int src = __ffsll((unsigned long long)bal) - 1;
-                found = __shfl(s, src, kWave);
-                const int mt = u - __shfl(excl, src, kWave);
-                pbeg = __shfl(b, src, kWave) + mt * kRowTile;
-                nr = min(kRowTile, __shfl(e, src, kWave) - pbeg);
-            }
-            run += __shfl(inc, kWave - 1, kWave);
+        for (int q = 0; q < 4; ++q) {
+            const int j = q * kWave + lane;
+            rk[q] = j < a.L ? a.rank[j] : 0;
+            of[q] = j < a.L ? offs[j] : 0;
         }
-        if (lane == 0) {
-            sh[0] = found;
-            sh[1] = pbeg;
-            sh[2] = nr;
-        }
+        const int id = (t < nt && v.id >= 0 && v.id < a.L) ? v.id : 0;
+        const int q = id / kWave, src = id % kWave;
+        const int r_sel = q == 0 ? rk[0] : q == 1 ? rk[1] : q == 2 ? rk[2] : rk[3];
+        const int64_t o_sel = q == 0 ? of[0] : q == 1 ? of[1] : q == 2 ? of[2] : of[3];
+        v.rp = __shfl(r_sel, src, kWave);
+        v.off = __shfl(o_sel, src, kWave);
+    } else {
+        const int id = (t < nt && v.id >= 0 && v.id < a.L) ? v.id : 0;
+        v.rp = a.rank[id];
+        v.off = offs[id];
     }
-    __syncthreads();
-    return UnitInfo{sh[0], sh[1], sh[2]};
+    if (t >= nt) v.seg = -1;
+    return v;
 }
 
 // ---------------------------------------------------------------------------
 // shrink: P[c][p][col] partial sums (p = sorted position, col = sl*r_max + j)
+// unit = (tile, K chunk c, column group cg of 64 S columns)
 // ---------------------------------------------------------------------------
-template <typename T, int NCB>
+template <typename T>
 __global__ __launch_bounds__(kTileThreads) void k_shrink_dense(LinearArgs a, const T* __restrict__ x,
                                                                 int64_t ldx, float* __restrict__ P,
-                                                                int C) {
-    __shared__ int sh[4];
+                                                                int C, int G, int units) {
     __shared__ int s_in[kRowTile], s_out[kRowTile];
-    const int u = blockIdx.x / C;
-    const int c = blockIdx.x % C;
-    const UnitInfo ui = find_row_tile(a, u, sh);
-    if (ui.seg < 0) return;
-    const int id = a.req_to_lora[ui.seg];
-    const int rp = a.rank[id];
-    for (int i = threadIdx.x; i < ui.n; i += kTileThreads) {
-        s_in[i] = a.sorted_idx[ui.pbeg + i];
-        s_out[i] = ui.pbeg + i;
+    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    if (u >= units) return;
+    const int tile = u / (C * G);
+    const int c = (u / G) % C;
+    const int cg = u % G;
+    const TileView v = tile_view(a, tile, true);
+    if (v.seg < 0) return;
+    if (threadIdx.x < kRowTile) {
+        s_in[threadIdx.x] = v.row;
+        s_out[threadIdx.x] = (int)threadIdx.x < v.n ? v.pbeg + (int)threadIdx.x : -1;
     }
     __syncthreads();
-    const RowSet rs{ui.n, kRowTile, s_in, s_out};
-    const int k0 = c * kKChunk;
-    const int k1 = min(a.K, k0 + kKChunk);
+    const RowSet rs{v.n, kRowTile, s_in, s_out};
     float* Pc = P + (int64_t)c * a.M * a.cols;
-    const T* A = reinterpret_cast<const T*>(a.A) + a.a_off[id];
+    const T* A = reinterpret_cast<const T*>(a.A) + v.off;
     if constexpr (sizeof(T) == 2) {
-        shrink_tile_bf16<NCB>(rs, reinterpret_cast<const uint16_t*>(x), ldx,
-                              reinterpret_cast<const uint16_t*>(A), a.K, rp, a.r_max, k0, k1,
-                              Pc, a.cols);
+        __shared__ uint4 sA[kShrinkLds / 16];
+        const int k0 = c * kShrinkK;
+        const int k1 = min(a.K, k0 + kShrinkK);
+        shrink_group_bf16(rs, reinterpret_cast<const uint16_t*>(x), ldx,
+                          reinterpret_cast<const uint16_t*>(A), a.K, a.n_sl, v.rp, a.r_max, cg,
+                          k0, k1, Pc, a.cols, sA);
     } else {
-        shrink_tile_simple<T>(rs, x, ldx, A, a.K, a.n_sl, rp, a.r_max, k0, k1, Pc, a.cols);
+        const int k0 = c * kKChunk;
+        const int k1 = min(a.K, k0 + kKChunk);
+        shrink_tile_simple<T>(rs, x, ldx, A, a.K, a.n_sl, v.rp, a.r_max, k0, k1, Pc, a.cols);
     }
 }
 
@@ -120,99 +123,69 @@ __global__ void k_reduce_partials(const float* __restrict__ P, int C, int64_t cs
 
 // ---------------------------------------------------------------------------
 // expand: y[sorted_idx[p], n] += S[p, sl, :rp] . B_i[n, :rp]
+// unit = (tile, group g of up to `tpw` consecutive 256-column tiles of one slice)
 // ---------------------------------------------------------------------------
-struct TileMap {
-    int n_tiles;
-    int tile_start[LORA_MAX_SLICES + 1];
+struct GroupMap {
+    int n_groups;                              // groups per row tile, all slices
+    int tpw;                                   // 256-column tiles per group
+    int group_start[LORA_MAX_SLICES + 1];      // first group of each slice
 };
 
-__device__ __forceinline__ void tile_cols(const LinearArgs& a, const TileMap& tm, int t, int* sl,
-                                          int* n0, int* n1) {
-    int s = 0;
-    while (s + 1 < a.n_sl && t >= tm.tile_start[s + 1]) ++s;
-    *sl = s;
-    *n0 = (int)(a.slice_off[s] + (int64_t)(t - tm.tile_start[s]) * kNTile);
-    *n1 = (int)min((int64_t)*n0 + kNTile, a.slice_off[s + 1]);
-}
-
 template <typename T>
-__global__ __launch_bounds__(kTileThreads) void k_expand_dense(LinearArgs a, TileMap tm,
+__global__ __launch_bounds__(kTileThreads) void k_expand_dense(LinearArgs a, GroupMap gm,
                                                                 const float* __restrict__ S,
-                                                                T* __restrict__ y, int64_t ldy) {
-    __shared__ int sh[4];
+                                                                T* __restrict__ y, int64_t ldy,
+                                                                int units) {
     __shared__ int s_in[kRowTile], s_out[kRowTile];
-    const int u = blockIdx.x / tm.n_tiles;
-    const int t = blockIdx.x % tm.n_tiles;
-    const UnitInfo ui = find_row_tile(a, u, sh);
-    if (ui.seg < 0) return;
-    const int id = a.req_to_lora[ui.seg];
-    const int rp = a.rank[id];
-    if (rp == 0) return;
-    for (int i = threadIdx.x; i < ui.n; i += kTileThreads) {
-        s_in[i] = ui.pbeg + i;
-        s_out[i] = a.sorted_idx[ui.pbeg + i];
+    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    if (u >= units) return;
+    const int tile = u / gm.n_groups;
+    const int g = u % gm.n_groups;
+    const TileView v = tile_view(a, tile, false);
+    if (v.seg < 0 || v.rp == 0) return;
+    if (threadIdx.x < kRowTile) {
+        s_in[threadIdx.x] = (int)threadIdx.x < v.n ? v.pbeg + (int)threadIdx.x : -1;
+        s_out[threadIdx.x] = v.row;
     }
     __syncthreads();
-    int sl, n0, n1;
-    tile_cols(a, tm, t, &sl, &n0, &n1);
-    const RowSet rs{ui.n, kRowTile, s_in, s_out};
-    const T* B = reinterpret_cast<const T*>(a.B) + a.b_off[id];
+    int sl = 0;
+    while (sl + 1 < a.n_sl && g >= gm.group_start[sl + 1]) ++sl;
+    const int64_t nb = a.slice_off[sl] + (int64_t)(g - gm.group_start[sl]) * gm.tpw * kNTile;
+    const int n_begin = (int)nb;
+    const int n_end = (int)min(nb + (int64_t)gm.tpw * kNTile, a.slice_off[sl + 1]);
+    const RowSet rs{v.n, kRowTile, s_in, s_out};
+    const T* B = reinterpret_cast<const T*>(a.B) + v.off;
     if constexpr (sizeof(T) == 2) {
-        expand_tile_bf16(rs, S, a.cols, sl * a.r_max, reinterpret_cast<const uint16_t*>(B), rp, n0,
-                         n1, reinterpret_cast<uint16_t*>(y), ldy);
+        __shared__ uint16_t sHi[64 * kSLds], sLo[64 * kSLds];
+        expand_rows_bf16(rs, S, a.cols, sl * a.r_max, reinterpret_cast<const uint16_t*>(B), v.rp,
+                         n_begin, n_end, reinterpret_cast<uint16_t*>(y), ldy, sHi, sLo);
     } else {
-        expand_tile_simple<T>(rs, S, a.cols, sl * a.r_max, B, rp, n0, n1, y, ldy);
+        for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
+            expand_tile_simple<T>(rs, S, a.cols, sl * a.r_max, B, v.rp, n0, min(n0 + kNTile, n_end),
+                                  y, ldy);
     }
 }
 
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-static int row_tiles_max(const LinearArgs& a) { return a.M / kRowTile + a.s_max; }
-
-TileMap make_tile_map(const LinearArgs& a) {
-    TileMap tm{};
-    int t = 0;
-    for (int s = 0; s < a.n_sl; ++s) {
-        tm.tile_start[s] = t;
-        const int64_t n = a.slice_off[s + 1] - a.slice_off[s];
-        t += (int)((n + kNTile - 1) / kNTile);
-    }
-    tm.tile_start[a.n_sl] = t;
-    tm.n_tiles = t;
-    return tm;
-}
-
-template <typename T, int NCB>
-static void launch_shrink_ncb(const LinearArgs& a, const void* x, int64_t ldx, float* P, int C,
-                              hipStream_t st) {
-    const unsigned grid = (unsigned)(row_tiles_max(a) * C);
-    hipLaunchKernelGGL((k_shrink_dense<T, NCB>), dim3(grid), dim3(kTileThreads), 0, st, a,
-                       reinterpret_cast<const T*>(x), ldx, P, C);
-}
-
-template <typename T>
-static hipError_t launch_shrink_t(const LinearArgs& a, const void* x, int64_t ldx, float* P,
-                                  int C, hipStream_t st) {
-    const int ncb = a.cols / 16;
-    switch (ncb) {
-#define MLORA_NCB(n) case n: launch_shrink_ncb<T, n>(a, x, ldx, P, C, st); break;
-        MLORA_NCB(1) MLORA_NCB(2) MLORA_NCB(3) MLORA_NCB(4) MLORA_NCB(5) MLORA_NCB(6)
-        MLORA_NCB(7) MLORA_NCB(8) MLORA_NCB(9) MLORA_NCB(10) MLORA_NCB(11) MLORA_NCB(12)
-        MLORA_NCB(13) MLORA_NCB(14) MLORA_NCB(15) MLORA_NCB(16)
-#undef MLORA_NCB
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
+static unsigned grid_of(int units) { return (unsigned)((units + kXcds - 1) / kXcds * kXcds); }
 
 hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float* S, void* ws,
                          hipStream_t st) {
-    const int C = kchunks(a.K);
+    const bool bf16 = a.dtype == LORA_BF16;
+    const int C = bf16 ? (a.K + kShrinkK - 1) / kShrinkK : kchunks(a.K);
+    const int G = bf16 ? (a.cols + kGroupCols - 1) / kGroupCols : 1;
+    const int units = a.max_tiles * C * G;
     const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.L, a.n_sl);
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.partial);
-    hipError_t e = (a.dtype == LORA_BF16) ? launch_shrink_t<uint16_t>(a, x, ldx, P, C, st)
-                                          : launch_shrink_t<float>(a, x, ldx, P, C, st);
+    if (bf16)
+        hipLaunchKernelGGL(k_shrink_dense<uint16_t>, dim3(grid_of(units)), dim3(kTileThreads), 0, st,
+                           a, reinterpret_cast<const uint16_t*>(x), ldx, P, C, G, units);
+    else
+        hipLaunchKernelGGL(k_shrink_dense<float>, dim3(grid_of(units)), dim3(kTileThreads), 0, st,
+                           a, reinterpret_cast<const float*>(x), ldx, P, C, G, units);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int64_t total4 = (int64_t)a.M * a.cols / 4;
     int64_t blocks = (total4 + 255) / 256;
@@ -223,16 +196,40 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
     return hipGetLastError();
 }
 
+// Column tiles per workgroup: about two workgroups per CU (the expand holds
+// two resident per CU), each walking consecutive 256-column tiles with S
+// staged once and the next tile's loads in flight.
+static GroupMap make_group_map(const LinearArgs& a) {
+    int tiles = 0;
+    for (int s = 0; s < a.n_sl; ++s)
+        tiles += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+    const int target = 512;
+    int tpw = (int)((int64_t)a.max_tiles * tiles / target);
+    if (tpw < 1) tpw = 1;
+    if (tpw > 8) tpw = 8;
+    GroupMap gm{};
+    gm.tpw = tpw;
+    int g = 0;
+    for (int s = 0; s < a.n_sl; ++s) {
+        gm.group_start[s] = g;
+        const int t = (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+        g += (t + tpw - 1) / tpw;
+    }
+    gm.group_start[a.n_sl] = g;
+    gm.n_groups = g;
+    return gm;
+}
+
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st) {
-    const TileMap tm = make_tile_map(a);
-    const unsigned grid = (unsigned)(row_tiles_max(a) * tm.n_tiles);
+    const GroupMap gm = make_group_map(a);
+    const int units = a.max_tiles * gm.n_groups;
     if (a.dtype == LORA_BF16) {
-        hipLaunchKernelGGL(k_expand_dense<uint16_t>, dim3(grid), dim3(kTileThreads), 0, st, a, tm,
-                           S, reinterpret_cast<uint16_t*>(y), ldy);
+        hipLaunchKernelGGL(k_expand_dense<uint16_t>, dim3(grid_of(units)), dim3(kTileThreads), 0, st,
+                           a, gm, S, reinterpret_cast<uint16_t*>(y), ldy, units);
     } else {
-        hipLaunchKernelGGL(k_expand_dense<float>, dim3(grid), dim3(kTileThreads), 0, st, a, tm, S,
-                           reinterpret_cast<float*>(y), ldy);
+        hipLaunchKernelGGL(k_expand_dense<float>, dim3(grid_of(units)), dim3(kTileThreads), 0, st, a,
+                           gm, S, reinterpret_cast<float*>(y), ldy, units);
     }
     return hipGetLastError();
 }

@@ -163,29 +163,35 @@ __device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool sh
     return MoeUnit{true, e};
 }
 
-template <typename T, int NCB>
+template <typename T>
 __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int which,
                                                               const T* __restrict__ in,
                                                               int64_t ld_in, float* __restrict__ P,
-                                                              int C, int K) {
+                                                              int C, int K, int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     const int nblk = a.max_tokens_padded / a.block_size_m;
-    const int unit = blockIdx.x / C;
-    const int c = blockIdx.x % C;
-    const int l = unit / nblk, b = unit % nblk;
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    if (unit >= units) return;
+    const int blk = unit / C;
+    const int c = unit % C;
+    const int l = blk / nblk, b = blk % nblk;
     const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out);
     if (!mu.ok) return;
     const int64_t ew = (int64_t)l * a.E + mu.e;
     const T* A = reinterpret_cast<const T*>(which == 0 ? a.A_gu : a.A_d) + ew * a.r * K;
     const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
-    const int k0 = c * kKChunk;
-    const int k1 = min(K, k0 + kKChunk);
     const int rows = a.L * a.max_tokens_padded;
     float* Pc = P + (int64_t)c * rows * a.r;
     if constexpr (sizeof(T) == 2) {
-        shrink_tile_bf16<NCB>(rs, reinterpret_cast<const uint16_t*>(in), ld_in,
-                              reinterpret_cast<const uint16_t*>(A), K, a.r, a.r, k0, k1, Pc, a.r);
+        __shared__ uint4 sA[kShrinkLds / 16];
+        const int k0 = c * kShrinkK;
+        const int k1 = min(K, k0 + kShrinkK);
+        shrink_group_bf16(rs, reinterpret_cast<const uint16_t*>(in), ld_in,
+                          reinterpret_cast<const uint16_t*>(A), K, 1, a.r, a.r, 0, k0, k1, Pc,
+                          a.r, sA);
     } else {
+        const int k0 = c * kKChunk;
+        const int k1 = min(K, k0 + kKChunk);
         shrink_tile_simple<T>(rs, in, ld_in, A, K, 1, a.r, a.r, k0, k1, Pc, a.r);
     }
 }
@@ -213,24 +219,29 @@ template <typename T>
 __global__ __launch_bounds__(kTileThreads) void k_moe_expand(MoeArgs a, int which,
                                                               const float* __restrict__ S,
                                                               T* __restrict__ out, int64_t ld_out,
-                                                              int N, int n_tiles) {
+                                                              int N, int n_groups, int tpw,
+                                                              int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     const int nblk = a.max_tokens_padded / a.block_size_m;
-    const int unit = blockIdx.x / n_tiles;
-    const int t = blockIdx.x % n_tiles;
-    const int l = unit / nblk, b = unit % nblk;
+    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    if (unit >= units) return;
+    const int blk = unit / n_groups;
+    const int g = unit % n_groups;
+    const int l = blk / nblk, b = blk % nblk;
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out);
     if (!mu.ok) return;
     const int64_t ew = (int64_t)l * a.E + mu.e;
     const T* B = reinterpret_cast<const T*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
-    const int n0 = t * kNTile;
-    const int n1 = min(N, n0 + kNTile);
+    const int n_begin = g * tpw * kNTile;
+    const int n_end = min(N, n_begin + tpw * kNTile);
     if constexpr (sizeof(T) == 2) {
-        expand_tile_bf16(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n0, n1,
-                         reinterpret_cast<uint16_t*>(out), ld_out);
+        __shared__ uint16_t sHi[64 * kSLds], sLo[64 * kSLds];
+        expand_rows_bf16(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin, n_end,
+                         reinterpret_cast<uint16_t*>(out), ld_out, sHi, sLo);
     } else {
-        expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, n1, out, ld_out);
+        for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
+            expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out);
     }
 }
 
@@ -239,22 +250,15 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
                               void* out, int64_t ld_out, void* ws, hipStream_t st) {
     const int K = which == 0 ? a.H : a.I;
     const int N = which == 0 ? 2 * a.I : a.H;
-    const int C = kchunks(K);
+    const int C = sizeof(T) == 2 ? (K + kShrinkK - 1) / kShrinkK : kchunks(K);
     const int nblk = a.max_tokens_padded / a.block_size_m;
     const MoeWs W = moe_ws_layout(a.L, a.max_tokens_padded, a.r, a.H > a.I ? a.H : a.I);
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.partial);
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
-    const unsigned g1 = (unsigned)(a.L * nblk * C);
-    switch (a.r / 16) {
-#define MLORA_MOE_NCB(n)                                                                          \
-    case n:                                                                                       \
-        hipLaunchKernelGGL((k_moe_shrink<T, n>), dim3(g1), dim3(kTileThreads), 0, st, a, which,   \
-                           reinterpret_cast<const T*>(in), ld_in, P, C, K);                       \
-        break;
-        MLORA_MOE_NCB(1) MLORA_MOE_NCB(2) MLORA_MOE_NCB(3) MLORA_MOE_NCB(4)
-#undef MLORA_MOE_NCB
-        default: return hipErrorInvalidValue;
-    }
+    const int units = a.L * nblk * C;
+    const unsigned g1 = (unsigned)((units + 7) / 8 * 8);
+    hipLaunchKernelGGL((k_moe_shrink<T>), dim3(g1), dim3(kTileThreads), 0, st, a, which,
+                       reinterpret_cast<const T*>(in), ld_in, P, C, K, units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
@@ -265,9 +269,14 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_tiles = (N + kNTile - 1) / kNTile;
-    const unsigned g2 = (unsigned)(a.L * nblk * n_tiles);
+    int tpw = (int)((int64_t)a.L * nblk * n_tiles / 512);
+    if (tpw < 1) tpw = 1;
+    if (tpw > 8) tpw = 8;
+    const int n_groups = (n_tiles + tpw - 1) / tpw;
+    const int units2 = a.L * nblk * n_groups;
+    const unsigned g2 = (unsigned)((units2 + 7) / 8 * 8);
     hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
-                       reinterpret_cast<T*>(out), ld_out, N, n_tiles);
+                       reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2);
     return hipGetLastError();
 }
 

@@ -10,6 +10,12 @@
 //      equal buckets are found with one ballot per id bit, so a token's rank
 //      among its equals is a popcount; earlier wavefronts' counts per bucket
 //      come from a small LDS table.  Order inside a bucket is token order.
+// It also writes the tile schedule the shrink / expand kernels run on (the
+// walkthrough's section 2.4: which block, which segment, which rank is worked
+// out before the product kernels start): every segment is cut into tiles of
+// 64 sorted positions, and each tile records its segment, adapter, first
+// position, row count and its 64 token indices, so a product workgroup finds
+// everything about its rows in one memory round trip.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,17 +28,23 @@ constexpr int kCachedTiles = 8;
 __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     const int32_t* __restrict__ ids, int M, int L, int32_t* __restrict__ sorted_idx,
     int32_t* __restrict__ seg_indptr, int32_t* __restrict__ req_to_lora,
-    int32_t* __restrict__ num_segments) {
+    int32_t* __restrict__ num_segments, int32_t* __restrict__ tile_info,
+    int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles, int max_tiles) {
     extern __shared__ int lds[];
     const int NB = L + 1;
-    int* count = lds;               // [NB]
-    int* base = lds + NB;           // [NB]   running output position per bucket
-    int* wcnt = lds + 2 * NB;       // [kSegWaves][NB] per-tile, per-wave bucket counts
+    int* count = lds;                    // [NB]
+    int* base = count + NB;              // [NB]  running output position per bucket
+    int* bstart = base + NB;             // [NB]  first sorted position of bucket b
+    int* btile = bstart + NB;            // [NB]  first tile of bucket b's segment
+    int* stile = btile + NB;             // [NB]  first tile of segment s (stile[nseg] = total)
+    int* sbucket = stile + NB;           // [NB]  adapter id of segment s
+    int* wcnt = sbucket + NB;            // [kSegWaves][NB] per-tile, per-wave bucket counts
+    __shared__ int s_segs, s_tiles;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
 
-    for (int i = tid; i < NB * (2 + kSegWaves); i += kSegThreads) lds[i] = 0;
+    for (int i = tid; i < NB * (6 + kSegWaves); i += kSegThreads) lds[i] = 0;
     __syncthreads();
 
     // bucket of each of this thread's tokens; the first kCachedTiles tiles stay
@@ -58,37 +70,77 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     __syncthreads();
 
     if (wave == 0) {
-        int run = 0, segs = 0;
+        int run = 0, segs = 0, trun = 0;
         for (int b0 = 0; b0 < NB; b0 += kWave) {
             const int b = b0 + lane;
             const int c = (b < NB) ? count[b] : 0;
-            int inc = c;
+            const bool present = (b < L) && (c > 0);
+            const int nt = present ? (c + kRowTileRows - 1) / kRowTileRows : 0;
+            int inc = c, tinc = nt;
 #pragma unroll
             for (int o = 1; o < kWave; o <<= 1) {
                 const int t = __shfl_up(inc, o, kWave);
-                if (lane >= o) inc += t;
+                const int u = __shfl_up(tinc, o, kWave);
+                if (lane >= o) {
+                    inc += t;
+                    tinc += u;
+                }
             }
             const int excl = run + inc - c;
-            if (b < NB) base[b] = excl;
-            const bool present = (b < L) && (c > 0);
+            const int texcl = trun + tinc - nt;
+            if (b < NB) {
+                base[b] = excl;
+                bstart[b] = excl;
+                btile[b] = texcl;
+            }
             const unsigned long long bal = __ballot(present);
             const int s = segs + __popcll(bal & ((1ull << lane) - 1ull));
             if (present) {
                 req_to_lora[s] = b;
                 seg_indptr[s + 1] = excl + c;
+                stile[s] = texcl;
+                sbucket[s] = b;
             }
             run += __shfl(inc, kWave - 1, kWave);
+            trun += __shfl(tinc, kWave - 1, kWave);
             segs += __popcll(bal);
         }
         const int m_valid = run - count[L];
         if (lane == 0) {
             seg_indptr[0] = 0;
             num_segments[0] = segs;
+            num_tiles[0] = trun;
+            stile[segs] = trun;
+            s_segs = segs;
+            s_tiles = trun;
         }
         for (int s = segs + 1 + lane; s <= L; s += kWave) seg_indptr[s] = m_valid;
         for (int s = segs + lane; s < L; s += kWave) req_to_lora[s] = -1;
     }
     __syncthreads();
+
+    // tile schedule: per 64-row tile its segment, adapter, first position and
+    // row count; rows past the count are marked -1 in tile_rows
+    {
+        const int segs = s_segs;
+        const int tiles = min(s_tiles, max_tiles);
+        for (int t = tid; t < tiles; t += kSegThreads) {
+            int lo = 0, hi = segs - 1;                 // last s with stile[s] <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (stile[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int b = sbucket[lo];
+            const int i = t - stile[lo];
+            const int beg = bstart[b] + i * kRowTileRows;
+            const int n = min(kRowTileRows, count[b] - i * kRowTileRows);
+            tile_info[t * 4 + 0] = lo;
+            tile_info[t * 4 + 1] = b;
+            tile_info[t * 4 + 2] = beg;
+            tile_info[t * 4 + 3] = n;
+            for (int r = n; r < kRowTileRows; ++r) tile_rows[t * kRowTileRows + r] = -1;
+        }
+    }
 
     const int nbits = 32 - __clz(L);          // enough bits for buckets 0..L
     const unsigned long long lt = (1ull << lane) - 1ull;
@@ -110,6 +162,11 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
             int pos = base[b] + rank_w;
             for (int w = 0; w < wave; ++w) pos += wcnt[w * NB + b];
             sorted_idx[pos] = m;
+            if (b < L) {
+                const int rel = pos - bstart[b];
+                const int t = btile[b] + rel / kRowTileRows;
+                if (t < max_tiles) tile_rows[t * kRowTileRows + rel % kRowTileRows] = m;
+            }
         }
         __syncthreads();
         if (leader) {
@@ -135,10 +192,12 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
 
 hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
                                  int32_t* seg_indptr, int32_t* req_to_lora,
-                                 int32_t* num_segments, hipStream_t st) {
-    const size_t lds = (size_t)(L + 1) * (2 + kSegWaves) * sizeof(int);
+                                 int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
+                                 int32_t* num_tiles, int max_tiles, hipStream_t st) {
+    const size_t lds = (size_t)(L + 1) * (6 + kSegWaves) * sizeof(int);
     hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kSegThreads), lds, st, ids, M, L,
-                       sorted_idx, seg_indptr, req_to_lora, num_segments);
+                       sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
+                       num_tiles, max_tiles);
     return hipGetLastError();
 }
 

@@ -102,14 +102,26 @@ typedef struct lora_weights {
  *                      entries past num_segments equal the number of tokens with an adapter;
  *   req_to_lora  [L]   adapter id of segment s; -1 past num_segments;
  *   num_segments [1]   number of non-empty segments.
+ * Tile schedule (walkthrough s2.4: block -> segment -> rank settled before
+ * the product kernels run): each segment is cut into tiles of
+ * LORA_TILE_ROWS sorted positions.
+ *   tile_info    [max_tiles][4]  segment, adapter id, first sorted position, rows;
+ *   tile_rows    [max_tiles][LORA_TILE_ROWS] token index of each row, -1 past the rows;
+ *   num_tiles    [1]   number of tiles;
+ *   max_tiles    capacity, >= lora_tile_capacity(M, L).
  */
+#define LORA_TILE_ROWS 64
+
 typedef struct lora_segments {
     const int32_t* sorted_idx;   /* device */
     const int32_t* seg_indptr;   /* device */
     const int32_t* req_to_lora;  /* device */
     const int32_t* num_segments; /* device */
+    const int32_t* tile_info;    /* device */
+    const int32_t* tile_rows;    /* device */
+    const int32_t* num_tiles;    /* device */
     int32_t L;                   /* capacity the table was built with (== weights L) */
-    int32_t reserved;
+    int32_t max_tiles;           /* tile capacity the table was built with */
 } lora_segments_t;
 
 /* ---------------------------------------------------------------- common */
@@ -167,19 +179,26 @@ lora_status lora_pack_adapter(int32_t dtype, int32_t K, int64_t N_total, int32_t
 
 /* ---------------------------------------------------------------- dense multi-LoRA */
 
+/* Tile capacity for M tokens and L slots: floor(M / LORA_TILE_ROWS) + min(L, M). */
+int32_t lora_tile_capacity(int32_t M, int32_t L);
+
 /*
  * lora_build_segments (Ascend walkthrough s2.3; one workgroup, stable
- * counting sort on the device).
+ * counting sort on the device) and the tile schedule.
  *   ids device [M] int32: adapter id per token; -1 (or any id outside
  *       [0, L)) means no adapter.
  *   outputs device: sorted_idx [M], seg_indptr [L+1], req_to_lora [L],
- *       num_segments [1], as described for lora_segments_t.
- * 0 <= M <= 2^24, 1 <= L <= LORA_MAX_ADAPTERS.  M == 0 still writes the
- * (empty) table.
+ *       num_segments [1], tile_info [max_tiles][4],
+ *       tile_rows [max_tiles][LORA_TILE_ROWS], num_tiles [1], as described
+ *       for lora_segments_t.
+ * 0 <= M <= 2^24, 1 <= L <= LORA_MAX_ADAPTERS,
+ * max_tiles >= lora_tile_capacity(M, L).  M == 0 still writes the (empty)
+ * table.
  */
 lora_status lora_build_segments(const int32_t* ids, int32_t M, int32_t L, int32_t* sorted_idx,
                                 int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
-                                hipStream_t stream);
+                                int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
+                                int32_t max_tiles, hipStream_t stream);
 
 /*
  * lora_shrink (Ascend walkthrough s2.2-s2.3, first product; SGLang

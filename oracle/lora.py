@@ -71,6 +71,27 @@ def build_segments(ids: Sequence[int], L: int) -> Tuple[np.ndarray, np.ndarray, 
     return sorted_idx, seg_indptr, req_to_lora, S
 
 
+def tile_schedule(ids: Sequence[int], L: int, rows: int = 64):
+    """Tile schedule over the segment table (Ascend walkthrough, section 2.4:
+    which block belongs to which segment, and its rank, is worked out before
+    the kernels run).  Segments in order, each cut into ceil(count / rows)
+    tiles of consecutive sorted positions.
+    Returns (info int32[T, 4] = (segment, adapter id, first position, rows),
+    tile_rows int32[T, rows] = token index per row, -1 past the rows)."""
+    sorted_idx, seg_indptr, req_to_lora, S = build_segments(ids, L)
+    info, trows = [], []
+    for s in range(S):
+        beg, end = int(seg_indptr[s]), int(seg_indptr[s + 1])
+        for p in range(beg, end, rows):
+            n = min(rows, end - p)
+            info.append([s, int(req_to_lora[s]), p, n])
+            r = [-1] * rows
+            r[:n] = [int(v) for v in sorted_idx[p:p + n]]
+            trows.append(r)
+    return (np.array(info, dtype=np.int32).reshape(-1, 4),
+            np.array(trows, dtype=np.int32).reshape(-1, rows))
+
+
 def slice_offsets(slice_sizes: Sequence[int]) -> List[int]:
     off = [0]
     for n in slice_sizes:

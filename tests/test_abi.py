@@ -65,9 +65,13 @@ def test_argument_checks_fail_before_any_launch():
     lib = _abi.lib
     INV = _abi.LORA_INVALID_ARG
     null = ctypes.c_void_p(0)
-    assert lib.lora_build_segments(null, -1, 4, null, null, null, null, null) == INV
-    assert lib.lora_build_segments(null, 4, 0, null, null, null, null, null) == INV
-    assert lib.lora_build_segments(null, 4, 4, null, null, null, null, null) == INV
+    assert lib.lora_build_segments(null, -1, 4, null, null, null, null, null, null, null, 8,
+                                   null) == INV
+    assert lib.lora_build_segments(null, 4, 0, null, null, null, null, null, null, null, 8,
+                                   null) == INV
+    assert lib.lora_build_segments(null, 4, 4, null, null, null, null, null, null, null, 8,
+                                   null) == INV
+    assert lib.lora_tile_capacity(130, 4) == 2 + 4 and lib.lora_tile_capacity(3, 20) == 3
     w = _abi.lora_weights_t()
     w.dtype, w.K, w.n_slices, w.L, w.r_max = 1, 100, 1, 4, 16     # K not a multiple of 8
     assert lib.lora_shrink_expand_add(ctypes.byref(w), null, 0, 1, None, null, 0, null, 0,

@@ -34,8 +34,11 @@ def gpu_segments(ml, ids_np, L):
     ml.lora_build_segments(ids, seg)
     torch.cuda.synchronize()
     M = len(ids_np)
+    nt = int(seg.num_tiles.cpu()[0])
     return (seg.sorted_idx[:M].cpu().numpy(), seg.seg_indptr.cpu().numpy(),
-            seg.req_to_lora.cpu().numpy(), int(seg.num_segments.cpu()[0]))
+            seg.req_to_lora.cpu().numpy(), int(seg.num_segments.cpu()[0]),
+            seg.tile_info.cpu().numpy().reshape(-1, 4)[:nt],
+            seg.tile_rows.cpu().numpy().reshape(-1, 64)[:nt])
 
 
 SEG_CASES = [
@@ -64,6 +67,9 @@ def test_segments_bit_exact(ml, name, mk):
     assert np.array_equal(got[1], ref[1])
     assert np.array_equal(got[2], ref[2])
     assert got[3] == ref[3]
+    info, rows = O.tile_schedule(ids, L)
+    assert np.array_equal(got[4], info)
+    assert np.array_equal(got[5], rows)
 
 
 # ---------------------------------------------------------------- full path

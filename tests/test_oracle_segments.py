@@ -80,3 +80,34 @@ def test_invariants_random(seed):
     assert np.all(req[n:] == -1)
     assert np.all(ids[si[mv:]] < 0)
     assert np.all(np.diff(si[mv:]) > 0)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_tile_schedule_invariants(seed):
+    """Tiles cover every sorted position with an adapter exactly once, never
+    straddle a segment, hold at most 64 rows, and their count respects the
+    capacity bound floor(M/64) + min(L, M)."""
+    rng = np.random.default_rng(100 + seed)
+    L = int(rng.integers(1, 40))
+    M = int(rng.integers(0, 3000))
+    ids = rng.integers(-1, L, size=M).astype(np.int32)
+    if seed == 0:
+        ids[:] = 3 % L                      # one long segment
+    info, rows = O.tile_schedule(ids, L)
+    si, seg, req, n = O.build_segments(ids, L)
+    assert len(info) <= M // 64 + min(L, M)
+    covered = []
+    for (s, a, p, cnt), r in zip(info, rows):
+        assert 1 <= cnt <= 64 and req[s] == a
+        assert seg[s] <= p and p + cnt <= seg[s + 1]
+        assert np.array_equal(r[:cnt], si[p:p + cnt]) and np.all(r[cnt:] == -1)
+        covered += list(range(p, p + cnt))
+    assert covered == list(range(int(seg[n])))
+
+
+def test_tile_schedule_hand_case():
+    """ids [0, 2, 0, 1] (walkthrough section 2.3 example) with 2-row tiles:
+    segment 0 -> tokens 0, 2 (one full tile); 1 -> token 3; 2 -> token 1."""
+    info, rows = O.tile_schedule([0, 2, 0, 1], 3, rows=2)
+    assert info.tolist() == [[0, 0, 0, 2], [1, 1, 2, 1], [2, 2, 3, 1]]
+    assert rows.tolist() == [[0, 2], [3, -1], [1, -1]]
