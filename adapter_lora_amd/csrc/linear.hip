@@ -90,12 +90,12 @@ __global__ __launch_bounds__(kTileThreads) void k_shrink_dense(LinearArgs a, con
     float* Pc = P + (int64_t)c * a.M * a.cols;
     const T* A = reinterpret_cast<const T*>(a.A) + v.off;
     if constexpr (sizeof(T) == 2) {
-        __shared__ uint4 sA[kShrinkLds / 16];
+        __shared__ uint4 sXA[kShrinkLds / 16];
         const int k0 = c * kShrinkK;
         const int k1 = min(a.K, k0 + kShrinkK);
-        shrink_group_bf16(rs, reinterpret_cast<const uint16_t*>(x), ldx,
+        shrink_group_bf16(rs, 0, reinterpret_cast<const uint16_t*>(x), ldx,
                           reinterpret_cast<const uint16_t*>(A), a.K, a.n_sl, v.rp, a.r_max, cg,
-                          k0, k1, Pc, a.cols, sA);
+                          k0, k1, Pc, a.cols, sXA, sXA + kShrinkLds / 32);
     } else {
         const int k0 = c * kKChunk;
         const int k1 = min(a.K, k0 + kKChunk);
@@ -132,7 +132,7 @@ struct GroupMap {
 };
 
 template <typename T>
-__global__ __launch_bounds__(kTileThreads) void k_expand_dense(LinearArgs a, GroupMap gm,
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_expand_dense(LinearArgs a, GroupMap gm,
                                                                 const float* __restrict__ S,
                                                                 T* __restrict__ y, int64_t ldy,
                                                                 int units) {
@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kTileThreads) void k_expand_dense(LinearArgs a, Gro
     const RowSet rs{v.n, kRowTile, s_in, s_out};
     const T* B = reinterpret_cast<const T*>(a.B) + v.off;
     if constexpr (sizeof(T) == 2) {
-        __shared__ uint16_t sHi[64 * kSLds], sLo[64 * kSLds];
+        __shared__ uint4 lds[kExpandLds / 16];
         expand_rows_bf16(rs, S, a.cols, sl * a.r_max, reinterpret_cast<const uint16_t*>(B), v.rp,
-                         n_begin, n_end, reinterpret_cast<uint16_t*>(y), ldy, sHi, sLo);
+                         n_begin, n_end, reinterpret_cast<uint16_t*>(y), ldy, lds);
     } else {
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
             expand_tile_simple<T>(rs, S, a.cols, sl * a.r_max, B, v.rp, n0, min(n0 + kNTile, n_end),
@@ -196,17 +196,11 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
     return hipGetLastError();
 }
 
-// Column tiles per workgroup: about two workgroups per CU (the expand holds
-// two resident per CU), each walking consecutive 256-column tiles with S
-// staged once and the next tile's loads in flight.
+// One 256-column tile per workgroup: a workgroup walks its tiles one after
+// another without overlapping them, so spreading tiles over more workgroups
+// (three resident per CU) hides more latency.
 static GroupMap make_group_map(const LinearArgs& a) {
-    int tiles = 0;
-    for (int s = 0; s < a.n_sl; ++s)
-        tiles += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
-    const int target = 512;
-    int tpw = (int)((int64_t)a.max_tiles * tiles / target);
-    if (tpw < 1) tpw = 1;
-    if (tpw > 8) tpw = 8;
+    const int tpw = 1;
     GroupMap gm{};
     gm.tpw = tpw;
     int g = 0;

@@ -183,12 +183,13 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
     const int rows = a.L * a.max_tokens_padded;
     float* Pc = P + (int64_t)c * rows * a.r;
     if constexpr (sizeof(T) == 2) {
-        __shared__ uint4 sA[kShrinkLds / 16];
+        __shared__ uint4 sXA[kShrinkLds / 16];
         const int k0 = c * kShrinkK;
         const int k1 = min(K, k0 + kShrinkK);
-        shrink_group_bf16(rs, reinterpret_cast<const uint16_t*>(in), ld_in,
-                          reinterpret_cast<const uint16_t*>(A), K, 1, a.r, a.r, 0, k0, k1, Pc,
-                          a.r, sA);
+        for (int r0 = 0; r0 < rs.n; r0 += 64)
+            shrink_group_bf16(rs, r0, reinterpret_cast<const uint16_t*>(in), ld_in,
+                              reinterpret_cast<const uint16_t*>(A), K, 1, a.r, a.r, 0, k0, k1, Pc,
+                              a.r, sXA, sXA + kShrinkLds / 32);
     } else {
         const int k0 = c * kKChunk;
         const int k1 = min(K, k0 + kKChunk);
@@ -216,7 +217,7 @@ __global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride
 }
 
 template <typename T>
-__global__ __launch_bounds__(kTileThreads) void k_moe_expand(MoeArgs a, int which,
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_moe_expand(MoeArgs a, int which,
                                                               const float* __restrict__ S,
                                                               T* __restrict__ out, int64_t ld_out,
                                                               int N, int n_groups, int tpw,
@@ -236,9 +237,9 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_expand(MoeArgs a, int whic
     const int n_begin = g * tpw * kNTile;
     const int n_end = min(N, n_begin + tpw * kNTile);
     if constexpr (sizeof(T) == 2) {
-        __shared__ uint16_t sHi[64 * kSLds], sLo[64 * kSLds];
+        __shared__ uint4 lds[kExpandLds / 16];
         expand_rows_bf16(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin, n_end,
-                         reinterpret_cast<uint16_t*>(out), ld_out, sHi, sLo);
+                         reinterpret_cast<uint16_t*>(out), ld_out, lds);
     } else {
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
             expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out);
@@ -269,9 +270,9 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_tiles = (N + kNTile - 1) / kNTile;
-    int tpw = (int)((int64_t)a.L * nblk * n_tiles / 512);
-    if (tpw < 1) tpw = 1;
-    if (tpw > 8) tpw = 8;
+    // one 256-column tile per workgroup: a workgroup walks its tiles one after
+    // another, so spreading them over more workgroups overlaps their latencies
+    const int tpw = 1;
     const int n_groups = (n_tiles + tpw - 1) / tpw;
     const int units2 = a.L * nblk * n_groups;
     const unsigned g2 = (unsigned)((units2 + 7) / 8 * 8);
