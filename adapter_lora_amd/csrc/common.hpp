@@ -58,23 +58,34 @@ template <> struct Io<uint16_t> {
 // ----------------------------------------------------------------------------
 // masked vector loads without branches: the load always happens, from `p`
 // when `ok` and otherwise from `safe` (any readable address, e.g. the start
-// of the same tensor), and the result is zeroed by a select.  A conditional
-// load (`ok ? *p : 0`) is compiled into per-dword loads under exec-mask
-// branches; this form stays one dwordx4 / dwordx2 load.
+// of the same tensor), and the result is cleared with a bitwise AND whose
+// mask the compiler cannot see through.  With a visible condition the
+// compiler turns "load, then select on ok" back into a load under an
+// exec-mask branch followed by a wait for it, which serialises the loads
+// that were meant to be in flight together.
 // ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t opaque_mask(bool ok) {
+    uint32_t m = ok ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));
+    return m;
+}
+
 __device__ __forceinline__ uint4 ld16_if(const void* p, bool ok, const void* safe) {
     const uint4 v = *reinterpret_cast<const uint4*>(ok ? p : safe);
-    return ok ? v : make_uint4(0, 0, 0, 0);
+    const uint32_t m = opaque_mask(ok);
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
 __device__ __forceinline__ uint2 ld8_if(const void* p, bool ok, const void* safe) {
     const uint2 v = *reinterpret_cast<const uint2*>(ok ? p : safe);
-    return ok ? v : make_uint2(0, 0);
+    const uint32_t m = opaque_mask(ok);
+    return make_uint2(v.x & m, v.y & m);
 }
 
 __device__ __forceinline__ float4 ldf4_if(const float* p, bool ok, const float* safe) {
-    const float4 v = *reinterpret_cast<const float4*>(ok ? p : safe);
-    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint4 v = ld16_if(p, ok, safe);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
 }
 
 // ----------------------------------------------------------------------------

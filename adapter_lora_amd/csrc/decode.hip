@@ -66,15 +66,17 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a
     v.id = a.req_to_lora[s];
     v.p0 = a.seg_indptr[s];
     const int p1 = a.seg_indptr[s + 1];
-    v.my_idx = lane < a.M ? a.sorted_idx[lane] : 0;
+    // indices are clamped rather than tested, so every load is unconditional
+    // and all of them are in flight together
+    v.my_idx = a.sorted_idx[min(lane, a.M - 1)];
     if (a.L <= 4 * kWave) {
         int rk[4];
         int64_t of[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int j = q * kWave + lane;
-            rk[q] = j < a.L ? a.rank[j] : 0;
-            of[q] = j < a.L ? offs[j] : 0;
+            const int j = min(q * kWave + lane, a.L - 1);
+            rk[q] = a.rank[j];
+            of[q] = offs[j];
         }
         const int id = v.id < 0 ? 0 : v.id;
         const int q = id / kWave, src = id % kWave;
@@ -270,11 +272,13 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
         const int n = nw + q * RPI + rsub;
         braw[q] = ld16_if(B + (int64_t)n * rp + g * EPC, gin && n < n1, B);
     }
+    // (row and column clamped into range: values of rows or columns that do
+    // not exist are never used)
     float yv[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
-        const int m = __shfl(v.my_idx, v.p0 + u, kWave);
-        yv[u] = (u < v.ms && nin) ? Io<T>::ld(Y + (int64_t)m * p.ldy + n_out) : 0.f;
+        const int m = __shfl(v.my_idx, v.p0 + min(u, v.ms - 1), kWave);
+        yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + min(n_out, n1 - 1));
     }
     // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
     //    polled kPollBatch slots at a time

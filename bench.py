@@ -10,10 +10,18 @@ Protocol:
     sized so that R copies exceed twice the 256 MB Infinity Cache; step i uses
     copy i % R, so each step reads its weights from HBM (cold MALL);
   * W warmup steps, then K timed steps between two device synchronisations;
-    ms_per_step is the wall time of the K steps (launch gaps included);
-  * the dominant kernel is bracketed by HIP events on the stream it runs on,
-    every step, and its mean duration gives the roofline figure:
-    algorithmic bytes per launch / mean duration, against 8 TB/s;
+    ms_per_step is the event time of the K steps on the launching stream
+    (launch gaps included);
+  * the dominant kernel is then launched K times back to back on the same
+    rotation (segment tables already built), bracketed by one HIP event pair
+    on its stream; elapsed / K is its mean duration, and algorithmic bytes
+    per launch / that duration gives the roofline figure against 8 TB/s;
+  * a plain streaming copy (bf16 negation, read + write) of the same byte
+    count and of 256 MB is timed the same way as the practical ceiling and as
+    the calibration kernel for the FETCH_SIZE / WRITE_SIZE counter runs;
+  * HBM traffic per launch comes from those counter runs, kept as a summary
+    under profiles/ with a hash of the kernel's sources; it is reported only
+    while the sources still match the hash;
   * the oracle (fp64 CPU) is timed on the host on a bounded sample.
 Other configurations (prefill, stacked QKV / gate-up, MoE) are measured the
 same way and reported under "extra" as context; the headline line is the
@@ -72,42 +80,91 @@ def linear_bytes_flops(case):
     return w_bytes + act, flops, m_valid, len(touched)
 
 
-class Timer:
-    """Event pairs around one kernel launch per step, on the launching stream."""
-
-    def __init__(self, n):
-        import torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
-        self.i = 0
-
-    def start(self):
-        self.ev[self.i][0].record()
-
-    def stop(self):
-        self.ev[self.i][1].record()
-        self.i += 1
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.ev[:self.i]]))
-
-
-def run_timed(step, steps, warmup, timer_slots):
+def run_timed(step, steps, warmup):
+    """W untimed steps, then K steps between two synchronisations; returns
+    (event ms per step on the launching stream, host wall ms per step)."""
     import torch
     for i in range(warmup):
-        step(i, None)
+        step(i)
     torch.cuda.synchronize()
-    timer = Timer(steps)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step(warmup + i, timer)
+        step(warmup + i)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return t0.elapsed_time(t1) / steps, timer.mean_ms(), wall / steps * 1e3
+    return t0.elapsed_time(t1) / steps, wall / steps * 1e3
+
+
+def back_to_back(launch, n):
+    """Mean duration (ms) of `launch(i)` over n back-to-back launches bracketed
+    by one event pair on the current stream (the stream the kernels use)."""
+    import torch
+    for i in range(min(n, 8)):
+        launch(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        launch(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
+def copy_ceiling(nbytes, n=50):
+    """A plain streaming copy (out = -in, bf16) moving `nbytes` in total
+    (nbytes/2 read, nbytes/2 written), rotated over enough buffers to miss the
+    Infinity Cache.  Returns GB/s over the back-to-back launches."""
+    import torch
+    elems = max(1, nbytes // 4)
+    R = max(2, int(np.ceil(2 * MALL_BYTES / (2 * elems * 2))))
+    R = min(R, 64)
+    src = [torch.randn(elems, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    dst = [torch.empty_like(t) for t in src]
+    ms = back_to_back(lambda i: torch.neg(src[i % R], out=dst[i % R]), n)
+    return {"bytes": 4 * elems, "ms": ms, "gbs": 4 * elems / (ms * 1e-3) / 1e9, "rotation": R,
+            "kernel": "torch neg (bf16), read + write"}
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["adapter_lora_amd/csrc/decode.hip", "adapter_lora_amd/csrc/common.hpp",
+                  "adapter_lora_amd/csrc/kernels.hpp", "include/mlora.h"]
+TRAFFIC_SUMMARY = "profiles/decode_fused_traffic.md"
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused decode kernel from the committed
+    counter summary, or None when it is absent or the sources changed since."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    try:
+        if vals["source_hash"] != source_hash(DECODE_SOURCES):
+            return None
+        return {"fetch_bytes": float(vals["fetch_bytes_per_launch"]),
+                "write_bytes": float(vals["write_bytes_per_launch"]),
+                "total_bytes": float(vals["traffic_bytes_per_launch"]),
+                "calibration": vals.get("calibration", "")}
+    except (KeyError, ValueError):
+        return None
 
 
 # ----------------------------------------------------------------------------- dense
@@ -130,19 +187,20 @@ def bench_linear(case, steps, warmup, fused_kernel_name):
     del A, B
     torch.cuda.synchronize()
 
-    def step(i, timer):
+    def step(i):
         table, ids, seg, x, y = copies[i % R]
         ml.lora_build_segments(ids, seg)
-        if timer:
-            timer.start()
         ml.lora_shrink_expand_add(table, x, seg, y, ws)
-        if timer:
-            timer.stop()
 
-    ms_step, ms_kernel, ms_wall = run_timed(step, steps, warmup, 1)
+    def kernel(i):
+        table, ids, seg, x, y = copies[i % R]
+        ml.lora_shrink_expand_add(table, x, seg, y, ws)
+
+    ms_step, ms_wall = run_timed(step, steps, warmup)
+    ms_kernel = back_to_back(kernel, steps)     # segment tables of every copy are built
     assert ml.lora_read_device_error(ws.buf) == 0, "device error during the bench"
     res = {
-        "ms_per_step": ms_step, "ms_kernel_events": ms_kernel, "ms_wall_host": ms_wall,
+        "ms_per_step": ms_step, "ms_kernel_b2b": ms_kernel, "ms_wall_host": ms_wall,
         "tokens_per_s": m_valid / (ms_step * 1e-3), "m_valid": m_valid, "M": case.M,
         "adapters_touched": touched, "alg_bytes": nbytes, "alg_flops": flops,
         "kernel": fused_kernel_name, "rotation_copies": R,
@@ -188,22 +246,25 @@ def bench_moe(case, steps, warmup):
     ws = ml.Workspace(ml.lora_moe_workspace_size(copies[0][0], cap))
     torch.cuda.synchronize()
 
-    def step(i, timer):
+    def step(i):
         w, x, c1, c3 = copies[i % R]
         ml.lora_moe_align_run(tid, ids, en, case.E, al)
-        if timer:
-            timer.start()
         ml.lora_moe_gate_up_add(w, x, case.topk, al, c1, ws)
         ml.lora_moe_silu_and_mul(c1, c2)
         ml.lora_moe_down_add(w, c2, case.M, case.topk, al, c3, ws)
-        if timer:
-            timer.stop()
         ml.lora_moe_topk_reduce(c3, wts, out)
 
-    ms_step, ms_deltas, ms_wall = run_timed(step, steps, warmup, 1)
+    def deltas(i):
+        w, x, c1, c3 = copies[i % R]
+        ml.lora_moe_gate_up_add(w, x, case.topk, al, c1, ws)
+        ml.lora_moe_silu_and_mul(c1, c2)
+        ml.lora_moe_down_add(w, c2, case.M, case.topk, al, c3, ws)
+
+    ms_step, ms_wall = run_timed(step, steps, warmup)
+    ms_deltas = back_to_back(deltas, steps)
     silu_bytes = P * 3 * I * es
     res = {
-        "ms_per_step": ms_step, "ms_deltas_and_silu_events": ms_deltas, "ms_wall_host": ms_wall,
+        "ms_per_step": ms_step, "ms_deltas_and_silu_b2b": ms_deltas, "ms_wall_host": ms_wall,
         "tokens_per_s": case.M / (ms_step * 1e-3), "pairs": len(pairs), "buckets": len(buckets),
         "alg_bytes_deltas": nbytes, "alg_bytes_silu": silu_bytes, "alg_flops": flops,
         "rotation_copies": R,
@@ -271,7 +332,12 @@ def main():
         results["moe_bf16"] = bench_moe(W.moe_case(0), args.steps, args.warmup)
 
     head = results.get("decode_bf16")
+    ceiling = {}
+    if head is not None:
+        ceiling["same_bytes_as_decode"] = copy_ceiling(head["alg_bytes"], args.steps)
+    ceiling["256MB"] = copy_ceiling(256 << 20, 20)
     cpu = None if args.no_cpu or head is None else cpu_baseline(dec_case, args.cpu_seconds)
+    traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"] if head else None,
@@ -291,10 +357,13 @@ def main():
                    "cold_mall_rotation": head["rotation_copies"] if head else None},
         "roofline": None if head is None else {
             "bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": head["hbm_frac"], "traffic": None,
-            "kernel": head["kernel"], "kernel_ms": head["ms_kernel_events"],
-            "alg_bytes_per_launch": head["alg_bytes"]},
+            "frac": head["hbm_frac"],
+            "traffic": None if traffic is None else traffic["total_bytes"],
+            "kernel": head["kernel"], "kernel_ms": head["ms_kernel_b2b"],
+            "alg_bytes_per_launch": head["alg_bytes"],
+            "traffic_detail": traffic},
         "cpu_baseline": cpu,
+        "copy_ceiling": ceiling,
         "extra": {k: v for k, v in results.items() if k != "decode_bf16"},
     }
     print(json.dumps(line), flush=True)
