@@ -54,6 +54,14 @@ SEG_CASES = [
     ("big_random", lambda: (np.random.default_rng(1).integers(-1, 1024, 20000).astype(np.int32),
                             1024)),
     ("L1", lambda: (np.random.default_rng(2).integers(-1, 1, 777).astype(np.int32), 1)),
+    # single-wavefront builder (M <= 64)
+    ("wave_M64_L1024", lambda: (np.random.default_rng(3).integers(-1, 1024, 64).astype(np.int32),
+                                1024)),
+    ("wave_M64_L3", lambda: (np.random.default_rng(4).integers(-2, 5, 64).astype(np.int32), 3)),
+    ("wave_M1", lambda: (np.array([5], np.int32), 8)),
+    ("wave_M63_one_id", lambda: (np.full(63, 2, np.int32), 3)),
+    ("wave_M65_block_path", lambda: (np.random.default_rng(5).integers(-1, 6, 65).astype(np.int32),
+                                     6)),
 ]
 
 
