@@ -66,7 +66,7 @@ template <> struct Io<uint16_t> {
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t opaque_mask(bool ok) {
     uint32_t m = ok ? 0xffffffffu : 0u;
-    asm volatile("" : "+v"(m));
+    asm("" : "+v"(m));     // not volatile: equal masks may still be shared
     return m;
 }
 

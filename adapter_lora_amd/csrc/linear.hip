@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kTileThreads) void k_shrink_dense(LinearArgs a, con
                                                                 int64_t ldx, float* __restrict__ P,
                                                                 int C, int G, int units) {
     __shared__ int s_in[kRowTile], s_out[kRowTile];
-    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    const int u = (int)blockIdx.x;
     if (u >= units) return;
     const int tile = u / (C * G);
     const int c = (u / G) % C;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kTileThreads) void k_shrink_dense(LinearArgs a, con
         const int k1 = min(a.K, k0 + kShrinkK);
         shrink_group_bf16(rs, 0, reinterpret_cast<const uint16_t*>(x), ldx,
                           reinterpret_cast<const uint16_t*>(A), a.K, a.n_sl, v.rp, a.r_max, cg,
-                          k0, k1, Pc, a.cols, sXA, sXA + kShrinkLds / 32);
+                          k0, k1, Pc, a.cols, sXA);
     } else {
         const int k0 = c * kKChunk;
         const int k1 = min(a.K, k0 + kKChunk);
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
                                                                 T* __restrict__ y, int64_t ldy,
                                                                 int units) {
     __shared__ int s_in[kRowTile], s_out[kRowTile];
-    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    const int u = (int)blockIdx.x;
     if (u >= units) return;
     const int tile = u / gm.n_groups;
     const int g = u % gm.n_groups;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-static unsigned grid_of(int units) { return (unsigned)((units + kXcds - 1) / kXcds * kXcds); }
+static unsigned grid_of(int units) { return (unsigned)(units > 0 ? units : 1); }
 
 hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float* S, void* ws,
                          hipStream_t st) {

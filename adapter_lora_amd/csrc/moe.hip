@@ -133,22 +133,28 @@ hipError_t launch_moe_align(const int32_t* topk_ids, const int32_t* ids,
 struct MoeUnit {
     bool ok;
     int e;
+    int n;     // rows to process: 1 + the last real row of the block
 };
 
 // Stage the rows of block b of adapter l.  `shrink` selects the row roles:
 // shrink: in = source row of the activation, out = P/S row (l*mtp + pos);
 // expand: in = S row, out = cache row f.
+// Every index load is issued at once (indices clamped, not tested), so the
+// unit is known after one memory round trip.  Padding rows (sentinels) read
+// and write nothing; rows past the block's last real row are not visited.
 __device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool shrink, int l, int b,
-                                            int* s_in, int* s_out) {
-    const int bs = a.block_size_m;
-    if (!a.adapter_enabled[l] || b * bs >= a.ntpp[l]) return MoeUnit{false, -1};
-    const int e = a.expert_ids[(int64_t)l * (a.max_tokens_padded / bs) + b];
-    if (e < 0 || e >= a.E) return MoeUnit{false, -1};
+                                            int* s_in, int* s_out, int* s_wlast) {
+    const int bs = a.block_size_m;                // <= kTileThreads
     const int P = a.M * a.topk;
-    for (int i = threadIdx.x; i < bs; i += kTileThreads) {
-        const int pos = b * bs + i;
-        const int f = a.sorted_token_ids[(int64_t)l * a.max_tokens_padded + pos];
-        const bool real = f >= 0 && f < P;
+    const int i = threadIdx.x;
+    const int pos = b * bs + min(i, bs - 1);
+    const int en = a.adapter_enabled[l];
+    const int np = a.ntpp[l];
+    const int e = a.expert_ids[(int64_t)l * (a.max_tokens_padded / bs) + b];
+    const int f = a.sorted_token_ids[(int64_t)l * a.max_tokens_padded + pos];
+    if (!en || b * bs >= np || e < 0 || e >= a.E) return MoeUnit{false, -1, 0};
+    const bool real = i < bs && f >= 0 && f < P;
+    if (i < bs) {
         const int srow = l * a.max_tokens_padded + pos;
         const int src = which == 0 ? f / a.topk : f;
         if (shrink) {
@@ -159,8 +165,13 @@ __device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool sh
             s_out[i] = real ? f : -1;
         }
     }
+    const unsigned long long bal = __ballot(real);
+    if (lane_id() == 0) s_wlast[i / kWave] = bal ? (i / kWave) * kWave + 63 - __clzll(bal) : -1;
     __syncthreads();
-    return MoeUnit{true, e};
+    int last = -1;
+#pragma unroll
+    for (int w = 0; w < kTileWaves; ++w) last = max(last, s_wlast[w]);
+    return MoeUnit{true, e, last + 1};
 }
 
 template <typename T>
@@ -170,16 +181,17 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
                                                               int C, int K, int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     const int nblk = a.max_tokens_padded / a.block_size_m;
-    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / C;
     const int c = unit % C;
     const int l = blk / nblk, b = blk % nblk;
-    const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out);
+    __shared__ int s_wlast[kTileWaves];
+    const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
     const int64_t ew = (int64_t)l * a.E + mu.e;
     const T* A = reinterpret_cast<const T*>(which == 0 ? a.A_gu : a.A_d) + ew * a.r * K;
-    const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
+    const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int rows = a.L * a.max_tokens_padded;
     float* Pc = P + (int64_t)c * rows * a.r;
     if constexpr (sizeof(T) == 2) {
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
         for (int r0 = 0; r0 < rs.n; r0 += 64)
             shrink_group_bf16(rs, r0, reinterpret_cast<const uint16_t*>(in), ld_in,
                               reinterpret_cast<const uint16_t*>(A), K, 1, a.r, a.r, 0, k0, k1, Pc,
-                              a.r, sXA, sXA + kShrinkLds / 32);
+                              a.r, sXA);
     } else {
         const int k0 = c * kKChunk;
         const int k1 = min(K, k0 + kKChunk);
@@ -224,16 +236,17 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
                                                               int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     const int nblk = a.max_tokens_padded / a.block_size_m;
-    const int unit = xcd_unit(blockIdx.x, gridDim.x);
+    const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / n_groups;
     const int g = unit % n_groups;
     const int l = blk / nblk, b = blk % nblk;
-    const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out);
+    __shared__ int s_wlast[kTileWaves];
+    const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
     const int64_t ew = (int64_t)l * a.E + mu.e;
     const T* B = reinterpret_cast<const T*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
-    const RowSet rs{a.block_size_m, a.block_size_m, s_in, s_out};
+    const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int n_begin = g * tpw * kNTile;
     const int n_end = min(N, n_begin + tpw * kNTile);
     if constexpr (sizeof(T) == 2) {
@@ -257,7 +270,7 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.partial);
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
     const int units = a.L * nblk * C;
-    const unsigned g1 = (unsigned)((units + 7) / 8 * 8);
+    const unsigned g1 = (unsigned)(units > 0 ? units : 1);
     hipLaunchKernelGGL((k_moe_shrink<T>), dim3(g1), dim3(kTileThreads), 0, st, a, which,
                        reinterpret_cast<const T*>(in), ld_in, P, C, K, units);
     hipError_t e = hipGetLastError();
@@ -275,7 +288,7 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     const int tpw = 1;
     const int n_groups = (n_tiles + tpw - 1) / tpw;
     const int units2 = a.L * nblk * n_groups;
-    const unsigned g2 = (unsigned)((units2 + 7) / 8 * 8);
+    const unsigned g2 = (unsigned)(units2 > 0 ? units2 : 1);
     hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
                        reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2);
     return hipGetLastError();

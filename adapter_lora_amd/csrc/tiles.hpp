@@ -47,13 +47,11 @@ __device__ __forceinline__ void split_hi_lo(const float* v, uint4& hi, uint4& lo
 
 constexpr int kTileThreads = 256;
 
-// Workgroup ids are handed to the 8 XCDs round robin; renumber them so that
-// consecutive work units (which share input rows) run on the same XCD and
-// meet in its L2.  grid must be a multiple of 8.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_unit(int b, int grid) {
-    return (b % kXcds) * (grid / kXcds) + b / kXcds;
-}
+// Work units are numbered by blockIdx directly.  The hardware hands
+// consecutive workgroups to the 8 XCDs round robin, which spreads the units
+// that find no work (tiles past the schedule, empty MoE blocks) evenly over
+// the XCDs; grouping consecutive units on one XCD for L2 reuse left half of
+// the XCDs idle when the empty units were contiguous.
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr int kMaxRowTile = 256;
 
@@ -65,6 +63,8 @@ struct RowSet {
     const int* out_row;      // LDS [RT]: output row index, -1 = padding row
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // ---------------------------------------------------------------------------
 // shrink unit: P[out_row][cg*64 + c] = sum_{k0 <= k < k1} x[in_row, k] A[row(c), k]
 // for the 64 S columns of column group cg and up to 64 rows (k1 - k0 <= 512).
@@ -72,15 +72,17 @@ struct RowSet {
 //   jj = cbg % (r_max/16); it is active when jj < rp/16 and then reads
 //   adapter rows sl*rp + jj*16 .. +16; inactive blocks store zeros (rank
 //   padding).
-// Both operand chunks (64 x rows and 64 A rows, 512 K values each: 2 x 64 KB)
-// are loaded row-major — a wavefront reads one contiguous 1 KB row segment
-// per instruction — with all 32 loads of a thread in flight at once, and
-// staged in LDS; row r's 16-byte chunk q lives at chunk q ^ (r & 15), so the
-// MFMA operand reads of 16 consecutive rows hit 64 distinct banks.
+// The A chunk (up to 64 rows x 512 K, 64 KB) goes to LDS with direct
+// global->LDS loads: one wave instruction moves one 1 KB row segment, lane l
+// fetching the 16-byte chunk that belongs at its LDS position (chunk q of row
+// r sits at position q ^ (r & 15), so the MFMA operand reads of 16
+// consecutive rows hit 64 distinct banks).  No registers hold A on the way.
+// Each wave keeps its 16 x rows for the chunk in registers; the x loads are
+// issued together with the A loads, so a unit costs one memory round trip.
 // ---------------------------------------------------------------------------
 constexpr int kShrinkK = 512;
 constexpr int kGroupCols = 64;
-constexpr int kShrinkLds = 2 * kGroupCols * kShrinkK * 2;   // bytes: x chunk + A chunk
+constexpr int kShrinkLds = kGroupCols * kShrinkK * 2;   // bytes: the A chunk
 
 __device__ __forceinline__ int swz(int r, int q) { return r * (kShrinkK / 8) + (q ^ (r & 15)); }
 
@@ -89,7 +91,7 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
                                                   const uint16_t* __restrict__ A, int K, int n_sl,
                                                   int rp, int r_max, int cg, int k0, int k1,
                                                   float* __restrict__ P, int pld,
-                                                  uint4* __restrict__ sX, uint4* __restrict__ sA) {
+                                                  uint4* __restrict__ sA) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -98,6 +100,7 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
     const int lr = lane % 16;
     const int lq = lane / 16;                 // 16-byte chunk within a 32-wide K step
     const int rows = min(64, rs.n - r0);
+    const int nq = (k1 - k0) / 8;             // valid 16-byte chunks per row segment
     bool act[4];
     int arow[4];
 #pragma unroll
@@ -108,41 +111,42 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
         arow[cb] = sl * rp + jj * 16;
     }
     const bool any = act[0] || act[1] || act[2] || act[3];
-    if (any) {
-        // thread t covers chunk (t % 64) of rows t / 64 + 4 i, i = 0..15
-        const int q = tid % 64;
-        const int k = k0 + q * 8;
-        uint4 av[16], xv[16];
+    // 1. A rows 16w .. 16w+15 of the group (column block w), one row per
+    //    instruction; chunks past k1 repeat the row's last valid chunk (their
+    //    x partners are zero)
+    if (act[wave]) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int r = i * 4 + tid / 64;
-            const int cb = r / 16;
-            av[i] = ld16_if(A + (int64_t)(arow[cb] + r % 16) * K + k, act[cb] && k < k1, A);
-            const int xr = r < rows ? rs.in_row[r0 + r] : -1;
-            xv[i] = ld16_if(x + (int64_t)xr * ldx + k, xr >= 0 && k < k1, x);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = i * 4 + tid / 64;
-            sA[swz(r, q)] = av[i];
-            sX[swz(r, q)] = xv[i];
+            const int r = wave * 16 + i;
+            const int q = min(lane ^ i, nq - 1);     // chunk stored at position `lane`
+            const uint16_t* src = A + (int64_t)(arow[wave] + i) * K + k0 + q * 8;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sA + r * (kShrinkK / 8)), 16, 0, 0);
         }
     }
-    __syncthreads();
-    // wave w: rows 16w .. 16w+15, the group's 4 column blocks
+    // 2. this wave's 16 x rows (rows 16w + lr), chunks kk*4 + lq
     const int rg = wave;
+    uint4 xv[kShrinkK / 32];
+    {
+        const int i = rg * 16 + lr;
+        const int xr = (i < rows) ? rs.in_row[r0 + i] : -1;
+        const uint16_t* xp = x + (int64_t)(xr < 0 ? 0 : xr) * ldx + k0 + lq * 8;
+#pragma unroll
+        for (int kk = 0; kk < kShrinkK / 32; ++kk)
+            xv[kk] = ld16_if(xp + kk * 32, any && xr >= 0 && kk * 4 + lq < nq, x);
+    }
+    __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
+    __syncthreads();
     f32x4_t acc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (any && rg * 16 < rows) {
 #pragma unroll
         for (int kk = 0; kk < kShrinkK / 32; ++kk) {
-            const uint4 a = sX[swz(rg * 16 + lr, kk * 4 + lq)];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 if (act[cb]) {
                     const uint4 b = sA[swz(cb * 16 + lr, kk * 4 + lq)];
-                    acc[cb] = mfma_bf16(a, b, acc[cb]);
+                    acc[cb] = mfma_bf16(xv[kk], b, acc[cb]);
                 }
             }
         }
@@ -157,7 +161,7 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
         for (int cb = 0; cb < 4; ++cb)
             if (cg * kGroupCols + cb * 16 < pld) pp[cb * 16] = acc[cb][qq];
     }
-    __syncthreads();     // sX / sA are reused by the next row block
+    __syncthreads();     // sA is reused by the next row block
 }
 
 // ---------------------------------------------------------------------------
@@ -178,8 +182,6 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
 constexpr int kYRowBytes = kNTile * 2;                       // 512
 constexpr int kSLds = LORA_MAX_RANK + 8;                     // bf16 row stride of staged S
 constexpr int kExpandLds = 64 * kYRowBytes + 2 * 64 * kSLds * 2;   // bytes
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ int ypos(int r, int q) { return r * (kYRowBytes / 16) + (q ^ (r & 15)); }
 
@@ -218,32 +220,42 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int j = st * 32 + lq * 8;
-            bop[nb][st] = ld16_if(B + (int64_t)n * rp + j, st < nsteps && n < n1 && j < rp, B);
+            // clamped, not masked: columns past n1 are never written back and
+            // rank positions past rp meet zero S values
+            bop[nb][st] = ld16(B + (int64_t)min(n, n1 - 1) * rp + min(j, rp - 8));
         }
     }
-    // 1c. S rows: thread t covers row t / 4, quarter t % 4 of rp
+    // 1c. S rows: thread t covers row t / 4, rank positions 16 (t % 4) .. +16;
+    //     positions past rp are written as zeros, so the MFMA operand reads
+    //     below need no mask
     {
         const int row = tid / 4, qt = tid % 4;
         const int sr = row < rows ? rs.in_row[r0 + row] : -1;
-        const int per = rp / 4;                       // 4..16, a multiple of 4
         float4 sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            sv[e] = ldf4_if(S + (int64_t)sr * sld + sc0 + qt * per + e * 4, sr >= 0 && e * 4 < per, S);
+        for (int e = 0; e < 4; ++e) {
+            const int j = qt * 16 + e * 4;
+            sv[e] = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
+        }
+        uint32_t h[8], l[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (e * 4 >= per) break;
             const float v[4] = {sv[e].x, sv[e].y, sv[e].z, sv[e].w};
-            uint32_t h[4], l[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                h[q] = f32_to_bf16(v[q]);
-                l[q] = f32_to_bf16(v[q] - bf16_to_f32(h[q]));
+            for (int q = 0; q < 4; q += 2) {
+                const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+                const uint32_t l0 = f32_to_bf16(v[q] - bf16_to_f32(h0));
+                const uint32_t l1 = f32_to_bf16(v[q + 1] - bf16_to_f32(h1));
+                h[e * 2 + q / 2] = h0 | (h1 << 16);
+                l[e * 2 + q / 2] = l0 | (l1 << 16);
             }
-            const int j = qt * per + e * 4;
-            *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
         }
+        uint4* hp = reinterpret_cast<uint4*>(sHi + row * kSLds + qt * 16);
+        uint4* lp = reinterpret_cast<uint4*>(sLo + row * kSLds + qt * 16);
+        hp[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        hp[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        lp[0] = make_uint4(l[0], l[1], l[2], l[3]);
+        lp[1] = make_uint4(l[4], l[5], l[6], l[7]);
     }
     __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
     __syncthreads();
@@ -256,9 +268,8 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 const int j = st * 32 + lq * 8;
-                const bool jin = st < nsteps && j < rp;
-                shi[st] = ld16_if(sHi + (rg * 16 + lr) * kSLds + j, jin, sHi);
-                slo[st] = ld16_if(sLo + (rg * 16 + lr) * kSLds + j, jin, sLo);
+                shi[st] = ld16(sHi + (rg * 16 + lr) * kSLds + j);
+                slo[st] = ld16(sLo + (rg * 16 + lr) * kSLds + j);
             }
             const int r = rg * 16 + lr;
 #pragma unroll
