@@ -64,6 +64,8 @@ template <> struct Io<uint16_t> {
 // exec-mask branch followed by a wait for it, which serialises the loads
 // that were meant to be in flight together.
 // ----------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
 __device__ __forceinline__ uint32_t opaque_mask(bool ok) {
     uint32_t m = ok ? 0xffffffffu : 0u;
     asm("" : "+v"(m));     // not volatile: equal masks may still be shared
@@ -98,6 +100,33 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Sum over each row of 16 lanes, left in every lane of the row, with DPP
+// lane swaps (VALU only: swap neighbours, swap pairs, mirror half rows, mirror
+// rows).  Fixed order, so the result is deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_move<0x141>(v);   // row_half_mirror
+    v += dpp_move<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Sum over the whole wavefront, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_total(float v) {
+    v = row16_sum(v);
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63)));
+}
 
 // ----------------------------------------------------------------------------
 // tagged exchange slots

@@ -9,16 +9,16 @@
 //   producers  (blockIdx <  grid1): unit = (segment, 16 rows of A, 512-wide K
 //              chunk).  Lanes stream one row of A chunk each 1 KB at a time
 //              (coalesced 16-byte loads), dot it with the segment's token rows
-//              and reduce across the wavefront.  Each partial sum goes into a
-//              tagged 64-bit exchange slot.
+//              and reduce across the wavefront with DPP lane swaps.  Each
+//              partial sum goes into a tagged 64-bit exchange slot.
 //   consumers  (blockIdx >= grid1): unit = (segment, 256 output columns of a
-//              slice).  They first issue the loads of their B tile (coalesced:
-//              consecutive lanes read consecutive 16-byte chunks of the
-//              row-major [N, rp] block) and only then wait for the segment's
-//              slots, sum the K chunks in a fixed order into LDS (S stays on
-//              chip), and finish with a lane-group reduce-scatter so that each
-//              lane ends up owning one output column for the read-modify-write
-//              of y.
+//              slice), thread t owning column n0 + t.  A thread first loads its
+//              column's B row (rp contiguous values) and the y values it will
+//              update, and only then waits for the segment's slots; the K-chunk
+//              partials are summed in a fixed order into LDS (S stays on chip,
+//              as a bf16 hi / lo pair for bf16 data) and each thread dots its B
+//              row with every token's S row, read from LDS as a broadcast.  No
+//              cross-lane reduction is needed on this side.
 // Consumers only wait on producers, which never wait, and producers have the
 // lower workgroup ids, so they are dispatched first; every wait is also
 // bounded (kMaxSpin) and reports a device error instead of hanging.
@@ -91,23 +91,6 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a
     }
     v.ms = p1 - v.p0;
     return v;
-}
-
-// Reduce-scatter of N partials over groups of N lanes (N a power of two):
-// afterwards v[0] on the lane with (lane % N) == g holds the group's sum of
-// partial index g.
-template <int N>
-__device__ __forceinline__ void reduce_scatter(float* v, int g) {
-#pragma unroll
-    for (int h = N / 2; h >= 1; h /= 2) {
-        const bool upper = (g & h) != 0;
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-            const float send = upper ? v[i] : v[i + h];
-            const float keep = upper ? v[i + h] : v[i];
-            v[i] = keep + __shfl_xor(send, h, kWave);
-        }
-    }
 }
 
 // ---------------------------------------------------------------- producers
@@ -233,12 +216,11 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
 #pragma unroll
         for (int u = 0; u < kTokGroup; ++u) {
             if (t0 + u >= v.ms) break;
-            // rows 0..3 summed over the wavefront: reduce-scatter inside groups
-            // of 4 lanes, then a butterfly over the 16 groups
-            reduce_scatter<4>(acc[u], lane & 3);
-            float tot = acc[u][0];
-#pragma unroll
-            for (int o = 4; o < kWave; o <<= 1) tot += __shfl_xor(tot, o, kWave);
+            // rows 0..3 summed over the wavefront (DPP row sums, then the four
+            // row totals); lane i < 4 writes row i
+            const float r0 = wave_total(acc[u][0]), r1 = wave_total(acc[u][1]);
+            const float r2 = wave_total(acc[u][2]), r3 = wave_total(acc[u][3]);
+            const float tot = lane == 0 ? r0 : lane == 1 ? r1 : lane == 2 ? r2 : r3;
             if (lane < 4) slot_put(out + (int64_t)(t0 + u) * a.cols + lane, tot);
         }
     }
@@ -249,39 +231,36 @@ constexpr int kPollBatch = 8;    // exchange slots polled together
 
 template <typename T, int RCAP>
 __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView& v, int s, int sl,
-                                            int n0, int n1, float* sS, int* sFlag) {
+                                            int n0, int n1, uint4* lds, int* sFlag) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
-    constexpr int CPR = RCAP / EPC;            // chunks per (capacity) row
-    constexpr int RPI = kWave / CPR;           // B rows per load instruction
+    constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
+    constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
     const LinearArgs& a = p.a;
     const int rp = v.rp;
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int g = lane % CPR;
-    const int rsub = lane / CPR;
-    const int nw = n0 + wave * 64;
-    const bool gin = g * EPC < rp;
+    const int tid = threadIdx.x;
     const T* B = reinterpret_cast<const T*>(a.B) + v.off;
     T* Y = reinterpret_cast<T*>(p.y);
-    const int n_out = nw + g * RPI + rsub;
+    // thread t owns output column n0 + t and keeps that column's B row
+    // (rank values 0..rp-1) in registers; rows and columns that do not exist
+    // are clamped into range and their results never stored
+    const int n_out = n0 + tid;
     const bool nin = n_out < n1;
-    // 1. B tile and the y values this lane will update, issued before any wait
-    uint4 braw[CPR];
+    const int n_ld = min(n_out, n1 - 1);
+    // 1. B row and the y values this thread will update, issued before any wait
+    uint4 brow[CPR];
 #pragma unroll
-    for (int q = 0; q < CPR; ++q) {
-        const int n = nw + q * RPI + rsub;
-        braw[q] = ld16_if(B + (int64_t)n * rp + g * EPC, gin && n < n1, B);
-    }
-    // (row and column clamped into range: values of rows or columns that do
-    // not exist are never used)
+    for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
     float yv[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
-        const int m = __shfl(v.my_idx, v.p0 + min(u, v.ms - 1), kWave);
-        yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + min(n_out, n1 - 1));
+        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + min(u, v.ms - 1));
+        yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
     }
     // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
-    //    polled kPollBatch slots at a time
+    //    polled kPollBatch slots at a time, into LDS (bf16: as a hi / lo pair)
+    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
+    float* sS = reinterpret_cast<float*>(lds);
     bool ok = true;
     const int64_t cstride = (int64_t)a.M * a.cols;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
@@ -315,51 +294,48 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
                 if (c0 + q < p.C && (uint32_t)(w[q] >> 32) == 1u)
                     acc += __uint_as_float((uint32_t)w[q]);
         }
-        sS[t * RCAP + j] = acc;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t h = f32_to_bf16(acc);
+            sHi[t * SLD + j] = (uint16_t)h;
+            sLo[t * SLD + j] = (uint16_t)f32_to_bf16(acc - bf16_to_f32(h));
+        } else {
+            sS[t * SLD + j] = acc;
+        }
     }
     if (!ok) atomicOr(p.err, kErrSpin);
     __syncthreads();
-    // 3. delta rows: lane (rsub, g) dots its chunk with S, then the CPR lanes
-    //    of a row group reduce-scatter so lane g owns row q = g of the group.
-    if (nw < n1) {
-        for (int t = 0; t < v.ms; ++t) {
-            float sv[EPC];
+    // 3. delta of column n for each token: B row . S row (read by every lane
+    //    at the same LDS address, a broadcast)
+    for (int t = 0; t < v.ms; ++t) {
+        float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) sv[e] = gin ? sS[t * RCAP + g * EPC + e] : 0.f;
-            float part[CPR];
-#pragma unroll
-            for (int q = 0; q < CPR; ++q) {
-                float bv[EPC];
-                if constexpr (sizeof(T) == 2) {
-                    const uint32_t w[4] = {braw[q].x, braw[q].y, braw[q].z, braw[q].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        bv[2 * i] = __uint_as_float(w[i] << 16);
-                        bv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-                    }
-                } else {
-                    bv[0] = __uint_as_float(braw[q].x);
-                    bv[1] = __uint_as_float(braw[q].y);
-                    bv[2] = __uint_as_float(braw[q].z);
-                    bv[3] = __uint_as_float(braw[q].w);
-                }
-                float acc = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) acc += sv[e] * bv[e];
-                part[q] = acc;
-            }
-            reduce_scatter<CPR>(part, g);
-            const int m = __shfl(v.my_idx, v.p0 + t, kWave);   // all lanes take part
-            if (nin) {
-                T* yp = Y + (int64_t)m * p.ldy + n_out;
-                float old = 0.f;
-#pragma unroll
-                for (int u = 0; u < kTokGroup; ++u)
-                    if (u == t) old = yv[u];
-                if (t >= kTokGroup) old = Io<T>::ld(yp);
-                Io<T>::st(yp, old + part[0]);
+        for (int q = 0; q < CPR; ++q) {
+            if (q * EPC >= rp) break;
+            if constexpr (sizeof(T) == 2) {
+                const uint4 h = *reinterpret_cast<const uint4*>(sHi + t * SLD + q * 8);
+                const uint4 l = *reinterpret_cast<const uint4*>(sLo + t * SLD + q * 8);
+                acc = dot2_bf16(brow[q].x, h.x, acc);
+                acc = dot2_bf16(brow[q].y, h.y, acc);
+                acc = dot2_bf16(brow[q].z, h.z, acc);
+                acc = dot2_bf16(brow[q].w, h.w, acc);
+                acc = dot2_bf16(brow[q].x, l.x, acc);
+                acc = dot2_bf16(brow[q].y, l.y, acc);
+                acc = dot2_bf16(brow[q].z, l.z, acc);
+                acc = dot2_bf16(brow[q].w, l.w, acc);
+            } else {
+                const float4 sv = *reinterpret_cast<const float4*>(sS + t * SLD + q * 4);
+                acc += __uint_as_float(brow[q].x) * sv.x + __uint_as_float(brow[q].y) * sv.y +
+                       __uint_as_float(brow[q].z) * sv.z + __uint_as_float(brow[q].w) * sv.w;
             }
         }
+        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + t);
+        T* yp = Y + (int64_t)m * p.ldy + n_out;
+        float old = 0.f;
+#pragma unroll
+        for (int u = 0; u < kTokGroup; ++u)
+            if (u == t) old = yv[u];
+        if (t >= kTokGroup) old = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
+        if (nin) Io<T>::st(yp, old + acc);
     }
     // 4. the last consumer of (segment, slice) empties the slots it shared
     __syncthreads();
@@ -383,7 +359,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
 
 template <typename T>
 __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
-    __shared__ float sS[LORA_DECODE_MAX_M * LORA_MAX_RANK];
+    __shared__ uint4 lds[LORA_DECODE_MAX_M * LORA_MAX_RANK * 4 / 16];   // the segment's S
     __shared__ int sFlag;
     if ((int)blockIdx.x < p.grid1) {
         dec_produce<T>(p, blockIdx.x);
@@ -400,11 +376,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
     const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
     const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
     if (v.rp <= 16)
-        dec_consume<T, 16>(p, v, s, sl, n0, n1, sS, &sFlag);
+        dec_consume<T, 16>(p, v, s, sl, n0, n1, lds, &sFlag);
     else if (v.rp <= 32)
-        dec_consume<T, 32>(p, v, s, sl, n0, n1, sS, &sFlag);
+        dec_consume<T, 32>(p, v, s, sl, n0, n1, lds, &sFlag);
     else
-        dec_consume<T, 64>(p, v, s, sl, n0, n1, sS, &sFlag);
+        dec_consume<T, 64>(p, v, s, sl, n0, n1, lds, &sFlag);
 }
 
 hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, void* y,

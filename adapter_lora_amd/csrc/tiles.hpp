@@ -29,8 +29,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
 // Split 8 fp32 values into bf16 hi / lo parts (8 each).
 __device__ __forceinline__ void split_hi_lo(const float* v, uint4& hi, uint4& lo) {
     uint32_t h[8], l[8];
