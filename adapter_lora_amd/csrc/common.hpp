@@ -91,6 +91,20 @@ __device__ __forceinline__ float4 ldf4_if(const float* p, bool ok, const float* 
 }
 
 // ----------------------------------------------------------------------------
+// bf16 MFMA, 16 x 16 output, K = 32 (v_mfma_f32_16x16x32_bf16).  Lane l
+// supplies row (l % 16) of the first operand and column (l % 16) of the
+// second, eight consecutive K values starting at 8 * (l / 16) for both; it
+// receives rows 4 * (l / 16) + q, q = 0..3, of column l % 16 of the result.
+// ----------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------
 // wavefront reductions
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

@@ -226,6 +226,60 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
     }
 }
 
+// bf16 producers on MFMA.  Same unit; wave w takes K values
+// [256 w, 256 w + 256) of the chunk in 8 steps of v_mfma_f32_16x16x32_bf16
+// with the segment's tokens (up to 16 at a time, missing ones zero) as the
+// first operand and the unit's 16 A rows as the second, so the reduction
+// over K happens inside the matrix core.  The four waves' 16 x 16 partials
+// are added in LDS in a fixed order and written to the exchange slots.
+__device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, int unit, float* red) {
+    const LinearArgs& a = p.a;
+    const int per_s = p.jb_max * p.C;
+    const int s = unit / per_s;
+    const int jb = (unit % per_s) / p.C;
+    const int c = unit % p.C;
+    const SegView v = seg_view(p, s, true);
+    if (s >= v.nseg || v.id < 0) return;
+    const int nb = v.rp / 16;
+    if (nb == 0 || jb >= nb * a.n_sl) return;
+    const int sl = jb / nb, jj = jb % nb;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane % 16, lq = lane / 16;
+    const int kw = c * 1024 + wave * 256 + lq * 8;          // this lane's first K value
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A) + v.off +
+                        (int64_t)(sl * v.rp + jj * 16 + lr) * a.K;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(p.x);
+    uint4 av[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < a.K, A);
+    slot_t* out = p.slots + ((int64_t)c * a.M + v.p0) * a.cols + sl * a.r_max + jj * 16;
+    for (int t0 = 0; t0 < v.ms; t0 += 16) {
+        const int nt = min(16, v.ms - t0);
+        const int m = __shfl(v.my_idx, v.p0 + t0 + min(lr, nt - 1), kWave);
+        const uint16_t* xp = X + (int64_t)m * p.ldx;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        uint4 xv[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) xv[kk] = ld16_if(xp + kw + kk * 32, lr < nt && kw + kk * 32 < a.K, X);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) acc = mfma_bf16(xv[kk], av[kk], acc);
+        // acc[q]: token 4 lq + q, A row lr
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(wave * 16 + lq * 4 + q) * 16 + lr] = acc[q];
+        __syncthreads();
+        {
+            const int tok = threadIdx.x / 16, row = threadIdx.x % 16;
+            if (tok < nt) {
+                const float sum = (red[(0 * 16 + tok) * 16 + row] + red[(1 * 16 + tok) * 16 + row]) +
+                                  (red[(2 * 16 + tok) * 16 + row] + red[(3 * 16 + tok) * 16 + row]);
+                slot_put(out + (int64_t)(t0 + tok) * a.cols + row, sum);
+            }
+        }
+        __syncthreads();     // red is rewritten by the next token group
+    }
+}
+
 // ---------------------------------------------------------------- consumers
 constexpr int kPollBatch = 8;    // exchange slots polled together
 
@@ -362,7 +416,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
     __shared__ uint4 lds[LORA_DECODE_MAX_M * LORA_MAX_RANK * 4 / 16];   // the segment's S
     __shared__ int sFlag;
     if ((int)blockIdx.x < p.grid1) {
-        dec_produce<T>(p, blockIdx.x);
+        if constexpr (sizeof(T) == 2)
+            dec_produce_mfma(p, blockIdx.x, reinterpret_cast<float*>(lds));
+        else
+            dec_produce<T>(p, blockIdx.x);
         return;
     }
     const LinearArgs& a = p.a;

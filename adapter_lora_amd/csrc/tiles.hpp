@@ -21,14 +21,6 @@
 
 namespace mlora {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
 // Split 8 fp32 values into bf16 hi / lo parts (8 each).
 __device__ __forceinline__ void split_hi_lo(const float* v, uint4& hi, uint4& lo) {
     uint32_t h[8], l[8];
