@@ -360,7 +360,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     __syncthreads();
     // 3. delta of column n for each token: B row . S row (read by every lane
     //    at the same LDS address, a broadcast)
-    for (int t = 0; t < v.ms; ++t) {
+    auto delta = [&](int t) {
         float acc = 0.f;
 #pragma unroll
         for (int q = 0; q < CPR; ++q) {
@@ -382,14 +382,28 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
                        __uint_as_float(brow[q].z) * sv.z + __uint_as_float(brow[q].w) * sv.w;
             }
         }
-        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + t);
-        T* yp = Y + (int64_t)m * p.ldy + n_out;
-        float old = 0.f;
+        return acc;
+    };
+    //    The first kTokGroup tokens take every prefetched y value before the
+    //    first store: the wait for a load counts the stores issued after it,
+    //    so a store in between would add its whole latency to the next token.
+    float res[kTokGroup];
 #pragma unroll
-        for (int u = 0; u < kTokGroup; ++u)
-            if (u == t) old = yv[u];
-        if (t >= kTokGroup) old = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
-        if (nin) Io<T>::st(yp, old + acc);
+    for (int u = 0; u < kTokGroup; ++u) {
+        if (u >= v.ms) break;
+        res[u] = yv[u] + delta(u);
+    }
+#pragma unroll
+    for (int u = 0; u < kTokGroup; ++u) {
+        if (u >= v.ms) break;
+        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + u);
+        if (nin) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, res[u]);
+    }
+    for (int t = kTokGroup; t < v.ms; ++t) {
+        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + t);
+        const float old = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
+        const float r = old + delta(t);
+        if (nin) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, r);
     }
     // 4. the last consumer of (segment, slice) empties the slots it shared
     __syncthreads();
