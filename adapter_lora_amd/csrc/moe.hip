@@ -144,7 +144,7 @@ struct MoeUnit {
 // and write nothing; rows past the block's last real row are not visited.
 __device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool shrink, int l, int b,
                                             int* s_in, int* s_out, int* s_wlast) {
-    const int bs = a.block_size_m;                // <= kTileThreads
+    const int bs = a.block_size_m;                // <= blockDim.x; s_wlast: one int per wave
     const int P = a.M * a.topk;
     const int i = threadIdx.x;
     const int pos = b * bs + min(i, bs - 1);
@@ -170,7 +170,7 @@ __device__ __forceinline__ MoeUnit moe_unit(const MoeArgs& a, int which, bool sh
     __syncthreads();
     int last = -1;
 #pragma unroll
-    for (int w = 0; w < kTileWaves; ++w) last = max(last, s_wlast[w]);
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) last = max(last, s_wlast[w]);
     return MoeUnit{true, e, last + 1};
 }
 
@@ -259,6 +259,31 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
     }
 }
 
+// bf16 expand over wide tiles: unit = (aligned block, 1024 output columns).
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_moe_expand_wide(MoeArgs a, int which,
+                                                                   const float* __restrict__ S,
+                                                                   uint16_t* __restrict__ out,
+                                                                   int64_t ld_out, int N,
+                                                                   int n_groups, int units) {
+    __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
+    __shared__ int s_wlast[kWideThreads / kWave];
+    __shared__ uint4 lds[kWideLds / 16];
+    const int nblk = a.max_tokens_padded / a.block_size_m;
+    const int unit = (int)blockIdx.x;
+    if (unit >= units) return;
+    const int blk = unit / n_groups;
+    const int g = unit % n_groups;
+    const int l = blk / nblk, b = blk % nblk;
+    const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
+    if (!mu.ok) return;
+    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const uint16_t* B =
+        reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
+    const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
+    const int n0 = g * kWideCols;
+    expand_rows_wide(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds);
+}
+
 template <typename T>
 static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64_t ld_in,
                               void* out, int64_t ld_out, void* ws, hipStream_t st) {
@@ -289,8 +314,19 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     const int n_groups = (n_tiles + tpw - 1) / tpw;
     const int units2 = a.L * nblk * n_groups;
     const unsigned g2 = (unsigned)(units2 > 0 ? units2 : 1);
-    hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
-                       reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2);
+    // wide 16 x 1024 tiles when the output is wide enough that 64 x 256 tiles
+    // would need many rounds of mostly idle workgroups (the gate/up output)
+    if (sizeof(T) == 2 && N >= 2 * kWideCols * 4) {
+        const int wg = (N + kWideCols - 1) / kWideCols;
+        const int wunits = a.L * nblk * wg;
+        hipLaunchKernelGGL(k_moe_expand_wide, dim3((unsigned)(wunits > 0 ? wunits : 1)),
+                           dim3(kWideThreads), 0, st, a, which, S,
+                           static_cast<uint16_t*>(out),
+                           ld_out, N, wg, wunits);
+    } else {
+        hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
+                           reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2);
+    }
     return hipGetLastError();
 }
 

@@ -317,6 +317,140 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
 // ---------------------------------------------------------------------------
 // plain vector-ALU versions (any storage type); used for fp32 storage
 // ---------------------------------------------------------------------------
+// Wide expand tile for sparse row blocks (MoE): 16 rows x 1024 columns, 512
+// threads.  Wave w owns columns n0 + 128w .. +128 as 8 blocks of 16.  The
+// same three phases as the 64 x 256 tile (y tile straight into LDS, MFMA
+// results folded into it, row-major write-back), but a unit with few rows
+// carries four times the columns, so an MoE block of about 16 real rows
+// needs a quarter of the workgroups.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 512;
+constexpr int kWideCols = 1024;
+constexpr int kWideRowChunks = kWideCols / 8;                       // 128 chunks of 16 bytes
+constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
+
+__device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
+
+__device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int rows,
+                                                 const float* __restrict__ S, int sld, int sc0,
+                                                 const uint16_t* __restrict__ B, int rp, int n0,
+                                                 int n1, uint16_t* __restrict__ y, int64_t ldy_,
+                                                 uint4* __restrict__ ytile,
+                                                 uint16_t* __restrict__ sHi,
+                                                 uint16_t* __restrict__ sLo) {
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;                 // 0..7
+    const int lr = lane % 16;
+    const int lq = lane / 16;
+    const int nsteps = (rp + 31) / 32;
+    const int nw = n0 + wave * 128;
+    const int nchunks = (n1 - n0) / 8;            // valid 16-byte chunks per row
+    // 1a. y rows -> LDS: 32 wave instructions of 1 KB (half a row); position
+    //     p of row r holds chunk p ^ r
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = wave * 4 + i;
+        const int r = k / 2, h = k % 2;
+        const int q = (h * 64 + lane) ^ r;
+        const int yr = r < rows ? rs.out_row[r0 + r] : -1;
+        const bool ok = yr >= 0 && q < nchunks;
+        const uint16_t* src = ok ? y + (int64_t)yr * ldy_ + n0 + q * 8 : y;
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(ytile + r * kWideRowChunks + h * 64), 16, 0,
+                                         0);
+    }
+    // 1b. B operands: rows nw + 16 nb + lr (clamped; see expand_tile_bf16)
+    uint4 bop[8][2];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        const int n = min(nw + nb * 16 + lr, n1 - 1);
+        bop[nb][0] = ld16(B + (int64_t)n * rp + min(lq * 8, rp - 8));
+        bop[nb][1] = make_uint4(0, 0, 0, 0);
+    }
+    if (nsteps > 1) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int n = min(nw + nb * 16 + lr, n1 - 1);
+            bop[nb][1] = ld16(B + (int64_t)n * rp + min(32 + lq * 8, rp - 8));
+        }
+    }
+    // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
+    //     .. +4; positions past rp are written as zeros
+    if (tid < 256) {
+        const int row = tid / 16, j = (tid % 16) * 4;
+        const int sr = row < rows ? rs.in_row[r0 + row] : -1;
+        const float4 v4 = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        uint32_t h[2], l[2];
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+            const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+            h[q / 2] = h0 | (h1 << 16);
+            l[q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
+                       (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
+        }
+        *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
+        *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
+    __syncthreads();
+    // 2. MFMA: the one 16-row group; each 16 x 16 result is added into the tile
+    if (nw < n1) {
+        uint4 shi[2], slo[2];
+        shi[0] = ld16(sHi + lr * kSLds + lq * 8);
+        slo[0] = ld16(sLo + lr * kSLds + lq * 8);
+        shi[1] = slo[1] = make_uint4(0, 0, 0, 0);
+        if (nsteps > 1) {
+            shi[1] = ld16(sHi + lr * kSLds + 32 + lq * 8);
+            slo[1] = ld16(sLo + lr * kSLds + 32 + lq * 8);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            // acc[e]: column c + e of row lr, where c = 128 wave + 16 nb + 4 lq
+            const int c = wave * 128 + nb * 16 + lq * 4;
+            uint2* yp = reinterpret_cast<uint2*>(ytile + wpos(lr, c / 8)) + ((c / 4) & 1);
+            const uint2 old = *yp;
+            f32x4_t acc = {__uint_as_float(old.x << 16), __uint_as_float(old.x & 0xffff0000u),
+                           __uint_as_float(old.y << 16), __uint_as_float(old.y & 0xffff0000u)};
+            acc = mfma_bf16(bop[nb][0], shi[0], acc);
+            acc = mfma_bf16(bop[nb][0], slo[0], acc);
+            if (nsteps > 1) {
+                acc = mfma_bf16(bop[nb][1], shi[1], acc);
+                acc = mfma_bf16(bop[nb][1], slo[1], acc);
+            }
+            uint2 nv;
+            nv.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+            nv.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            *yp = nv;
+        }
+    }
+    __syncthreads();
+    // 3. row-major write-back: a wave instruction stores 64 chunks of one row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = i * kWideThreads + tid;
+        const int r = idx / kWideRowChunks, q = idx % kWideRowChunks;
+        const int yr = r < rows ? rs.out_row[r0 + r] : -1;
+        if (yr >= 0 && q < nchunks)
+            *reinterpret_cast<uint4*>(y + (int64_t)yr * ldy_ + n0 + q * 8) = ytile[wpos(r, q)];
+    }
+    __syncthreads();     // the LDS tile is reused by the next row group
+}
+
+// All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
+__device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* __restrict__ S,
+                                                 int sld, int sc0,
+                                                 const uint16_t* __restrict__ B, int rp, int n0,
+                                                 int n1, uint16_t* __restrict__ y, int64_t ldy_,
+                                                 uint4* __restrict__ lds) {
+    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
+    uint16_t* sLo = sHi + 16 * kSLds;
+    for (int r0 = 0; r0 < rs.n; r0 += 16)
+        expand_wide_bf16(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds, sHi,
+                         sLo);
+}
+
+// ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void shrink_tile_simple(const RowSet& rs, const T* __restrict__ x,
                                                    int64_t ldx, const T* __restrict__ A, int K,

@@ -75,6 +75,11 @@ MOE_CASES = [
                                             block_size_m=16, p_none=0.2, enabled=[1, 1, 0])),
     ("small_fp32", lambda: W.moe_case(5, M=33, H=136, I=72, E=4, topk=2, L=2, rank=16,
                                       block_size_m=64, dtype=W.F32)),
+    # gate/up output of 2I = 8208 columns: the wide (16 x 1024) expand tiles
+    # with a ragged last tile of 16 columns; rank 64 (two K steps); blocks of
+    # 32 rows with up to 2 row groups of 16
+    ("wide_ragged_bf16", lambda: W.moe_case(7, M=150, H=264, I=4104, E=3, topk=2, L=2, rank=64,
+                                            block_size_m=32)),
 ]
 
 
