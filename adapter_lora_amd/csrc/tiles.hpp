@@ -251,15 +251,22 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
     __syncthreads();
     // 2. MFMA; each 16 x 16 result is added into the LDS tile
     if (nw < n1) {
+        // S operands of the next row group are read while this one's MFMAs run
+        uint4 shi[2], slo[2], nhi[2], nlo[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            shi[st] = ld16(sHi + lr * kSLds + st * 32 + lq * 8);
+            slo[st] = ld16(sLo + lr * kSLds + st * 32 + lq * 8);
+        }
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             if (rg * 16 >= rows) break;
-            uint4 shi[2], slo[2];
+            if (rg < 3) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int j = st * 32 + lq * 8;
-                shi[st] = ld16(sHi + (rg * 16 + lr) * kSLds + j);
-                slo[st] = ld16(sLo + (rg * 16 + lr) * kSLds + j);
+                for (int st = 0; st < 2; ++st) {
+                    nhi[st] = ld16(sHi + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
+                    nlo[st] = ld16(sLo + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
+                }
             }
             const int r = rg * 16 + lr;
 #pragma unroll
@@ -282,6 +289,11 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
                 nv.y = f32_to_bf16(__uint_as_float(old.y << 16) + acc[2]) |
                        (f32_to_bf16(__uint_as_float(old.y & 0xffff0000u) + acc[3]) << 16);
                 *yp = nv;
+            }
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                shi[st] = nhi[st];
+                slo[st] = nlo[st];
             }
         }
     }
