@@ -22,6 +22,8 @@ Protocol:
   * HBM traffic per launch comes from those counter runs, kept as a summary
     under profiles/ with a hash of the kernel's sources; it is reported only
     while the sources still match the hash;
+  * the same step is also captured as a HIP graph (one per input copy) and
+    replayed, reported under "graph_replay" as context;
   * the oracle (fp64 CPU) is timed on the host on a bounded sample.
 Other configurations (prefill, stacked QKV / gate-up, MoE) are measured the
 same way and reported under "extra" as context; the headline line is the
@@ -198,9 +200,25 @@ def bench_linear(case, steps, warmup, fused_kernel_name):
 
     ms_step, ms_wall = run_timed(step, steps, warmup)
     ms_kernel = back_to_back(kernel, steps)     # segment tables of every copy are built
+    # the same step captured as one HIP graph per input copy, replayed in turn
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ms_graph, _ = run_timed(lambda i: graphs[i % R].replay(), steps, warmup)
     assert ml.lora_read_device_error(ws.buf) == 0, "device error during the bench"
     res = {
         "ms_per_step": ms_step, "ms_kernel_b2b": ms_kernel, "ms_wall_host": ms_wall,
+        "ms_per_step_graph": ms_graph,
         "tokens_per_s": m_valid / (ms_step * 1e-3), "m_valid": m_valid, "M": case.M,
         "adapters_touched": touched, "alg_bytes": nbytes, "alg_flops": flops,
         "kernel": fused_kernel_name, "rotation_copies": R,
@@ -209,7 +227,7 @@ def bench_linear(case, steps, warmup, fused_kernel_name):
     }
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     res["mfma_frac"] = res["tflops"] / BF16_MFMA_PEAK_TFLOPS
-    del copies
+    del copies, graphs
     torch.cuda.empty_cache()
     return res
 
@@ -364,6 +382,10 @@ def main():
             "traffic_detail": traffic},
         "cpu_baseline": cpu,
         "copy_ceiling": ceiling,
+        "graph_replay": None if head is None else {
+            "ms_per_step": head["ms_per_step_graph"],
+            "tokens_per_s": head["m_valid"] / (head["ms_per_step_graph"] * 1e-3),
+            "note": "the same step captured as one HIP graph per input copy"},
         "extra": {k: v for k, v in results.items() if k != "decode_bf16"},
     }
     print(json.dumps(line), flush=True)
