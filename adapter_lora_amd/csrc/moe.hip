@@ -209,6 +209,70 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
     }
 }
 
+// bf16 shrink for sparse blocks: unit = (aligned block, K chunk of 1024, 16
+// S columns).  Wave w takes K values [256 w, 256 w + 256) of the chunk in 8
+// steps of v_mfma_f32_16x16x32_bf16 with 16 of the block's rows as the first
+// operand and the unit's 16 A rows (kept in registers for every row group)
+// as the second; the four waves' partials are added in LDS in a fixed order.
+// Only real rows are visited, 16 at a time, so a block of ~16 real rows costs
+// one MFMA chain per wave instead of a 64-row tile.
+constexpr int kNarrowK = 1024;
+
+__global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, int which,
+                                                                     const uint16_t* __restrict__ in,
+                                                                     int64_t ld_in,
+                                                                     float* __restrict__ P, int C,
+                                                                     int G, int K, int units) {
+    __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
+    __shared__ int s_wlast[kTileWaves];
+    __shared__ float red[kTileWaves * 16 * 16];
+    const int nblk = a.max_tokens_padded / a.block_size_m;
+    const int unit = (int)blockIdx.x;
+    if (unit >= units) return;
+    const int blk = unit / (C * G);
+    const int c = (unit / G) % C;
+    const int cb = unit % G;
+    const int l = blk / nblk, b = blk % nblk;
+    const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out, s_wlast);
+    if (!mu.ok) return;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane % 16, lq = lane / 16;
+    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(which == 0 ? a.A_gu : a.A_d) +
+                        (ew * a.r + cb * 16 + lr) * K;
+    const int kw = c * kNarrowK + wave * 256 + lq * 8;     // this lane's first K value
+    uint4 av[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < K, A);
+    float* Pc = P + (int64_t)c * a.L * a.max_tokens_padded * a.r;
+    for (int r0 = 0; r0 < mu.n; r0 += 16) {
+        const int i = r0 + lr;
+        const int xr = i < mu.n ? s_in[i] : -1;
+        const uint16_t* xp = in + (int64_t)(xr < 0 ? 0 : xr) * ld_in;
+        uint4 xv[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            xv[kk] = ld16_if(xp + kw + kk * 32, xr >= 0 && kw + kk * 32 < K, in);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) acc = mfma_bf16(xv[kk], av[kk], acc);
+        // acc[q]: block row r0 + 4 lq + q, S column cb*16 + lr
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[(wave * 16 + lq * 4 + q) * 16 + lr] = acc[q];
+        __syncthreads();
+        {
+            const int row = threadIdx.x / 16, col = threadIdx.x % 16;
+            const int orow = r0 + row < mu.n ? s_out[r0 + row] : -1;
+            if (orow >= 0)
+                Pc[(int64_t)orow * a.r + cb * 16 + col] =
+                    (red[(0 * 16 + row) * 16 + col] + red[(1 * 16 + row) * 16 + col]) +
+                    (red[(2 * 16 + row) * 16 + col] + red[(3 * 16 + row) * 16 + col]);
+        }
+        __syncthreads();     // red is rewritten by the next row group
+    }
+}
+
 // S rows of the aligned positions that exist (pos < ntpp[l]).
 __global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride,
                              float* __restrict__ S, int r, int mtp,
@@ -289,15 +353,23 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
                               void* out, int64_t ld_out, void* ws, hipStream_t st) {
     const int K = which == 0 ? a.H : a.I;
     const int N = which == 0 ? 2 * a.I : a.H;
-    const int C = sizeof(T) == 2 ? (K + kShrinkK - 1) / kShrinkK : kchunks(K);
+    const int C = sizeof(T) == 2 ? (K + kNarrowK - 1) / kNarrowK : kchunks(K);
     const int nblk = a.max_tokens_padded / a.block_size_m;
     const MoeWs W = moe_ws_layout(a.L, a.max_tokens_padded, a.r, a.H > a.I ? a.H : a.I);
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.partial);
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
-    const int units = a.L * nblk * C;
-    const unsigned g1 = (unsigned)(units > 0 ? units : 1);
-    hipLaunchKernelGGL((k_moe_shrink<T>), dim3(g1), dim3(kTileThreads), 0, st, a, which,
-                       reinterpret_cast<const T*>(in), ld_in, P, C, K, units);
+    if constexpr (sizeof(T) == 2) {
+        const int G = a.r / 16;
+        const int units = a.L * nblk * C * G;
+        hipLaunchKernelGGL(k_moe_shrink_narrow, dim3((unsigned)(units > 0 ? units : 1)),
+                           dim3(kTileThreads), 0, st, a, which,
+                           reinterpret_cast<const uint16_t*>(in), ld_in, P, C, G, K, units);
+    } else {
+        const int units = a.L * nblk * C;
+        hipLaunchKernelGGL((k_moe_shrink<T>), dim3((unsigned)(units > 0 ? units : 1)),
+                           dim3(kTileThreads), 0, st, a, which, reinterpret_cast<const T*>(in),
+                           ld_in, P, C, K, units);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
