@@ -20,7 +20,8 @@ from ._abi import (LORA_BF16, LORA_F32, LORA_MAX_ADAPTERS, LORA_MAX_RANK,
 __all__ = [
     "LORA_BF16", "LORA_F32", "LoraError", "LoraTable", "Segments", "Workspace",
     "MoeWeights", "MoeAlign",
-    "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
+    "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",
+    "lora_shrink_expand_add", "lora_fused_decode",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
     "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
@@ -151,13 +152,28 @@ class Segments:
                                  p32(self.num_tiles), self.L, self.max_tiles)
 
 
-def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None) -> None:
-    if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1:
-        raise LoraError("ids must be a 1-D int32 device tensor")
-    M = ids.shape[0]
+def _ids_arg(ids: torch.Tensor) -> int:
+    if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1 or not ids.is_contiguous():
+        raise LoraError("ids must be a contiguous 1-D int32 device tensor")
+    return ids.shape[0]
+
+
+def _mask_arg(adapter_enabled: Optional[torch.Tensor], L: int) -> ctypes.c_void_p:
+    if adapter_enabled is None:
+        return _ptr(None)
+    t = adapter_enabled
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.numel() < L:
+        raise LoraError("adapter_enabled must be a contiguous int32 device tensor of L entries")
+    return _ptr(t)
+
+
+def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None,
+                        adapter_enabled: Optional[torch.Tensor] = None) -> None:
+    M = _ids_arg(ids)
     if M > seg.sorted_idx.shape[0]:
         raise LoraError("segment buffers too small")
-    check(lib.lora_build_segments(_ptr(ids), M, seg.L, _ptr(seg.sorted_idx), _ptr(seg.seg_indptr),
+    check(lib.lora_build_segments(_ptr(ids), _mask_arg(adapter_enabled, seg.L), M, seg.L,
+                                  _ptr(seg.sorted_idx), _ptr(seg.seg_indptr),
                                   _ptr(seg.req_to_lora), _ptr(seg.num_segments),
                                   _ptr(seg.tile_info), _ptr(seg.tile_rows), _ptr(seg.num_tiles),
                                   seg.max_tiles, stream_handle(stream)), "lora_build_segments")
@@ -225,6 +241,32 @@ def lora_shrink_expand_add(table: LoraTable, x: torch.Tensor, seg: Segments, y: 
                                      ctypes.byref(seg.c), _ptr(y), ldy, _ptr(ws.buf),
                                      ws.buf.numel(), stream_handle(stream)),
           "lora_shrink_expand_add")
+
+
+def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
+                      ws: Workspace, seg: Optional[Segments] = None,
+                      adapter_enabled: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One launch: y += (x A_id^T) B_id^T for up to 64 tokens, grouped by
+    adapter on chip; when `seg` is given the launch also writes the batch's
+    segment table there."""
+    M = _ids_arg(ids)
+    ldx, ldy = _rows(x, "x"), _rows(y, "y")
+    if x.shape[0] != M or y.shape[0] != M:
+        raise LoraError("ids, x and y must have the same number of rows")
+    if seg is not None:
+        if seg.L != table.L or M > seg.sorted_idx.shape[0]:
+            raise LoraError("segment buffers do not match the table or the batch")
+        outs = [_ptr(seg.sorted_idx), _ptr(seg.seg_indptr), _ptr(seg.req_to_lora),
+                _ptr(seg.num_segments), _ptr(seg.tile_info), _ptr(seg.tile_rows),
+                _ptr(seg.num_tiles)]
+        cap = seg.max_tiles
+    else:
+        outs = [_ptr(None)] * 7
+        cap = 0
+    check(lib.lora_fused_decode(ctypes.byref(table.c), _ptr(ids),
+                                _mask_arg(adapter_enabled, table.L), _ptr(x), ldx, M, _ptr(y),
+                                ldy, *outs, cap, _ptr(ws.buf), ws.buf.numel(),
+                                stream_handle(stream)), "lora_fused_decode")
 
 
 # ------------------------------------------------------------------------- MoE

@@ -17,7 +17,7 @@ LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
 LORA_TILE_ROWS = 64
-MLORA_ABI_VERSION = 1
+MLORA_ABI_VERSION = 2
 
 
 class LoraError(RuntimeError):
@@ -76,10 +76,12 @@ SIGNATURES = {
     "lora_table_plan": (I32, [I32, PI32, I32, I32, I64, PI32, PI64, PI64, PI64, PI64]),
     "lora_pack_adapter": (I32, [I32, I32, I64, I32, I32, I32, P, P, P, P, P]),
     "lora_tile_capacity": (I32, [I32, I32]),
-    "lora_build_segments": (I32, [P, I32, I32, P, P, P, P, P, P, P, I32, P]),
+    "lora_build_segments": (I32, [P, P, I32, I32, P, P, P, P, P, P, P, I32, P]),
     "lora_shrink": (I32, [PW, P, I64, I32, PS, P, P, SZ, P]),
     "lora_expand_add": (I32, [PW, P, I32, PS, P, I64, P]),
     "lora_shrink_expand_add": (I32, [PW, P, I64, I32, PS, P, I64, P, SZ, P]),
+    "lora_fused_decode": (I32, [PW, P, P, P, I64, I32, P, I64, P, P, P, P, P, P, P, I32, P, SZ,
+                                P]),
     "lora_moe_align_capacity": (I32, [I32, I32, I32, I32]),
     "lora_moe_align_run": (I32, [P, P, P, I32, I32, I32, I32, PMA, P]),
     "lora_moe_workspace_size": (SZ, [PMW, I32]),

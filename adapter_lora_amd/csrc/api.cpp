@@ -222,17 +222,18 @@ int32_t lora_tile_capacity(int32_t M, int32_t L) {
     return M / LORA_TILE_ROWS + std::min(L, M);
 }
 
-lora_status lora_build_segments(const int32_t* ids, int32_t M, int32_t L, int32_t* sorted_idx,
-                                int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
-                                int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
-                                int32_t max_tiles, hipStream_t stream) {
+lora_status lora_build_segments(const int32_t* ids, const int32_t* adapter_enabled, int32_t M,
+                                int32_t L, int32_t* sorted_idx, int32_t* seg_indptr,
+                                int32_t* req_to_lora, int32_t* num_segments, int32_t* tile_info,
+                                int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
+                                hipStream_t stream) {
     if (M < 0 || M > (1 << 24) || L < 1 || L > LORA_MAX_ADAPTERS) return LORA_INVALID_ARG;
     if (!seg_indptr || !req_to_lora || !num_segments || !num_tiles) return LORA_INVALID_ARG;
     if (max_tiles < lora_tile_capacity(M, L)) return LORA_INVALID_ARG;
     if (M > 0 && (!ids || !sorted_idx || !tile_info || !tile_rows)) return LORA_INVALID_ARG;
-    return from_hip(launch_build_segments(ids, M, L, sorted_idx, seg_indptr, req_to_lora,
-                                          num_segments, tile_info, tile_rows, num_tiles,
-                                          max_tiles, stream));
+    return from_hip(launch_build_segments(ids, adapter_enabled, M, L, sorted_idx, seg_indptr,
+                                          req_to_lora, num_segments, tile_info, tile_rows,
+                                          num_tiles, max_tiles, stream));
 }
 
 lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int32_t M,
@@ -281,11 +282,51 @@ lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64
     const LinearWs L = layout_for(w, M);
     if (workspace_bytes < L.total) return LORA_INVALID_ARG;
     const LinearArgs a = make_args(w, seg, M);
-    if (M <= LORA_DECODE_MAX_M) return from_hip(launch_decode_fused(a, x, ldx, y, ldy, workspace, stream));
+    if (M <= LORA_DECODE_MAX_M)
+        return from_hip(launch_decode_fused(a, nullptr, nullptr, SegOut{}, x, ldx, y, ldy,
+                                            workspace, stream));
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.S);
     hipError_t e = launch_shrink(a, x, ldx, S, workspace, stream);
     if (e != hipSuccess) return LORA_HIP_ERROR;
     return from_hip(launch_expand(a, S, y, ldy, stream));
+}
+
+lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
+                              const int32_t* adapter_enabled, const void* x, int64_t ldx,
+                              int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                              int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
+                              int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
+                              int32_t max_tiles, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    lora_status st = check_weights(w);
+    if (st != LORA_OK) return st;
+    if (M < 0) return LORA_INVALID_ARG;
+    if (M > LORA_DECODE_MAX_M) return LORA_UNSUPPORTED;
+    const bool table = sorted_idx != nullptr;
+    if (table) {
+        if (!seg_indptr || !req_to_lora || !num_segments || !tile_info || !tile_rows || !num_tiles)
+            return LORA_INVALID_ARG;
+        if (max_tiles < lora_tile_capacity(M, w->L)) return LORA_INVALID_ARG;
+    }
+    if (M == 0) {
+        if (!table) return LORA_OK;
+        return from_hip(launch_build_segments(nullptr, nullptr, 0, w->L, sorted_idx, seg_indptr,
+                                              req_to_lora, num_segments, tile_info, tile_rows,
+                                              num_tiles, max_tiles, stream));
+    }
+    if (!ids) return LORA_INVALID_ARG;
+    if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
+    if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+        return LORA_INVALID_ARG;
+    if (workspace_bytes < layout_for(w, M).total) return LORA_INVALID_ARG;
+    // segment-table fields of the args are unused in ids mode
+    lora_segments_t none{};
+    LinearArgs a = make_args(w, &none, M);
+    const SegOut out{sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
+                     num_tiles};
+    return from_hip(launch_decode_fused(a, ids, adapter_enabled, out, x, ldx, y, ldy, workspace,
+                                        stream));
 }
 
 // ------------------------------------------------------------------ MoE

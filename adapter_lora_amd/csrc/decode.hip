@@ -24,6 +24,7 @@
 // bounded (kMaxSpin) and reports a device error instead of hanging.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "wave_groups.hpp"
 
 namespace mlora {
 
@@ -44,14 +45,20 @@ struct DecodeParams {
     int grid1;
     int n_tiles;
     int tile_start[LORA_MAX_SLICES + 1];
+    const int32_t* ids;      // non-null: segments grouped on chip from the ids
+    const int32_t* enabled;  // adapter mask for that grouping (may be null)
+    SegOut out;              // segment table written by the last workgroup (ids mode)
+    int writer;              // 1 when the last workgroup writes `out`
 };
 
 // ---------------------------------------------------------------- shared view
 // Everything a workgroup needs to know about segment s, fetched with
 // independent loads so that the index lookups cost one memory round trip:
-// the segment bounds, its adapter id, the whole sorted token list (M <= 64,
-// one entry per lane) and, for tables of up to 256 slots, every slot's rank
-// and weight offset (picked by lane shuffle once the id is known).
+// either the segment table's entries for s and the whole sorted token list
+// (M <= 64, one entry per lane), or, in ids mode, every token's id (the
+// grouping is then computed in registers, wave_groups.hpp); and, for tables
+// of up to 256 slots, every slot's rank and weight offset (picked by lane
+// shuffle once the id is known).
 struct SegView {
     int nseg, id, rp, p0, ms, my_idx;
     int64_t off;
@@ -62,30 +69,46 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a
     const int lane = lane_id();
     const int64_t* offs = a_side ? a.a_off : a.b_off;
     SegView v;
-    v.nseg = a.num_segments[0];
-    v.id = a.req_to_lora[s];
-    v.p0 = a.seg_indptr[s];
-    const int p1 = a.seg_indptr[s + 1];
-    // indices are clamped rather than tested, so every load is unconditional
-    // and all of them are in flight together
-    v.my_idx = a.sorted_idx[min(lane, a.M - 1)];
-    if (a.L <= 4 * kWave) {
-        int rk[4];
-        int64_t of[4];
+    TokenLoad tl;
+    int p1 = 0;
+    if (p.ids) {
+        tl = load_token(p.ids, p.enabled, a.M, a.L);
+    } else {
+        v.nseg = a.num_segments[0];
+        v.id = a.req_to_lora[s];
+        v.p0 = a.seg_indptr[s];
+        p1 = a.seg_indptr[s + 1];
+        // indices are clamped rather than tested, so every load is
+        // unconditional and all of them are in flight together
+        v.my_idx = a.sorted_idx[min(lane, a.M - 1)];
+    }
+    int rk[4];
+    int64_t of[4];
+    const bool small = a.L <= 4 * kWave;
+    if (small) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int j = min(q * kWave + lane, a.L - 1);
             rk[q] = a.rank[j];
             of[q] = offs[j];
         }
-        const int id = v.id < 0 ? 0 : v.id;
+    }
+    if (p.ids) {
+        const WaveGroups g = wave_group(token_bucket(tl, p.enabled, a.L), a.M, a.L);
+        int n;
+        wave_segment(g, s, &v.p0, &n, &v.id);
+        v.nseg = g.nseg;
+        v.my_idx = g.key & 63;
+        p1 = v.p0 + n;
+    }
+    const int id = v.id < 0 ? 0 : v.id;
+    if (small) {
         const int q = id / kWave, src = id % kWave;
         const int r_sel = q == 0 ? rk[0] : q == 1 ? rk[1] : q == 2 ? rk[2] : rk[3];
         const int64_t o_sel = q == 0 ? of[0] : q == 1 ? of[1] : q == 2 ? of[2] : of[3];
         v.rp = __shfl(r_sel, src, kWave);
         v.off = __shfl(o_sel, src, kWave);
     } else {
-        const int id = v.id < 0 ? 0 : v.id;
         v.rp = a.rank[id];
         v.off = offs[id];
     }
@@ -429,6 +452,18 @@ template <typename T>
 __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
     __shared__ uint4 lds[LORA_DECODE_MAX_M * LORA_MAX_RANK * 4 / 16];   // the segment's S
     __shared__ int sFlag;
+    if (p.writer && blockIdx.x == gridDim.x - 1) {
+        // ids mode: the segment table for later calls on the same batch
+        if (threadIdx.x < kWave) {
+            const LinearArgs& a = p.a;
+            const int b = token_bucket(load_token(p.ids, p.enabled, a.M, a.L), p.enabled, a.L);
+            const WaveGroups g = wave_group(b, a.M, a.L);
+            write_wave_segments(g, a.M, a.L, p.out.sorted_idx, p.out.seg_indptr,
+                                p.out.req_to_lora, p.out.num_segments, p.out.tile_info,
+                                p.out.tile_rows, p.out.num_tiles);
+        }
+        return;
+    }
     if ((int)blockIdx.x < p.grid1) {
         if constexpr (sizeof(T) == 2)
             dec_produce_mfma(p, blockIdx.x, reinterpret_cast<float*>(lds));
@@ -454,10 +489,15 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
         dec_consume<T, 64>(p, v, s, sl, n0, n1, lds, &sFlag);
 }
 
-hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, void* y,
+hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
+                               const SegOut& out, const void* x, int64_t ldx, void* y,
                                int64_t ldy, void* ws, hipStream_t st) {
     DecodeParams p{};
     p.a = a;
+    p.ids = ids;
+    p.enabled = ids ? enabled : nullptr;
+    p.out = out;
+    p.writer = (ids && out.sorted_idx) ? 1 : 0;
     p.x = x;
     p.ldx = ldx;
     p.y = y;
@@ -478,7 +518,7 @@ hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, 
     }
     p.tile_start[a.n_sl] = t;
     p.n_tiles = t;
-    const unsigned grid = (unsigned)(p.grid1 + a.s_max * p.n_tiles);
+    const unsigned grid = (unsigned)(p.grid1 + a.s_max * p.n_tiles + p.writer);
     if (a.dtype == LORA_BF16) {
         hipLaunchKernelGGL(k_decode_fused<uint16_t>, dim3(grid), dim3(kDecThreads), 0, st, p);
     } else {

@@ -69,8 +69,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // rows per tile of the tile schedule
 constexpr int kRowTileRows = 64;
 
-hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
-                                 int32_t* seg_indptr, int32_t* req_to_lora,
+// `enabled` (device [L], may be null): a token whose adapter is disabled is
+// treated like a token without an adapter.
+hipError_t launch_build_segments(const int32_t* ids, const int32_t* enabled, int M, int L,
+                                 int32_t* sorted_idx, int32_t* seg_indptr, int32_t* req_to_lora,
                                  int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
                                  int32_t* num_tiles, int max_tiles, hipStream_t st);
 
@@ -78,7 +80,23 @@ hipError_t launch_pack_adapter(int dtype, int K, int64_t N, int n_sl, int rank, 
                                const void* A_src, const void* B_src, void* A_dst, void* B_dst,
                                hipStream_t st);
 
-hipError_t launch_decode_fused(const LinearArgs& a, const void* x, int64_t ldx, void* y,
+// Segment table outputs of the single-launch decode (all null: not written).
+struct SegOut {
+    int32_t* sorted_idx;
+    int32_t* seg_indptr;
+    int32_t* req_to_lora;
+    int32_t* num_segments;
+    int32_t* tile_info;
+    int32_t* tile_rows;
+    int32_t* num_tiles;
+};
+
+// Fused decode (M <= LORA_DECODE_MAX_M).  With `ids` null the segments come
+// from the table in `a`; otherwise every workgroup groups the batch from
+// `ids` (and `enabled`, may be null) on chip and one extra workgroup writes
+// the segment table into `out` when out.sorted_idx is not null.
+hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
+                               const SegOut& out, const void* x, int64_t ldx, void* y,
                                int64_t ldy, void* ws, hipStream_t st);
 
 // S (fp32 [M][cols], sorted rows) from x; `ws` holds the partial sums.

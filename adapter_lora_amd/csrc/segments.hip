@@ -18,6 +18,7 @@
 // everything about its rows in one memory round trip.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "wave_groups.hpp"
 
 namespace mlora {
 
@@ -26,10 +27,11 @@ constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kCachedTiles = 8;
 
 __global__ __launch_bounds__(kSegThreads) void k_build_segments(
-    const int32_t* __restrict__ ids, int M, int L, int32_t* __restrict__ sorted_idx,
-    int32_t* __restrict__ seg_indptr, int32_t* __restrict__ req_to_lora,
-    int32_t* __restrict__ num_segments, int32_t* __restrict__ tile_info,
-    int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles, int max_tiles) {
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ enabled, int M, int L,
+    int32_t* __restrict__ sorted_idx, int32_t* __restrict__ seg_indptr,
+    int32_t* __restrict__ req_to_lora, int32_t* __restrict__ num_segments,
+    int32_t* __restrict__ tile_info, int32_t* __restrict__ tile_rows,
+    int32_t* __restrict__ num_tiles, int max_tiles) {
     extern __shared__ int lds[];
     const int NB = L + 1;
     int* count = lds;                    // [NB]
@@ -46,6 +48,11 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
 
     for (int i = tid; i < NB * (6 + kSegWaves); i += kSegThreads) lds[i] = 0;
     __syncthreads();
+    // bucket L collects tokens without an (enabled) adapter
+    auto bucket_of = [&](int v) {
+        const bool in = v >= 0 && v < L;
+        return (in && (!enabled || enabled[v] != 0)) ? v : L;
+    };
 
     // bucket of each of this thread's tokens; the first kCachedTiles tiles stay
     // in registers for the scatter (their loads are issued together)
@@ -54,18 +61,14 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     for (int i = 0; i < kCachedTiles; ++i) {
         const int m = i * kSegThreads + tid;
         int b = L;
-        if (m < M) {
-            const int v = ids[m];
-            b = (v >= 0 && v < L) ? v : L;
-        }
+        if (m < M) b = bucket_of(ids[m]);
         bk[i] = b;
     }
 #pragma unroll
     for (int i = 0; i < kCachedTiles; ++i)
         if (i * kSegThreads + tid < M) atomicAdd(&count[bk[i]], 1);
     for (int m = kCachedTiles * kSegThreads + tid; m < M; m += kSegThreads) {
-        const int v = ids[m];
-        atomicAdd(&count[(v >= 0 && v < L) ? v : L], 1);
+        atomicAdd(&count[bucket_of(ids[m])], 1);
     }
     __syncthreads();
 
@@ -182,99 +185,42 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     }
     for (int t0 = kCachedTiles * kSegThreads; t0 < M; t0 += kSegThreads) {
         int b = L;
-        if (t0 + tid < M) {
-            const int v = ids[t0 + tid];
-            b = (v >= 0 && v < L) ? v : L;
-        }
+        if (t0 + tid < M) b = bucket_of(ids[t0 + tid]);
         scatter_tile(t0, b);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Small batches (M <= 64, the decode case): one wavefront, no LDS and no
-// barriers.  Lane m holds the key (bucket << 6) | m, a bitonic sort across
-// the 64 lanes orders the keys (bucket first, then token: a stable order),
-// segment starts are found by comparing each key's bucket with its left
-// neighbour's, and segment numbers are popcounts of the start mask.  Every
-// segment has at most 64 rows, so it is exactly one tile of the schedule.
+// barriers (wave_groups.hpp: bitonic sort of (bucket, token) keys across the
+// 64 lanes, segment starts from neighbour comparisons, segment numbers from
+// popcounts).  Every segment has at most 64 rows, so it is exactly one tile
+// of the schedule.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kWave) void k_build_segments_wave(
-    const int32_t* __restrict__ ids, int M, int L, int32_t* __restrict__ sorted_idx,
-    int32_t* __restrict__ seg_indptr, int32_t* __restrict__ req_to_lora,
-    int32_t* __restrict__ num_segments, int32_t* __restrict__ tile_info,
-    int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles) {
-    const int lane = lane_id();
-    const bool valid = lane < M;
-    int key = 0x7fffffff;
-    if (M > 0) {
-        const int v = ids[min(lane, M - 1)];
-        const int b = (v >= 0 && v < L) ? v : L;
-        key = valid ? (b << 6) | lane : 0x7fffffff;
-    }
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const int other = __shfl_xor(key, j, kWave);
-            const bool ascending = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            key = (lower == ascending) ? min(key, other) : max(key, other);
-        }
-    }
-    const int m = key & 63;
-    const int b = key >> 6;
-    const bool has = valid && b < L;
-    const int prev = __shfl_up(b, 1, kWave);
-    const bool start = has && (lane == 0 || prev != b);
-    const unsigned long long smask = __ballot(start);
-    const int S = __popcll(smask);
-    const int mvalid = __popcll(__ballot(has));
-    const unsigned long long le = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1ull);
-    if (valid) sorted_idx[lane] = m;
-    if (start) {
-        const int s = __popcll(smask & le) - 1;
-        const unsigned long long above = smask & ~le;
-        const int n = (above ? __ffsll((long long)above) - 1 : mvalid) - lane;
-        req_to_lora[s] = b;
-        seg_indptr[s] = lane;
-        tile_info[s * 4 + 0] = s;
-        tile_info[s * 4 + 1] = b;
-        tile_info[s * 4 + 2] = lane;
-        tile_info[s * 4 + 3] = n;
-    }
-    // rows of tile s: sorted positions p0 .. p0 + n - 1, then -1
-    {
-        const unsigned long long above = smask & ~le;
-        const int n_here = (above ? __ffsll((long long)above) - 1 : mvalid) - lane;
-        unsigned long long rest = smask;
-        for (int s = 0; s < S; ++s) {
-            const int p0 = __ffsll((long long)rest) - 1;
-            rest &= rest - 1;
-            const int n = __shfl(n_here, p0, kWave);
-            const int r = __shfl(m, min(p0 + lane, kWave - 1), kWave);
-            tile_rows[s * kRowTileRows + lane] = lane < n ? r : -1;
-        }
-    }
-    for (int s = S + lane; s <= L; s += kWave) seg_indptr[s] = mvalid;
-    for (int s = S + lane; s < L; s += kWave) req_to_lora[s] = -1;
-    if (lane == 0) {
-        num_segments[0] = S;
-        num_tiles[0] = S;
-    }
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ enabled, int M, int L,
+    int32_t* __restrict__ sorted_idx, int32_t* __restrict__ seg_indptr,
+    int32_t* __restrict__ req_to_lora, int32_t* __restrict__ num_segments,
+    int32_t* __restrict__ tile_info, int32_t* __restrict__ tile_rows,
+    int32_t* __restrict__ num_tiles) {
+    const int b = M > 0 ? token_bucket(load_token(ids, enabled, M, L), enabled, L) : L;
+    const WaveGroups g = wave_group(b, M, L);
+    write_wave_segments(g, M, L, sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info,
+                        tile_rows, num_tiles);
 }
 
-hipError_t launch_build_segments(const int32_t* ids, int M, int L, int32_t* sorted_idx,
-                                 int32_t* seg_indptr, int32_t* req_to_lora,
+hipError_t launch_build_segments(const int32_t* ids, const int32_t* enabled, int M, int L,
+                                 int32_t* sorted_idx, int32_t* seg_indptr, int32_t* req_to_lora,
                                  int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
                                  int32_t* num_tiles, int max_tiles, hipStream_t st) {
     if (M <= kWave) {
-        hipLaunchKernelGGL(k_build_segments_wave, dim3(1), dim3(kWave), 0, st, ids, M, L,
+        hipLaunchKernelGGL(k_build_segments_wave, dim3(1), dim3(kWave), 0, st, ids, enabled, M, L,
                            sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info,
                            tile_rows, num_tiles);
         return hipGetLastError();
     }
     const size_t lds = (size_t)(L + 1) * (6 + kSegWaves) * sizeof(int);
-    hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kSegThreads), lds, st, ids, M, L,
+    hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kSegThreads), lds, st, ids, enabled, M, L,
                        sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
                        num_tiles, max_tiles);
     return hipGetLastError();

@@ -2,8 +2,12 @@
 
 Headline workload: decode, bf16, M=32 tokens (one per sequence), K=N=4096,
 20 adapters with ranks drawn from {16,32,64}, 10% of tokens without an
-adapter.  One step = lora_build_segments + lora_shrink_expand_add (the fused
-decode kernel) on one batch.  Inputs are synthetic and seeded (workloads.py).
+adapter.  One step = lora_fused_decode on one batch: a single kernel launch
+that groups the tokens by adapter, writes the batch's segment table and tile
+schedule, and adds every token's delta.  The same work as two launches
+(lora_build_segments, then lora_shrink_expand_add on the built table, the
+form later layers of a model use) is reported beside it.  Inputs are
+synthetic and seeded (workloads.py).
 
 Protocol:
   * R copies of every input (packed weight table, x, y, ids, segment table)
@@ -13,9 +17,9 @@ Protocol:
     ms_per_step is the event time of the K steps on the launching stream
     (launch gaps included);
   * the dominant kernel is then launched K times back to back on the same
-    rotation (segment tables already built), bracketed by one HIP event pair
-    on its stream; elapsed / K is its mean duration, and algorithmic bytes
-    per launch / that duration gives the roofline figure against 8 TB/s;
+    rotation, bracketed by one HIP event pair on its stream; elapsed / K is
+    its mean duration, and algorithmic bytes per launch / that duration gives
+    the roofline figure against 8 TB/s;
   * a plain streaming copy (bf16 negation, read + write) of the same byte
     count and of 256 MB is timed the same way as the practical ceiling and as
     the calibration kernel for the FETCH_SIZE / WRITE_SIZE counter runs;
@@ -143,7 +147,8 @@ def source_hash(files):
 
 
 DECODE_SOURCES = ["adapter_lora_amd/csrc/decode.hip", "adapter_lora_amd/csrc/common.hpp",
-                  "adapter_lora_amd/csrc/kernels.hpp", "include/mlora.h"]
+                  "adapter_lora_amd/csrc/wave_groups.hpp", "adapter_lora_amd/csrc/kernels.hpp",
+                  "include/mlora.h"]
 TRAFFIC_SUMMARY = "profiles/decode_fused_traffic.md"
 
 
@@ -170,7 +175,7 @@ def measured_traffic():
 
 
 # ----------------------------------------------------------------------------- dense
-def bench_linear(case, steps, warmup, fused_kernel_name):
+def bench_linear(case, steps, warmup, fused_kernel_name, single_launch=False):
     import torch
     import adapter_lora_amd as ml
     nbytes, flops, m_valid, touched = linear_bytes_flops(case)
@@ -189,17 +194,29 @@ def bench_linear(case, steps, warmup, fused_kernel_name):
     del A, B
     torch.cuda.synchronize()
 
-    def step(i):
+    def two_launch(i):
         table, ids, seg, x, y = copies[i % R]
         ml.lora_build_segments(ids, seg)
         ml.lora_shrink_expand_add(table, x, seg, y, ws)
 
-    def kernel(i):
+    def table_kernel(i):
         table, ids, seg, x, y = copies[i % R]
         ml.lora_shrink_expand_add(table, x, seg, y, ws)
 
+    def fused(i):
+        table, ids, seg, x, y = copies[i % R]
+        ml.lora_fused_decode(table, ids, x, y, ws, seg=seg)
+
+    step = fused if single_launch else two_launch
+    kernel = fused if single_launch else table_kernel
     ms_step, ms_wall = run_timed(step, steps, warmup)
-    ms_kernel = back_to_back(kernel, steps)     # segment tables of every copy are built
+    ms_kernel = back_to_back(kernel, steps)
+    extra = {}
+    if single_launch:
+        # context: the two-launch form, and its product kernel alone on a
+        # prebuilt table (the form every later layer of a batch runs)
+        extra["ms_per_step_two_launch"], _ = run_timed(two_launch, steps, warmup)
+        extra["ms_table_kernel_b2b"] = back_to_back(table_kernel, steps)
     # the same step captured as one HIP graph per input copy, replayed in turn
     graphs = []
     side = torch.cuda.Stream()
@@ -224,6 +241,7 @@ def bench_linear(case, steps, warmup, fused_kernel_name):
         "kernel": fused_kernel_name, "rotation_copies": R,
         "hbm_gbs": nbytes / (ms_kernel * 1e-3) / 1e9,
         "tflops": flops / (ms_kernel * 1e-3) / 1e12,
+        **extra,
     }
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     res["mfma_frac"] = res["tflops"] / BF16_MFMA_PEAK_TFLOPS
@@ -336,7 +354,7 @@ def main():
     dec_case = W.decode_bf16(0)
     if want("decode"):
         results["decode_bf16"] = bench_linear(dec_case, args.steps, args.warmup,
-                                              "k_decode_fused<uint16_t>")
+                                              "k_decode_fused<uint16_t>", single_launch=True)
     if want("prefill"):
         results["prefill_bf16"] = bench_linear(W.prefill_bf16(0), args.steps, args.warmup,
                                                "k_shrink_dense + k_reduce_partials + k_expand_dense")
@@ -371,7 +389,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_bf16: M=32 tokens, K=4096, N=4096, 20 adapters, ranks "
                                "from {16,32,64}, 10% tokens without adapter, seed 0",
-                   "step": "lora_build_segments + lora_shrink_expand_add",
+                   "step": "lora_fused_decode (one launch: segment table + delta)",
                    "cold_mall_rotation": head["rotation_copies"] if head else None},
         "roofline": None if head is None else {
             "bound": "hbm", "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -386,6 +404,11 @@ def main():
             "ms_per_step": head["ms_per_step_graph"],
             "tokens_per_s": head["m_valid"] / (head["ms_per_step_graph"] * 1e-3),
             "note": "the same step captured as one HIP graph per input copy"},
+        "two_launch": None if head is None else {
+            "ms_per_step": head["ms_per_step_two_launch"],
+            "tokens_per_s": head["m_valid"] / (head["ms_per_step_two_launch"] * 1e-3),
+            "ms_table_kernel_b2b": head["ms_table_kernel_b2b"],
+            "note": "lora_build_segments + lora_shrink_expand_add on the built table"},
         "extra": {k: v for k, v in results.items() if k != "decode_bf16"},
     }
     print(json.dumps(line), flush=True)

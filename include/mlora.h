@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLORA_ABI_VERSION 1
+#define MLORA_ABI_VERSION 2
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -187,6 +187,10 @@ int32_t lora_tile_capacity(int32_t M, int32_t L);
  * counting sort on the device) and the tile schedule.
  *   ids device [M] int32: adapter id per token; -1 (or any id outside
  *       [0, L)) means no adapter.
+ *   adapter_enabled device [L] int32, or NULL (every adapter enabled): a
+ *       token whose adapter has adapter_enabled == 0 is treated like a
+ *       token without an adapter (SGLang "LoRA + MoE" page: the per-adapter
+ *       enable mask that lets one captured graph serve any active set).
  *   outputs device: sorted_idx [M], seg_indptr [L+1], req_to_lora [L],
  *       num_segments [1], tile_info [max_tiles][4],
  *       tile_rows [max_tiles][LORA_TILE_ROWS], num_tiles [1], as described
@@ -195,10 +199,11 @@ int32_t lora_tile_capacity(int32_t M, int32_t L);
  * max_tiles >= lora_tile_capacity(M, L).  M == 0 still writes the (empty)
  * table.
  */
-lora_status lora_build_segments(const int32_t* ids, int32_t M, int32_t L, int32_t* sorted_idx,
-                                int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
-                                int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
-                                int32_t max_tiles, hipStream_t stream);
+lora_status lora_build_segments(const int32_t* ids, const int32_t* adapter_enabled, int32_t M,
+                                int32_t L, int32_t* sorted_idx, int32_t* seg_indptr,
+                                int32_t* req_to_lora, int32_t* num_segments, int32_t* tile_info,
+                                int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
+                                hipStream_t stream);
 
 /*
  * lora_shrink (Ascend walkthrough s2.2-s2.3, first product; SGLang
@@ -241,6 +246,40 @@ lora_status lora_expand_add(const lora_weights_t* w, const float* S, int32_t M,
 lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64_t ldx,
                                    int32_t M, const lora_segments_t* seg, void* y, int64_t ldy,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lora_fused_decode: the whole decode path in one kernel launch (Ascend
+ * walkthrough s2.1 "fused LoRA operator"; s2.3 grouping by id; s1.2 decode,
+ * where every token may carry a different adapter).  For
+ * 1 <= M <= LORA_DECODE_MAX_M tokens:
+ *     y[m] += (x[m] A_i^T) B_i^T      with i = ids[m], for every token whose
+ *                                     id lies in [0, L), whose slot has a
+ *                                     non-zero rank and whose adapter is
+ *                                     enabled; other rows are untouched.
+ * Every workgroup groups the batch by adapter itself (the order
+ * lora_build_segments produces), so no segment table has to exist before
+ * the call.  When sorted_idx is not NULL the launch also writes the segment
+ * table and tile schedule of the batch, bit-identical to what
+ * lora_build_segments(ids, adapter_enabled, M, L, ...) writes, so later calls
+ * on the same batch (other layers) can use lora_shrink_expand_add with it;
+ * the seven table pointers are then all required and max_tiles must be at
+ * least lora_tile_capacity(M, L).
+ *   ids device [M] int32; adapter_enabled device [L] or NULL;
+ *   x device [M, ldx]; y device [M, ldy] updated in place;
+ *   workspace as for lora_shrink_expand_add (same size, same rules: zeroed
+ *   once, left ready for the next call; calls sharing it are ordered on
+ *   one stream).
+ * M == 0 writes the empty table (when asked) and nothing else;
+ * M > LORA_DECODE_MAX_M returns LORA_UNSUPPORTED (use lora_build_segments
+ * and lora_shrink_expand_add).
+ */
+lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
+                              const int32_t* adapter_enabled, const void* x, int64_t ldx,
+                              int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                              int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
+                              int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
+                              int32_t max_tiles, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /* ---------------------------------------------------------------- MoE LoRA */
 

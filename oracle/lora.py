@@ -19,6 +19,8 @@ Sources (the pages, by title and section):
   * SGLang "LoRA Layers" page, per-layer table: stacked QKV A (3r, in),
     B (q+2kv, r); gate/up A (2r, in), B (2*out, r); output_offset of the
     B-side call; rank-0 slot returns at once.
+  * SGLang "LoRA + MoE" page, CUDA-graph section: an adapter_enabled mask
+    switches adapters off without changing the captured shapes.
 
 Readings where the pages are silent (each listed in the design doc):
   * segment order: ascending adapter id; stable inside a segment;
@@ -27,7 +29,9 @@ Readings where the pages are silent (each listed in the design doc):
     (seg_indptr tail = M_valid, req_to_lora tail = -1);
   * stacked slices: A rows [s*r, (s+1)*r) and B rows [off_s, off_{s+1})
     belong to slice s; each slice has its own S columns;
-  * rank-0 adapters behave like -1 for their tokens' outputs.
+  * rank-0 adapters behave like -1 for their tokens' outputs;
+  * a token whose adapter is disabled in the enable mask is a token without
+    an adapter (it is in no segment and its row passes through).
 """
 from __future__ import annotations
 
@@ -40,9 +44,24 @@ def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def build_segments(ids: Sequence[int], L: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int]:
+def mask_ids(ids: Sequence[int], enabled, L: int) -> np.ndarray:
+    """Apply an adapter enable mask (SGLang "LoRA + MoE" page, adapter_enabled):
+    a token whose id is a slot with enabled == 0 becomes a token without an
+    adapter (-1).  enabled=None leaves the ids as they are."""
+    ids = np.asarray(ids, dtype=np.int64).copy()
+    if enabled is None:
+        return ids
+    for m in range(ids.shape[0]):
+        v = int(ids[m])
+        if 0 <= v < L and int(enabled[v]) == 0:
+            ids[m] = -1
+    return ids
+
+
+def build_segments(ids: Sequence[int], L: int,
+                   enabled=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int]:
     """Token clustering by lora id into a segment table (Ascend walkthrough,
-    section 2.3).
+    section 2.3), after the enable mask (mask_ids).
 
     Steps:
       1. key(m) = ids[m] when 0 <= ids[m] < L, otherwise +inf (no adapter);
@@ -54,7 +73,7 @@ def build_segments(ids: Sequence[int], L: int) -> Tuple[np.ndarray, np.ndarray, 
     Returns (sorted_idx int32[M], seg_indptr int32[L+1], req_to_lora int32[L],
     num_segments).
     """
-    ids = np.asarray(ids, dtype=np.int64)
+    ids = mask_ids(ids, enabled, L)
     M = ids.shape[0]
     valid = (ids >= 0) & (ids < L)
     key = np.where(valid, ids, np.iinfo(np.int64).max)
@@ -71,14 +90,14 @@ def build_segments(ids: Sequence[int], L: int) -> Tuple[np.ndarray, np.ndarray, 
     return sorted_idx, seg_indptr, req_to_lora, S
 
 
-def tile_schedule(ids: Sequence[int], L: int, rows: int = 64):
+def tile_schedule(ids: Sequence[int], L: int, rows: int = 64, enabled=None):
     """Tile schedule over the segment table (Ascend walkthrough, section 2.4:
     which block belongs to which segment, and its rank, is worked out before
     the kernels run).  Segments in order, each cut into ceil(count / rows)
     tiles of consecutive sorted positions.
     Returns (info int32[T, 4] = (segment, adapter id, first position, rows),
     tile_rows int32[T, rows] = token index per row, -1 past the rows)."""
-    sorted_idx, seg_indptr, req_to_lora, S = build_segments(ids, L)
+    sorted_idx, seg_indptr, req_to_lora, S = build_segments(ids, L, enabled)
     info, trows = [], []
     for s in range(S):
         beg, end = int(seg_indptr[s]), int(seg_indptr[s + 1])
@@ -100,7 +119,7 @@ def slice_offsets(slice_sizes: Sequence[int]) -> List[int]:
 
 
 def lora_linear(x, ids, A: Sequence, B: Sequence, ranks: Sequence[int],
-                slice_sizes: Sequence[int], y_base) -> np.ndarray:
+                slice_sizes: Sequence[int], y_base, enabled=None) -> np.ndarray:
     """y = y_base + per-token delta (Ascend walkthrough sections 1.1, 2.2,
     3.4; stacked slices per the SGLang "LoRA Layers" table).
 
@@ -110,12 +129,14 @@ def lora_linear(x, ids, A: Sequence, B: Sequence, ranks: Sequence[int],
             S[s, j] = sum_k x[m, k] * A_i[s*r_i + j, k]          (j < r_i)
             y[m, n] = y_base[m, n] + sum_j S[s, j] * B_i[n, j]   (off_s <= n < off_{s+1})
     All arithmetic in float64.  Rows that get no delta are copied bit for bit.
+    Disabled adapters (enable mask) count as -1.
     """
     x = _f64(x)
     y = np.array(y_base, dtype=np.float64, copy=True)
     M = x.shape[0]
     off = slice_offsets(slice_sizes)
     L = len(ranks)
+    ids = mask_ids(ids, enabled, L)
     for m in range(M):
         i = int(ids[m])
         if i < 0 or i >= L or ranks[i] == 0:
@@ -179,10 +200,10 @@ def lora_expand_add(S, ids, B: Sequence, ranks: Sequence[int], slice_sizes: Sequ
     return y
 
 
-def delta_rows(ids, ranks) -> np.ndarray:
+def delta_rows(ids, ranks, enabled=None) -> np.ndarray:
     """Boolean mask of the rows that receive a delta."""
-    ids = np.asarray(ids)
     L = len(ranks)
+    ids = mask_ids(ids, enabled, L)
     ok = (ids >= 0) & (ids < L)
     out = np.zeros(ids.shape[0], dtype=bool)
     for m in np.nonzero(ok)[0]:

@@ -22,6 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
+              "lora_fused_decode",
               "lora_moe_align_run", "lora_moe_gate_up_add", "lora_moe_silu_and_mul",
               "lora_moe_down_add", "lora_moe_topk_reduce", "lora_workspace_size",
               "lora_status_string", "lora_read_device_error", "lora_table_plan",
@@ -65,12 +66,12 @@ def test_argument_checks_fail_before_any_launch():
     lib = _abi.lib
     INV = _abi.LORA_INVALID_ARG
     null = ctypes.c_void_p(0)
-    assert lib.lora_build_segments(null, -1, 4, null, null, null, null, null, null, null, 8,
-                                   null) == INV
-    assert lib.lora_build_segments(null, 4, 0, null, null, null, null, null, null, null, 8,
-                                   null) == INV
-    assert lib.lora_build_segments(null, 4, 4, null, null, null, null, null, null, null, 8,
-                                   null) == INV
+    assert lib.lora_build_segments(null, null, -1, 4, null, null, null, null, null, null, null,
+                                   8, null) == INV
+    assert lib.lora_build_segments(null, null, 4, 0, null, null, null, null, null, null, null,
+                                   8, null) == INV
+    assert lib.lora_build_segments(null, null, 4, 4, null, null, null, null, null, null, null,
+                                   8, null) == INV
     assert lib.lora_tile_capacity(130, 4) == 2 + 4 and lib.lora_tile_capacity(3, 20) == 3
     w = _abi.lora_weights_t()
     w.dtype, w.K, w.n_slices, w.L, w.r_max = 1, 100, 1, 4, 16     # K not a multiple of 8
@@ -80,6 +81,23 @@ def test_argument_checks_fail_before_any_launch():
     w.slice_offsets[0], w.slice_offsets[1] = 0, 128              # pointers still null
     assert lib.lora_expand_add(ctypes.byref(w), null, 1, None, null, 0, null) == INV
     assert lib.lora_workspace_size(ctypes.byref(w), 8) == 0      # invalid table -> 0
+    # fused decode: more tokens than one launch groups on chip, then a table
+    # request with a missing buffer (checked before the null weight pointers
+    # would matter: both need no GPU)
+    w2 = _abi.lora_weights_t()
+    w2.dtype, w2.K, w2.n_slices, w2.L, w2.r_max = 1, 128, 1, 4, 16
+    w2.slice_offsets[0], w2.slice_offsets[1] = 0, 128
+    w2.A = w2.B = ctypes.c_void_p(256)
+    w2.a_off = w2.b_off = ctypes.cast(ctypes.c_void_p(256), ctypes.POINTER(ctypes.c_int64))
+    w2.rank = ctypes.cast(ctypes.c_void_p(256), ctypes.POINTER(ctypes.c_int32))
+    args = [null] * 7
+    assert lib.lora_fused_decode(ctypes.byref(w2), null, null, null, 128, 65, null, 128, *args, 8,
+                                 null, 0, null) == _abi.LORA_UNSUPPORTED
+    some = ctypes.c_void_p(256)
+    assert lib.lora_fused_decode(ctypes.byref(w2), null, null, null, 128, 8, null, 128, some,
+                                 null, null, null, null, null, null, 8, null, 0, null) == INV
+    assert lib.lora_fused_decode(ctypes.byref(w2), null, null, null, 128, 8, null, 128, *args, 0,
+                                 null, 0, null) == INV                            # ids null
     ma = _abi.lora_moe_align_t()
     ma.max_tokens_padded, ma.block_size_m = 100, 64               # not a multiple of the block
     assert lib.lora_moe_align_run(null, null, null, 4, 2, 8, 2, ctypes.byref(ma), null) == INV

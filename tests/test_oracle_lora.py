@@ -201,3 +201,25 @@ def test_shrink_matches_segment_matmul_and_composes(mk):
     y = O.lora_expand_add(S, case.ids, B, case.ranks, case.slice_sizes, case.y_base.values)
     ref = run(case)
     assert np.allclose(y, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+def test_enable_mask_matches_merged_weights_of_enabled_adapters():
+    """With an enable mask (SGLang "LoRA + MoE" page, adapter_enabled), rows
+    of disabled adapters pass through bit for bit and every other row equals
+    the merged-weight closed form; an all-ones mask changes nothing."""
+    case = W.random_linear(21, 40, 72, [48, 24], [16, 8, 32, 5], W.F32, p_none=0.1)
+    A, B = vals(case)
+    enabled = np.array([1, 0, 1, 0], np.int32)
+    y = O.lora_linear(case.x.values, case.ids, A, B, case.ranks, case.slice_sizes,
+                      case.y_base.values, enabled)
+    off_rows = np.isin(case.ids, [1, 3])
+    assert off_rows.any()
+    assert np.array_equal(y[off_rows], case.y_base.values[off_rows])
+    ref = merged_weight_reference(case)
+    on = ~off_rows
+    assert np.max(np.abs(y[on] - ref[on])) <= 1e-12 * np.max(np.abs(ref))
+    y1 = O.lora_linear(case.x.values, case.ids, A, B, case.ranks, case.slice_sizes,
+                       case.y_base.values, np.ones(4, np.int32))
+    assert np.array_equal(y1, run(case))
+    assert np.array_equal(O.delta_rows(case.ids, case.ranks, enabled),
+                          O.delta_rows(case.ids, case.ranks) & on)

@@ -147,3 +147,36 @@ def test_moe_wrong_flattening_caught():
     P = M * topk
     remap = lambda f: (f % topk) * M + f // topk if f < P else P
     assert not np.array_equal(np.vectorize(remap)(s), s)
+
+
+# ---------------------------------------------------------------- enable mask
+def mask_by_token(ids, enabled, L):
+    """Planted slip: the mask indexed by token instead of by adapter id."""
+    ids = np.asarray(ids, np.int64).copy()
+    for m in range(ids.shape[0]):
+        if 0 <= ids[m] < L and not enabled[m % L]:
+            ids[m] = -1
+    return ids
+
+
+def mask_keep_disabled(ids, enabled, L):
+    """Planted slip: the mask inverted (disabled adapters kept)."""
+    ids = np.asarray(ids, np.int64).copy()
+    for m in range(ids.shape[0]):
+        if 0 <= ids[m] < L and enabled[ids[m]]:
+            ids[m] = -1
+    return ids
+
+
+@pytest.mark.parametrize("mut", [mask_by_token, mask_keep_disabled])
+def test_mask_mutant_caught(mut, monkeypatch):
+    """The brute-force grouping pin rejects each mask mutant."""
+    import itertools
+    monkeypatch.setattr(O, "mask_ids", mut)
+    caught = False
+    for mask in itertools.product([0, 1], repeat=3):
+        for ids in itertools.product([-1, 0, 1, 2], repeat=3):
+            got = O.build_segments(np.array(ids, np.int32), 3, np.array(mask, np.int32))
+            if got[0].tolist() != grouping_definition(list(ids), 3, mask)[0]:
+                caught = True
+    assert caught

@@ -12,13 +12,14 @@ import pytest
 from oracle import lora as O
 
 
-def grouping_definition(ids, L):
-    """Independent definition: collect token lists per valid id in a dict,
-    concatenate them by ascending id, then the tokens with no adapter."""
+def grouping_definition(ids, L, enabled=None):
+    """Independent definition: collect token lists per valid (and enabled)
+    id in a dict, concatenate them by ascending id, then the tokens with no
+    adapter."""
     groups = {}
     rest = []
     for m, v in enumerate(ids):
-        if 0 <= v < L:
+        if 0 <= v < L and (enabled is None or enabled[v]):
             groups.setdefault(v, []).append(m)
         else:
             rest.append(m)
@@ -55,6 +56,36 @@ def test_brute_force_all_maps(M, L):
         assert seg.tolist() == e_seg, ids
         assert req.tolist() == e_req, ids
         assert n == e_n
+
+
+@pytest.mark.parametrize("L", [1, 2, 3])
+@pytest.mark.parametrize("M", [0, 1, 2, 3])
+def test_brute_force_enable_masks(M, L):
+    """Every id map and every enable mask: a disabled adapter's tokens join
+    the tokens without an adapter (SGLang "LoRA + MoE" page, adapter_enabled)."""
+    values = list(range(-1, L)) + [L]
+    for mask in itertools.product([0, 1], repeat=L):
+        for ids in itertools.product(values, repeat=M):
+            ids = list(ids)
+            got = O.build_segments(np.array(ids, np.int32), L, np.array(mask, np.int32))
+            exp = grouping_definition(ids, L, mask)
+            assert got[0].tolist() == exp[0], (ids, mask)
+            assert got[1].tolist() == exp[1], (ids, mask)
+            assert got[2].tolist() == exp[2], (ids, mask)
+            assert got[3] == exp[3]
+
+
+def test_enable_mask_hand_case():
+    """ids [0, 2, -1, 1, 2], adapter 1 disabled: segments are adapter 0
+    (token 0) and adapter 2 (tokens 1, 4); tokens 2 and 3 come last."""
+    si, seg, req, n = O.build_segments([0, 2, -1, 1, 2], 3, [1, 0, 1])
+    assert si.tolist() == [0, 1, 4, 2, 3]
+    assert seg.tolist() == [0, 1, 3, 3]
+    assert req.tolist() == [0, 2, -1]
+    assert n == 2
+    info, rows = O.tile_schedule([0, 2, -1, 1, 2], 3, rows=2, enabled=[1, 0, 1])
+    assert info.tolist() == [[0, 0, 0, 1], [1, 2, 1, 2]]
+    assert rows.tolist() == [[0, -1], [1, 4]]
 
 
 @pytest.mark.parametrize("seed", range(6))
