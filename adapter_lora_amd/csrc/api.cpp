@@ -87,26 +87,29 @@ LinearArgs make_args(const lora_weights_t* w, const lora_segments_t* seg, int M)
 }
 
 LinearWs layout_for(const lora_weights_t* w, int M) {
-    return linear_ws_layout(M, w->K, w->n_slices * w->r_max, w->L, w->n_slices);
+    int tiles = 0;
+    for (int s = 0; s < w->n_slices; ++s)
+        tiles += (int)((w->slice_offsets[s + 1] - w->slice_offsets[s] + kNTile - 1) / kNTile);
+    return linear_ws_layout(M, w->K, w->n_slices * w->r_max, w->r_max, tiles);
 }
 
 }  // namespace
 
 namespace mlora {
 
-// header | decode counters [L][n_sl] | decode slots [C][64][cols] |
-// shrink partials [C][M][cols] | S [M][cols].  The decode region does not
-// depend on M, so calls of any M may share one workspace.
-LinearWs linear_ws_layout(int M, int K, int cols, int L, int n_sl) {
+// header | decode slots [Cd][n_tiles][64][r_max] | shrink partials
+// [C][M][cols] | S [M][cols], with Cd = ceil(K / kDecKChunk) and
+// C = ceil(K / kKChunk).  The decode region does not depend on M, so calls
+// of any M may share one workspace.
+LinearWs linear_ws_layout(int M, int K, int cols, int r_max, int n_tiles) {
     LinearWs ws{};
     const size_t C = (size_t)kchunks(K);
+    const size_t Cd = (size_t)((K + kDecKChunk - 1) / kDecKChunk);
     size_t off = 0;
     ws.header = off;
     off += up(sizeof(WsHeader));
-    ws.counters = off;
-    off += up((size_t)L * n_sl * sizeof(int));
     ws.slots = off;
-    off += up(C * LORA_DECODE_MAX_M * cols * sizeof(slot_t));
+    off += up(Cd * n_tiles * LORA_DECODE_MAX_M * r_max * sizeof(slot_t));
     ws.partial = off;
     off += up(C * (size_t)M * cols * sizeof(float));
     ws.S = off;

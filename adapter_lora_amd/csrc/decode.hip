@@ -38,8 +38,7 @@ struct DecodeParams {
     void* y;
     int64_t ldy;
     int* err;
-    int* counters;     // [s_max][n_sl]
-    slot_t* slots;     // [C][M][cols]
+    slot_t* slots;     // [C][n_tiles][64][r_max]: one copy per consumer tile
     int C;
     int jb_max;        // n_sl * r_max / 16
     int grid1;
@@ -63,6 +62,12 @@ struct SegView {
     int nseg, id, rp, p0, ms, my_idx;
     int64_t off;
 };
+
+// Exchange slot of K chunk c, consumer tile t (its own copy), sorted
+// position pos and slice-local S column j.
+__device__ __forceinline__ slot_t* slot_at(const DecodeParams& p, int c, int t, int pos, int j) {
+    return p.slots + (((int64_t)c * p.n_tiles + t) * LORA_DECODE_MAX_M + pos) * p.a.r_max + j;
+}
 
 __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a_side) {
     const LinearArgs& a = p.a;
@@ -88,9 +93,14 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a
     if (small) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int j = min(q * kWave + lane, a.L - 1);
-            rk[q] = a.rank[j];
-            of[q] = offs[j];
+            if (q * kWave < a.L) {          // one load per 64 slots and lane
+                const int j = min(q * kWave + lane, a.L - 1);
+                rk[q] = a.rank[j];
+                of[q] = offs[j];
+            } else {
+                rk[q] = 0;
+                of[q] = 0;
+            }
         }
     }
     if (p.ids) {
@@ -103,11 +113,14 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, int s, bool a
     }
     const int id = v.id < 0 ? 0 : v.id;
     if (small) {
+        // id is the same in every lane: the entry is read with readlane
         const int q = id / kWave, src = id % kWave;
         const int r_sel = q == 0 ? rk[0] : q == 1 ? rk[1] : q == 2 ? rk[2] : rk[3];
         const int64_t o_sel = q == 0 ? of[0] : q == 1 ? of[1] : q == 2 ? of[2] : of[3];
-        v.rp = __shfl(r_sel, src, kWave);
-        v.off = __shfl(o_sel, src, kWave);
+        v.rp = __builtin_amdgcn_readlane(r_sel, src);
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o_sel, src);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)o_sel >> 32), src);
+        v.off = (int64_t)(((uint64_t)hi << 32) | lo);
     } else {
         v.rp = a.rank[id];
         v.off = offs[id];
@@ -212,7 +225,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
         }
     }
     const T* X = reinterpret_cast<const T*>(p.x);
-    slot_t* out = p.slots + ((int64_t)c * a.M + v.p0) * a.cols + sl * a.r_max + jj * 16 + wave * 4;
+    const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += kTokGroup) {
         float acc[kTokGroup][4];
 #pragma unroll
@@ -244,7 +257,9 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, int unit) {
             const float r0 = wave_total(acc[u][0]), r1 = wave_total(acc[u][1]);
             const float r2 = wave_total(acc[u][2]), r3 = wave_total(acc[u][3]);
             const float tot = lane == 0 ? r0 : lane == 1 ? r1 : lane == 2 ? r2 : r3;
-            if (lane < 4) slot_put(out + (int64_t)(t0 + u) * a.cols + lane, tot);
+            if (lane < 4)
+                for (int t = t_beg; t < t_end; ++t)
+                    slot_put(slot_at(p, c, t, v.p0 + t0 + u, jj * 16 + wave * 4 + lane), tot);
         }
     }
 }
@@ -276,7 +291,7 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, int unit
     uint4 av[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < a.K, A);
-    slot_t* out = p.slots + ((int64_t)c * a.M + v.p0) * a.cols + sl * a.r_max + jj * 16;
+    const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += 16) {
         const int nt = min(16, v.ms - t0);
         const int m = __shfl(v.my_idx, v.p0 + t0 + min(lr, nt - 1), kWave);
@@ -296,7 +311,9 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, int unit
             if (tok < nt) {
                 const float sum = (red[(0 * 16 + tok) * 16 + row] + red[(1 * 16 + tok) * 16 + row]) +
                                   (red[(2 * 16 + tok) * 16 + row] + red[(3 * 16 + tok) * 16 + row]);
-                slot_put(out + (int64_t)(t0 + tok) * a.cols + row, sum);
+                // one copy for every consumer tile of the slice
+                for (int t = t_beg; t < t_end; ++t)
+                    slot_put(slot_at(p, c, t, v.p0 + t0 + tok, jj * 16 + row), sum);
             }
         }
         __syncthreads();     // red is rewritten by the next token group
@@ -307,8 +324,8 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, int unit
 constexpr int kPollBatch = 8;    // exchange slots polled together
 
 template <typename T, int RCAP>
-__device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView& v, int s, int sl,
-                                            int n0, int n1, uint4* lds, int* sFlag) {
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView& v, int tile,
+                                            int n0, int n1, uint4* lds) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
     constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
@@ -339,10 +356,10 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
     float* sS = reinterpret_cast<float*>(lds);
     bool ok = true;
-    const int64_t cstride = (int64_t)a.M * a.cols;
+    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * a.r_max;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
-        const slot_t* sp = p.slots + (int64_t)(v.p0 + t) * a.cols + sl * a.r_max + j;
+        slot_t* sp = slot_at(p, 0, tile, v.p0 + t, j);
         float acc = 0.f;
         for (int c0 = 0; c0 < p.C; c0 += kPollBatch) {
             slot_t w[kPollBatch];
@@ -370,6 +387,10 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
             for (int q = 0; q < kPollBatch; ++q)
                 if (c0 + q < p.C && (uint32_t)(w[q] >> 32) == 1u)
                     acc += __uint_as_float((uint32_t)w[q]);
+            // this workgroup is the copy's only reader: empty it for the next call
+#pragma unroll
+            for (int q = 0; q < kPollBatch; ++q)
+                if (c0 + q < p.C) slot_clear(sp + (c0 + q) * cstride);
         }
         if constexpr (sizeof(T) == 2) {
             const uint32_t h = f32_to_bf16(acc);
@@ -428,30 +449,11 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
         const float r = old + delta(t);
         if (nin) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, r);
     }
-    // 4. the last consumer of (segment, slice) empties the slots it shared
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int tiles = p.tile_start[sl + 1] - p.tile_start[sl];
-        int* cnt = p.counters + s * a.n_sl + sl;
-        const int old = atomic_add_agent(cnt, 1);
-        *sFlag = (old == tiles - 1);
-        if (*sFlag) atomic_store_agent(cnt, 0);
-    }
-    __syncthreads();
-    if (*sFlag) {
-        for (int e = threadIdx.x; e < v.ms * rp * p.C; e += kDecThreads) {
-            const int c = e / (v.ms * rp);
-            const int r = e % (v.ms * rp);
-            const int t = r / rp, j = r % rp;
-            slot_clear(p.slots + ((int64_t)c * a.M + v.p0 + t) * a.cols + sl * a.r_max + j);
-        }
-    }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
     __shared__ uint4 lds[LORA_DECODE_MAX_M * LORA_MAX_RANK * 4 / 16];   // the segment's S
-    __shared__ int sFlag;
     if (p.writer && blockIdx.x == gridDim.x - 1) {
         // ids mode: the segment table for later calls on the same batch
         if (threadIdx.x < kWave) {
@@ -482,11 +484,11 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeParams p) {
     const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
     const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
     if (v.rp <= 16)
-        dec_consume<T, 16>(p, v, s, sl, n0, n1, lds, &sFlag);
+        dec_consume<T, 16>(p, v, t, n0, n1, lds);
     else if (v.rp <= 32)
-        dec_consume<T, 32>(p, v, s, sl, n0, n1, lds, &sFlag);
+        dec_consume<T, 32>(p, v, t, n0, n1, lds);
     else
-        dec_consume<T, 64>(p, v, s, sl, n0, n1, lds, &sFlag);
+        dec_consume<T, 64>(p, v, t, n0, n1, lds);
 }
 
 hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
@@ -502,13 +504,13 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     p.ldx = ldx;
     p.y = y;
     p.ldy = ldy;
-    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.L, a.n_sl);
+    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.r_max, ntiles_total(a));
     char* base = reinterpret_cast<char*>(ws);
     p.err = reinterpret_cast<int*>(base + L.header);
-    p.counters = reinterpret_cast<int*>(base + L.counters);
     p.slots = reinterpret_cast<slot_t*>(base + L.slots);
-    const int kc = 512 * (a.dtype == LORA_BF16 ? dec_steps<uint16_t>() : dec_steps<float>());
-    p.C = (a.K + kc - 1) / kc;
+    static_assert(512 * dec_steps<uint16_t>() == kDecKChunk && 512 * dec_steps<float>() == kDecKChunk,
+                  "producer K chunk");
+    p.C = (a.K + kDecKChunk - 1) / kDecKChunk;
     p.jb_max = a.cols / 16;
     p.grid1 = a.s_max * p.jb_max * p.C;
     int t = 0;

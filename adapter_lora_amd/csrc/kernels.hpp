@@ -52,17 +52,20 @@ inline int ntiles_total(const LinearArgs& a) {
     return t;
 }
 
+// K columns handled by one fused-decode producer unit.
+constexpr int kDecKChunk = 1024;
+
 // Workspace layout (bytes from the start), see api.cpp.
 struct LinearWs {
     size_t header;      // WsHeader
-    size_t counters;    // int[s_max * n_sl] (decode consumer counters)
-    size_t slots;       // slot_t[C][M][cols] (decode exchange)
+    size_t slots;       // slot_t[Cd][n_tiles][64][r_max] (decode exchange, one copy per consumer tile)
     size_t partial;     // float[C][M][cols]   (MFMA shrink partial sums)
     size_t S;           // float[M][cols]      (S between shrink and expand)
     size_t total;
 };
 
-LinearWs linear_ws_layout(int M, int K, int cols, int L, int n_sl);
+// n_tiles: 256-column output tiles over all slices (ntiles_total)
+LinearWs linear_ws_layout(int M, int K, int cols, int r_max, int n_tiles);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -1,13 +1,18 @@
 // Grouping of a small batch (M <= 64 tokens) by adapter id inside one
 // wavefront ("vLLM-Ascend dynamic LoRA operator" walkthrough, section 2.3:
-// equal ids made contiguous, one segment per id).  Lane m starts with the
-// key (bucket << 6) | m, where bucket is the token's adapter id or L for
-// "no adapter"; a bitonic sort across the 64 lanes orders the keys by bucket
-// and, inside a bucket, by token (a stable order).  Segment starts are the
-// sorted positions whose bucket differs from the left neighbour's, and
-// segment numbers are popcounts of the start mask, so any segment's bounds
-// are found with one ballot.  No LDS and no barriers: every wavefront that
-// needs the grouping computes it itself.
+// equal ids made contiguous, one segment per id).  Token m (lane m) has a
+// bucket: its adapter id, or L for "no adapter".  The sorted order is by
+// bucket and, inside a bucket, by token (a stable order); token m's sorted
+// position is the number of tokens with a smaller bucket plus the number of
+// earlier tokens with the same bucket.  Both counts come from ballots, one
+// per bit of the bucket from the highest down: after the bits above bit i,
+// each lane knows which lanes still agree with it (`eq`) and which were
+// already found smaller (`less`).  A single forward lane permute then puts
+// every token at its sorted position.  Segment starts are the sorted
+// positions whose bucket differs from the left neighbour's, and segment
+// numbers are popcounts of the start mask, so any segment's bounds are found
+// with one ballot.  No LDS and no barriers: every wavefront that needs the
+// grouping computes it itself.
 #pragma once
 
 #include "common.hpp"
@@ -21,23 +26,30 @@ struct WaveGroups {
     int mvalid;                // tokens with an adapter
 };
 
+// mask of bits 0..p (p in 0..63)
+__device__ __forceinline__ unsigned long long bits_upto(int p) {
+    return p >= kWave - 1 ? ~0ull : ((2ull << p) - 1ull);
+}
+
 // `bucket` is lane m's bucket (0..L-1, or L for none); lanes >= M are ignored.
 __device__ __forceinline__ WaveGroups wave_group(int bucket, int M, int L) {
     const int lane = lane_id();
     const bool valid = lane < M;
-    int key = valid ? (bucket << 6) | lane : 0x7fffffff;
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const int other = __shfl_xor(key, j, kWave);
-            const bool ascending = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            key = (lower == ascending) ? min(key, other) : max(key, other);
-        }
+    const unsigned long long vmask = __ballot(valid);
+    unsigned long long less = 0ull, eq = vmask;
+    const int nbits = 32 - __clz(L);          // bits of the buckets 0..L
+    for (int i = nbits - 1; i >= 0; --i) {
+        const bool bit = (bucket >> i) & 1;
+        const unsigned long long B = __ballot(valid && bit);
+        less |= bit ? (eq & ~B) : 0ull;
+        eq &= bit ? B : ~B;
     }
+    // lanes >= M keep their own position: the valid tokens fill 0 .. M-1
+    const int pos = valid ? __popcll(less) + __popcll(eq & ((1ull << lane) - 1ull)) : lane;
+    const int mine = valid ? (bucket << 6) | lane : 0x7fffffff;
+    const int key = __builtin_amdgcn_ds_permute(pos * 4, mine);
     const int b = key >> 6;
-    const bool has = valid && b < L;
+    const bool has = lane < M && b < L;
     const int prev = __shfl_up(b, 1, kWave);
     const bool start = has && (lane == 0 || prev != b);
     WaveGroups g;
@@ -46,11 +58,6 @@ __device__ __forceinline__ WaveGroups wave_group(int bucket, int M, int L) {
     g.nseg = __popcll(g.smask);
     g.mvalid = __popcll(__ballot(has));
     return g;
-}
-
-// mask of bits 0..p (p in 0..63)
-__device__ __forceinline__ unsigned long long bits_upto(int p) {
-    return p >= kWave - 1 ? ~0ull : ((2ull << p) - 1ull);
 }
 
 // Segment s of a grouping: first sorted position, token count and adapter
@@ -71,14 +78,14 @@ __device__ __forceinline__ void wave_segment(const WaveGroups& g, int s, int* p0
     const int p1 = above ? __ffsll((long long)above) - 1 : g.mvalid;
     *p0 = p;
     *n = p1 - p;
-    *id = __shfl(g.key, p, kWave) >> 6;
+    *id = __builtin_amdgcn_readlane(g.key, p) >> 6;
 }
 
 // Bucket of token `lane` (lanes >= M read token M - 1 and are ignored):
 // its id when that lies in [0, L) and the adapter is enabled, else L.
 // `enabled` may be null (every adapter enabled).  Split in two so that a
 // caller can issue other loads between them: load_token() issues the id
-// load and, for L <= 256, four independent mask loads per lane;
+// load and, for L <= 256, one mask load per 64 slots and lane;
 // token_bucket() picks the token's mask entry by lane shuffle (a dependent
 // load only for larger tables).  M >= 1.
 struct TokenLoad {
@@ -95,7 +102,8 @@ __device__ __forceinline__ TokenLoad load_token(const int32_t* __restrict__ ids,
     for (int q = 0; q < 4; ++q) t.e[q] = 1;
     if (enabled && L <= 4 * kWave) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) t.e[q] = enabled[min(q * kWave + lane, L - 1)];
+        for (int q = 0; q < 4; ++q)
+            if (q * kWave < L) t.e[q] = enabled[min(q * kWave + lane, L - 1)];
     }
     return t;
 }
@@ -108,9 +116,13 @@ __device__ __forceinline__ int token_bucket(const TokenLoad& t, const int32_t* _
     if (L <= 4 * kWave) {
         const int vv = in ? t.v : 0;
         const int src = vv % kWave, q = vv / kWave;
-        const int e0 = __shfl(t.e[0], src, kWave), e1 = __shfl(t.e[1], src, kWave);
-        const int e2 = __shfl(t.e[2], src, kWave), e3 = __shfl(t.e[3], src, kWave);
-        on = q == 0 ? e0 : q == 1 ? e1 : q == 2 ? e2 : e3;
+        on = __shfl(t.e[0], src, kWave);
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+            if (k * kWave < L) {
+                const int ek = __shfl(t.e[k], src, kWave);
+                on = q == k ? ek : on;
+            }
     } else {
         on = in ? enabled[t.v] : 0;
     }
