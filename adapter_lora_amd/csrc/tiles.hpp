@@ -76,6 +76,29 @@ constexpr int kShrinkLds = kGroupCols * kShrinkK * 2;   // bytes: the A chunk
 
 __device__ __forceinline__ int swz(int r, int q) { return r * (kShrinkK / 8) + (q ^ (r & 15)); }
 
+// The MFMA steps of one shrink unit over the first NB column blocks.  There
+// is no branch in the loop and each step's LDS operand reads are issued one
+// step ahead of its MFMAs, so operand reads and matrix work overlap (a branch
+// per block inside the loop makes every MFMA wait out its own LDS read).
+template <int NB>
+__device__ __forceinline__ void shrink_mfma_steps(const uint4* __restrict__ sA, const uint4* xv,
+                                                  f32x4_t* acc, int lr, int lq) {
+    constexpr int KS = kShrinkK / 32;
+    uint4 b[2][NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) b[0][cb] = sA[swz(cb * 16 + lr, lq)];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) {
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                b[(kk + 1) & 1][cb] = sA[swz(cb * 16 + lr, (kk + 1) * 4 + lq)];
+        }
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) acc[cb] = mfma_bf16(xv[kk], b[kk & 1][cb], acc[cb]);
+    }
+}
+
 __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
                                                   const uint16_t* __restrict__ x, int64_t ldx,
                                                   const uint16_t* __restrict__ A, int K, int n_sl,
@@ -130,15 +153,20 @@ __device__ __forceinline__ void shrink_group_bf16(const RowSet& rs, int r0,
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (any && rg * 16 < rows) {
+        // active blocks are a prefix for one slice (rank blocks 0 .. rp/16-1);
+        // other patterns run all four and drop the blocks without A rows
+        const int mask = (act[0] ? 1 : 0) | (act[1] ? 2 : 0) | (act[2] ? 4 : 0) | (act[3] ? 8 : 0);
+        if (mask == 1) {
+            shrink_mfma_steps<1>(sA, xv, acc, lr, lq);
+        } else if (mask == 3) {
+            shrink_mfma_steps<2>(sA, xv, acc, lr, lq);
+        } else if (mask == 7) {
+            shrink_mfma_steps<3>(sA, xv, acc, lr, lq);
+        } else {
+            shrink_mfma_steps<4>(sA, xv, acc, lr, lq);
 #pragma unroll
-        for (int kk = 0; kk < kShrinkK / 32; ++kk) {
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                if (act[cb]) {
-                    const uint4 b = sA[swz(cb * 16 + lr, kk * 4 + lq)];
-                    acc[cb] = mfma_bf16(xv[kk], b, acc[cb]);
-                }
-            }
+            for (int cb = 0; cb < 4; ++cb)
+                if (!act[cb]) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
 #pragma unroll
