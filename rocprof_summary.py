@@ -2,9 +2,10 @@
 
   python rocprof_summary.py stats DIR "COMMAND" > profiles/<kernel>_<workload>.md
       per-kernel duration table from DIR's *_kernel_stats.csv
-  python rocprof_summary.py traffic FETCH_DIR WRITE_DIR "FETCH_CMD" "WRITE_CMD" \\
+  python rocprof_summary.py traffic FETCH_DIR WRITE_DIR "FETCH_CMD" "WRITE_CMD" [WORKGROUPS] \\
       > profiles/decode_fused_traffic.md
-      HBM bytes per launch of the fused decode kernel from two counter runs
+      HBM bytes per launch of the fused decode kernel (only the dispatches with
+      WORKGROUPS workgroups when given: the single-launch form) from two counter runs
       (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what
       the same counter reads for the 256 MB streaming copy that bench.py runs
       (the torch bf16 negation: half of its bytes read, half written).
@@ -57,9 +58,11 @@ def stats(directory, command):
               f"{float(r['Percentage']):.1f} |")
 
 
-def _per_dispatch_kib(rows, counter, match):
+def _per_dispatch_kib(rows, counter, match, workgroups=None):
     vals = {}
     for r in rows:
+        if workgroups is not None and int(r["Grid_Size"]) != workgroups * int(r["Workgroup_Size"]):
+            continue
         if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
             vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     if not vals:
@@ -68,12 +71,13 @@ def _per_dispatch_kib(rows, counter, match):
     return sum(v) / len(v), len(v), v[len(v) // 2]
 
 
-def traffic(fetch_dir, write_dir, fetch_cmd, write_cmd):
+def traffic(fetch_dir, write_dir, fetch_cmd, write_cmd, workgroups=None):
     import bench
+    wg = None if workgroups is None else int(workgroups)
     fr = _rows(fetch_dir, "counter_collection.csv")
     wr = _rows(write_dir, "counter_collection.csv")
-    kf, nkf, kf_med = _per_dispatch_kib(fr, "FETCH_SIZE", DECODE_KERNEL)
-    kw, nkw, kw_med = _per_dispatch_kib(wr, "WRITE_SIZE", DECODE_KERNEL)
+    kf, nkf, kf_med = _per_dispatch_kib(fr, "FETCH_SIZE", DECODE_KERNEL, wg)
+    kw, nkw, kw_med = _per_dispatch_kib(wr, "WRITE_SIZE", DECODE_KERNEL, wg)
     # the calibration copies of bench.copy_ceiling have two sizes; take the 256 MB ones
     half = CALIB_BYTES / 2
     cal = [v for v in _all(fr, "FETCH_SIZE", CALIB_KERNEL) if v * 1024 > 0.5 * half]
@@ -88,7 +92,8 @@ def traffic(fetch_dir, write_dir, fetch_cmd, write_cmd):
     print("the same run (128 MB read, 128 MB written).\n")
     print(f"FETCH_SIZE run:\n\n```\n{fetch_cmd}\n```\n")
     print(f"WRITE_SIZE run:\n\n```\n{write_cmd}\n```\n")
-    print(f"- kernel: `{DECODE_KERNEL}<uint16_t>`")
+    print(f"- kernel: `{DECODE_KERNEL}<uint16_t>`" +
+          ("" if wg is None else f", dispatches of {wg} workgroups"))
     print(f"- dispatches: `{nkf}` (fetch run), `{nkw}` (write run)")
     print(f"- fetch_kib_per_dispatch_raw: `{kf:.1f}` (median {kf_med:.1f})")
     print(f"- write_kib_per_dispatch_raw: `{kw:.1f}` (median {kw_med:.1f})")
@@ -111,6 +116,6 @@ if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "traffic":
-        traffic(*sys.argv[2:6])
+        traffic(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
