@@ -209,3 +209,30 @@ def delta_rows(ids, ranks, enabled=None) -> np.ndarray:
     for m in np.nonzero(ok)[0]:
         out[m] = ranks[int(ids[m])] > 0
     return out
+
+
+def embedding_add(tokens, ids, A: Sequence, B: Sequence, ranks: Sequence[int], vocab: int,
+                  y_base, enabled=None) -> np.ndarray:
+    """Embedding LoRA (SGLang "LoRA Layers" page, VocabParallelEmbeddingWithLoRA:
+    the A side is an embedding lookup of A_i [r, vocab], the B side the usual
+    product with B_i [emb, r] added to the base output).
+
+    For each token m with adapter i = ids[m] (skipped when i is -1, out of
+    range, disabled or rank[i] == 0) and token id t = tokens[m]:
+        S[j] = A_i[j, t]                               (j < r_i)
+        y[m, n] = y_base[m, n] + sum_j S[j] * B_i[n, j]
+    A token id outside [0, vocab) gets no delta (the page masks such added
+    tokens for the base lookup; LoRA for them is not supported there).
+    float64; rows without a delta are copied bit for bit."""
+    y = np.array(y_base, dtype=np.float64, copy=True)
+    L = len(ranks)
+    ids = mask_ids(ids, enabled, L)
+    for m in range(y.shape[0]):
+        i = int(ids[m])
+        t = int(tokens[m])
+        if i < 0 or i >= L or ranks[i] == 0 or t < 0 or t >= vocab:
+            continue
+        r = int(ranks[i])
+        S = _f64(A[i])[:r, t]                  # the lookup: column t of A_i
+        y[m] = y[m] + _f64(B[i])[:, :r] @ S
+    return y

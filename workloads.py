@@ -252,6 +252,71 @@ def integer_linear(seed: int, M: int, K: int, slice_sizes, ranks, dtype: str) ->
 # ----------------------------------------------------------------------------
 # MoE LoRA case
 # ----------------------------------------------------------------------------
+# ----------------------------------------------------------------------------
+# embedding and LM-head LoRA (SGLang "LoRA Layers" page: the embedding's A
+# side is a lookup of A (r, vocab), its B is (emb, r); the LM head is a dense
+# LoRA linear whose output width is the vocabulary)
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class EmbeddingCase:
+    name: str
+    dtype: str
+    M: int
+    vocab: int
+    emb: int
+    ranks: List[int]
+    ids: np.ndarray                 # int32 [M] adapter per token; -1 = none
+    tokens: np.ndarray              # int32 [M] token ids (may lie outside [0, vocab))
+    A: List[Tensor]                 # per adapter: [r_i, vocab]
+    B: List[Tensor]                 # per adapter: [emb, r_i]
+    y_base: Tensor                  # [M, emb]: the base embedding rows
+
+    @property
+    def L(self) -> int:
+        return len(self.ranks)
+
+
+def embedding_bf16(seed: int = 0, M: int = 32, vocab: int = 32000, emb: int = 4096,
+                   L: int = 20, p_none: float = 0.1, ranks=None, dtype: str = BF16,
+                   contiguous: bool = False, p_outside: float = 0.0) -> EmbeddingCase:
+    """Embedding LoRA on a decode batch (ids as in the decode workload: ranks
+    from {16,32,64}, 10% of tokens without an adapter) or, with contiguous,
+    on a prefill batch of Dirichlet(1) segments.  Token ids are uniform over
+    the vocabulary; a fraction p_outside of them is moved past its end.
+    A, B ~ N(0, 0.02^2), y_base ~ N(0,1)."""
+    rng = np.random.default_rng([seed, 7])
+    if ranks is None:
+        ranks = [int(v) for v in rng.choice([16, 32, 64], size=L)]
+    ranks = [int(r) for r in ranks]
+    L = len(ranks)
+    if contiguous:
+        lengths = dirichlet_lengths(rng, M, L)
+        order = rng.permutation(L)
+        ids = np.concatenate([np.full(lengths[a], a, dtype=np.int32) for a in order])
+    else:
+        ids = rng.integers(0, L, size=M).astype(np.int32)
+        ids[rng.random(M) < p_none] = -1
+    tokens = rng.integers(0, vocab, size=M).astype(np.int32)
+    outside = rng.random(M) < p_outside
+    tokens[outside] = vocab + rng.integers(0, 100, size=int(outside.sum())).astype(np.int32)
+    A, B = [], []
+    for r in ranks:
+        A.append(make_tensor(rng.standard_normal((r, vocab), dtype=np.float32) * 0.02, dtype))
+        B.append(make_tensor(rng.standard_normal((emb, r), dtype=np.float32) * 0.02, dtype))
+    y = make_tensor(rng.standard_normal((M, emb), dtype=np.float32), dtype)
+    return EmbeddingCase(f"embedding_{dtype}", dtype, M, vocab, emb, ranks, ids.astype(np.int32),
+                         tokens, A, B, y)
+
+
+def lm_head_bf16(seed: int = 0, M: int = 32, K: int = 4096, vocab: int = 32000,
+                 L: int = 20, dtype: str = BF16) -> LinearCase:
+    """LM-head LoRA on a decode batch: the decode workload with the output
+    width set to the vocabulary (hidden 4096 -> 32000 logits)."""
+    case = decode_bf16(seed, M=M, K=K, N=vocab, L=L, dtype=dtype)
+    case.name = f"lm_head_{dtype}"
+    return case
+
+
 @dataclasses.dataclass
 class MoECase:
     name: str
