@@ -22,6 +22,7 @@ __all__ = [
     "MoeWeights", "MoeAlign",
     "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",
     "lora_shrink_expand_add", "lora_fused_decode",
+    "lora_pack_embedding_adapter", "lora_embedding_shrink",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
     "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
@@ -77,16 +78,26 @@ def lora_pack_adapter(A_src: torch.Tensor, B_src: torch.Tensor, K: int, N_total:
                                 stream_handle(stream)), "lora_pack_adapter")
 
 
+def lora_pack_embedding_adapter(A_src: torch.Tensor, B_src: torch.Tensor, vocab: int, emb: int,
+                                rank: int, rank_pad: int, A_dst: torch.Tensor,
+                                B_dst: torch.Tensor, stream=None) -> None:
+    check(lib.lora_pack_embedding_adapter(_dtype_code(A_src.dtype), vocab, emb, rank, rank_pad,
+                                          _ptr(A_src), _ptr(B_src), _ptr(A_dst), _ptr(B_dst),
+                                          stream_handle(stream)), "lora_pack_embedding_adapter")
+
+
 class LoraTable:
     """Rank-grouped packed adapter table on the device (load time).
 
     A[i]: [n_slices * r_i, K] (slice s = rows [s*r_i, (s+1)*r_i)),
     B[i]: [N_total, r_i]; rank 0 (or None) marks an empty slot.
+    embedding=True: an embedding table (K = vocab, one slice of width emb),
+    A[i] [r_i, vocab] packed transposed for the lookup.
     """
 
     def __init__(self, A: Sequence[Optional[torch.Tensor]], B: Sequence[Optional[torch.Tensor]],
                  ranks: Sequence[int], slice_sizes: Sequence[int], K: int,
-                 dtype: torch.dtype, device="cuda", stream=None):
+                 dtype: torch.dtype, device="cuda", stream=None, embedding: bool = False):
         self.L = len(ranks)
         if not (1 <= self.L <= LORA_MAX_ADAPTERS):
             raise LoraError("adapter count out of range")
@@ -110,8 +121,14 @@ class LoraTable:
             b = B[i].to(device=device, dtype=dtype).contiguous()
             if tuple(a.shape) != (self.n_slices * r, self.K) or tuple(b.shape) != (self.N, r):
                 raise LoraError(f"adapter {i}: bad A/B shape {tuple(a.shape)} {tuple(b.shape)}")
-            lora_pack_adapter(a, b, self.K, self.N, self.n_slices, r, rp[i],
-                              self.A_table[ao[i]:], self.B_table[bo[i]:], stream)
+            if embedding:
+                if self.n_slices != 1:
+                    raise LoraError("an embedding table has one output slice")
+                lora_pack_embedding_adapter(a, b, self.K, self.N, r, rp[i], self.A_table[ao[i]:],
+                                            self.B_table[bo[i]:], stream)
+            else:
+                lora_pack_adapter(a, b, self.K, self.N, self.n_slices, r, rp[i],
+                                  self.A_table[ao[i]:], self.B_table[bo[i]:], stream)
         self.a_off = torch.tensor(ao, dtype=torch.int64, device=device)
         self.b_off = torch.tensor(bo, dtype=torch.int64, device=device)
         self.rank_dev = torch.tensor(rp, dtype=torch.int32, device=device)
@@ -221,6 +238,16 @@ def lora_shrink(table: LoraTable, x: torch.Tensor, seg: Segments, S: torch.Tenso
     check(lib.lora_shrink(ctypes.byref(table.c), _ptr(x), ldx, x.shape[0], ctypes.byref(seg.c),
                           _ptr(S), _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
           "lora_shrink")
+
+
+def lora_embedding_shrink(table: LoraTable, tokens: torch.Tensor, seg: Segments,
+                          S: torch.Tensor, stream=None) -> None:
+    """Embedding lookup side: S [M, r_max] (sorted rows) from the token ids."""
+    M = _ids_arg(tokens)
+    if S.dtype != torch.float32 or not S.is_contiguous() or S.numel() < M * table.cols:
+        raise LoraError("S must be a contiguous fp32 [M, r_max] tensor")
+    check(lib.lora_embedding_shrink(ctypes.byref(table.c), _ptr(tokens), M, ctypes.byref(seg.c),
+                                    _ptr(S), stream_handle(stream)), "lora_embedding_shrink")
 
 
 def lora_expand_add(table: LoraTable, S: torch.Tensor, seg: Segments, y: torch.Tensor,

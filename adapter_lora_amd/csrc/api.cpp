@@ -332,6 +332,33 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
                                         stream));
 }
 
+lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t emb, int32_t rank,
+                                        int32_t rank_pad, const void* A_src, const void* B_src,
+                                        void* A_dst, void* B_dst, hipStream_t stream) {
+    if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_INVALID_ARG;
+    if (vocab <= 0 || vocab % 8 || emb <= 0 || emb % 8) return LORA_INVALID_ARG;
+    if (rank < 0 || rank > LORA_MAX_RANK) return LORA_INVALID_ARG;
+    if (rank_pad != (rank + LORA_RANK_ALIGN - 1) / LORA_RANK_ALIGN * LORA_RANK_ALIGN)
+        return LORA_INVALID_ARG;
+    if (rank == 0) return LORA_OK;
+    if (!A_src || !B_src || !A_dst || !B_dst) return LORA_INVALID_ARG;
+    return from_hip(launch_pack_embedding_adapter(dtype, vocab, emb, rank, rank_pad, A_src, B_src,
+                                                  A_dst, B_dst, stream));
+}
+
+lora_status lora_embedding_shrink(const lora_weights_t* w, const int32_t* tokens, int32_t M,
+                                  const lora_segments_t* seg, float* S, hipStream_t stream) {
+    lora_status st = check_weights(w);
+    if (st != LORA_OK) return st;
+    if (w->n_slices != 1) return LORA_INVALID_ARG;
+    if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
+    if ((st = check_segments(seg, w, M)) != LORA_OK) return st;
+    if (M == 0) return LORA_OK;
+    if (!tokens || !S || !aligned16(S)) return LORA_INVALID_ARG;
+    const LinearArgs a = make_args(w, seg, M);
+    return from_hip(launch_embedding_shrink(a, tokens, S, stream));
+}
+
 // ------------------------------------------------------------------ MoE
 int32_t lora_moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_size_m) {
     if (M < 0 || topk < 1 || E < 1 || block_size_m < 1) return 0;

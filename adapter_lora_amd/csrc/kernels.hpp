@@ -83,6 +83,11 @@ hipError_t launch_pack_adapter(int dtype, int K, int64_t N, int n_sl, int rank, 
                                const void* A_src, const void* B_src, void* A_dst, void* B_dst,
                                hipStream_t st);
 
+// Embedding adapter: A stored transposed ([vocab, rank_pad]), B as usual.
+hipError_t launch_pack_embedding_adapter(int dtype, int vocab, int64_t emb, int rank,
+                                         int rank_pad, const void* A_src, const void* B_src,
+                                         void* A_dst, void* B_dst, hipStream_t st);
+
 // Segment table outputs of the single-launch decode (all null: not written).
 struct SegOut {
     int32_t* sorted_idx;
@@ -108,6 +113,11 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
 
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st);
+
+// Embedding lookup: S (fp32 [M][r_max], sorted rows) = rows of the
+// transposed A table selected by token id (a.K is the vocabulary).
+hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, float* S,
+                                   hipStream_t st);
 
 // MoE
 struct MoeArgs {

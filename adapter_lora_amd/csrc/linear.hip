@@ -167,6 +167,50 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
 }
 
 // ---------------------------------------------------------------------------
+// embedding lookup (SGLang "LoRA Layers" page, the embedding's A side):
+// S[p][j] = A_i[j, t] for the token t at sorted position p, read from the
+// transposed table row A_i^T[t] (rp contiguous values); zero past rp and for
+// token ids outside [0, vocab).  unit = one tile of the schedule; thread
+// (row, q) covers rank positions 16q .. 16q+15 of one row.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kTileThreads) void k_embed_shrink(LinearArgs a,
+                                                                const int32_t* __restrict__ tokens,
+                                                                float* __restrict__ S, int units) {
+    const int tile = (int)blockIdx.x;
+    if (tile >= units) return;
+    const TileView v = tile_view(a, tile, true);
+    if (v.seg < 0) return;
+    const int row = threadIdx.x / 4, q = threadIdx.x % 4;
+    const int m = __shfl(v.row, row, kWave);          // every wave holds the tile's 64 rows
+    if (row >= v.n || q * 16 >= a.r_max) return;
+    const int vocab = a.K;
+    const int tok = tokens[m];
+    const bool on = q * 16 < v.rp && tok >= 0 && tok < vocab;
+    const T* src = reinterpret_cast<const T*>(a.A) + v.off + (int64_t)(on ? tok : 0) * v.rp + q * 16;
+    float vals[16];
+    if constexpr (sizeof(T) == 2) {
+        const uint4 lo = ld16_if(src, on, src), hi = ld16_if(src + 8, on, src);
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            vals[2 * i] = __uint_as_float(w[i] << 16);
+            vals[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = ldf4_if(src + 4 * i, on, src);
+            vals[4 * i] = f.x; vals[4 * i + 1] = f.y; vals[4 * i + 2] = f.z; vals[4 * i + 3] = f.w;
+        }
+    }
+    float4* dst = reinterpret_cast<float4*>(S + (int64_t)(v.pbeg + row) * a.cols + q * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dst[i] = make_float4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 static unsigned grid_of(int units) { return (unsigned)(units > 0 ? units : 1); }
@@ -212,6 +256,18 @@ static GroupMap make_group_map(const LinearArgs& a) {
     gm.group_start[a.n_sl] = g;
     gm.n_groups = g;
     return gm;
+}
+
+hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, float* S,
+                                   hipStream_t st) {
+    const int units = a.max_tiles;
+    if (a.dtype == LORA_BF16)
+        hipLaunchKernelGGL(k_embed_shrink<uint16_t>, dim3(grid_of(units)), dim3(kTileThreads), 0,
+                           st, a, tokens, S, units);
+    else
+        hipLaunchKernelGGL(k_embed_shrink<float>, dim3(grid_of(units)), dim3(kTileThreads), 0, st,
+                           a, tokens, S, units);
+    return hipGetLastError();
 }
 
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,

@@ -34,6 +34,21 @@ __global__ void k_pack_B(const E* __restrict__ src, E* __restrict__ dst, int64_t
     }
 }
 
+// Embedding adapters (SGLang "LoRA Layers" page: A (rank, vocab) is read by
+// an embedding lookup): A is stored transposed, [vocab, rp] row-major, so the
+// lookup of a token reads one contiguous row of rp values.
+template <typename E>
+__global__ void k_pack_A_T(const E* __restrict__ src, E* __restrict__ dst, int vocab, int r,
+                           int rp) {
+    const int64_t total = (int64_t)vocab * rp;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t t = i / rp;
+        const int j = (int)(i - t * rp);
+        dst[i] = (j < r) ? src[(int64_t)j * vocab + t] : E(0);
+    }
+}
+
 static unsigned blocks_for(int64_t n) {
     int64_t b = (n + 255) / 256;
     if (b > 8192) b = 8192;
@@ -56,6 +71,25 @@ hipError_t launch_pack_adapter(int dtype, int K, int64_t N, int n_sl, int rank, 
                            (const uint32_t*)A_src, (uint32_t*)A_dst, K, n_sl, rank, rank_pad);
         hipLaunchKernelGGL(k_pack_B<uint32_t>, dim3(blocks_for(nb)), dim3(256), 0, st,
                            (const uint32_t*)B_src, (uint32_t*)B_dst, N, rank, rank_pad);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_embedding_adapter(int dtype, int vocab, int64_t emb, int rank,
+                                         int rank_pad, const void* A_src, const void* B_src,
+                                         void* A_dst, void* B_dst, hipStream_t st) {
+    const int64_t na = (int64_t)vocab * rank_pad;
+    const int64_t nb = emb * rank_pad;
+    if (dtype == LORA_BF16) {
+        hipLaunchKernelGGL(k_pack_A_T<uint16_t>, dim3(blocks_for(na)), dim3(256), 0, st,
+                           (const uint16_t*)A_src, (uint16_t*)A_dst, vocab, rank, rank_pad);
+        hipLaunchKernelGGL(k_pack_B<uint16_t>, dim3(blocks_for(nb)), dim3(256), 0, st,
+                           (const uint16_t*)B_src, (uint16_t*)B_dst, emb, rank, rank_pad);
+    } else {
+        hipLaunchKernelGGL(k_pack_A_T<uint32_t>, dim3(blocks_for(na)), dim3(256), 0, st,
+                           (const uint32_t*)A_src, (uint32_t*)A_dst, vocab, rank, rank_pad);
+        hipLaunchKernelGGL(k_pack_B<uint32_t>, dim3(blocks_for(nb)), dim3(256), 0, st,
+                           (const uint32_t*)B_src, (uint32_t*)B_dst, emb, rank, rank_pad);
     }
     return hipGetLastError();
 }

@@ -29,9 +29,10 @@ Protocol:
   * the same step is also captured as a HIP graph (one per input copy) and
     replayed, reported under "graph_replay" as context;
   * the oracle (fp64 CPU) is timed on the host on a bounded sample.
-Other configurations (prefill, stacked QKV / gate-up, MoE) are measured the
-same way and reported under "extra" as context; the headline line is the
-decode workload.
+Other configurations (prefill, stacked QKV / gate-up, MoE, and the
+LM-head and embedding LoRA decode cases: 32 tokens, 32000-token vocabulary,
+4096 hidden) are measured the same way and reported under "extra" as
+context; the headline line is the decode workload.
 """
 from __future__ import annotations
 
@@ -57,7 +58,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--only", default="", help="comma list: decode,prefill,qkv,gate_up,moe")
+    p.add_argument("--only", default="",
+                   help="comma list: decode,prefill,qkv,gate_up,moe,lm_head,embedding")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -250,6 +252,60 @@ def bench_linear(case, steps, warmup, fused_kernel_name, single_launch=False):
     return res
 
 
+# ----------------------------------------------------------------------------- embedding
+def bench_embedding(case, steps, warmup):
+    """Embedding LoRA on a decode batch: step = lora_build_segments +
+    lora_embedding_shrink (lookup) + lora_expand_add.  Algorithmic bytes: the
+    looked-up A rows and the B table of every touched adapter, the ids and
+    token ids, and the y rows of tokens with a delta read and written."""
+    import torch
+    import adapter_lora_amd as ml
+    es = 2 if case.dtype == "bf16" else 4
+    valid = [m for m in range(case.M) if 0 <= case.ids[m] < case.L
+             and case.ranks[case.ids[m]] > 0 and 0 <= case.tokens[m] < case.vocab]
+    touched = sorted(set(int(case.ids[m]) for m in valid))
+    b_bytes = sum(case.ranks[i] * case.emb * es for i in touched)
+    a_bytes = sum(case.ranks[int(case.ids[m])] * es for m in valid)
+    nbytes = b_bytes + a_bytes + 8 * case.M + 2 * len(valid) * case.emb * es
+    R = max(2, min(12, int(np.ceil(2 * MALL_BYTES / max(b_bytes, 1)))))
+    A = [dev_tensor(a) for a in case.A]
+    B = [dev_tensor(b) for b in case.B]
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    copies = []
+    for _ in range(R):
+        table = ml.LoraTable(A, B, case.ranks, [case.emb], case.vocab, dt, embedding=True)
+        seg = ml.Segments(case.M, case.L)
+        S = torch.zeros(case.M, table.cols, dtype=torch.float32, device="cuda")
+        copies.append((table, seg, S, dev_tensor(case.y_base)))
+    del A, B
+    ids = torch.from_numpy(case.ids).cuda()
+    toks = torch.from_numpy(case.tokens).cuda()
+    torch.cuda.synchronize()
+
+    def step(i):
+        table, seg, S, y = copies[i % R]
+        ml.lora_build_segments(ids, seg)
+        ml.lora_embedding_shrink(table, toks, seg, S)
+        ml.lora_expand_add(table, S, seg, y)
+
+    def kernels(i):
+        table, seg, S, y = copies[i % R]
+        ml.lora_embedding_shrink(table, toks, seg, S)
+        ml.lora_expand_add(table, S, seg, y)
+
+    ms_step, ms_wall = run_timed(step, steps, warmup)
+    ms_kernels = back_to_back(kernels, steps)
+    res = {"ms_per_step": ms_step, "ms_lookup_expand_b2b": ms_kernels, "ms_wall_host": ms_wall,
+           "tokens_per_s": len(valid) / (ms_step * 1e-3), "m_valid": len(valid), "M": case.M,
+           "adapters_touched": len(touched), "alg_bytes": nbytes, "rotation_copies": R,
+           "hbm_gbs": nbytes / (ms_kernels * 1e-3) / 1e9,
+           "kernel": "k_embed_shrink + k_expand_dense"}
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- MoE
 def bench_moe(case, steps, warmup):
     import torch
@@ -366,6 +422,13 @@ def main():
                                                        args.warmup, "shrink + reduce + expand")
     if want("moe"):
         results["moe_bf16"] = bench_moe(W.moe_case(0), args.steps, args.warmup)
+    if want("lm_head"):
+        results["lm_head_decode_bf16"] = bench_linear(W.lm_head_bf16(0), args.steps, args.warmup,
+                                                      "k_decode_fused<uint16_t>",
+                                                      single_launch=True)
+    if want("embedding"):
+        results["embedding_decode_bf16"] = bench_embedding(W.embedding_bf16(0), args.steps,
+                                                           args.warmup)
 
     head = results.get("decode_bf16")
     ceiling = {}

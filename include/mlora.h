@@ -281,6 +281,42 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
                               int32_t max_tiles, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* ---------------------------------------------------------------- embedding LoRA */
+
+/*
+ * Embedding LoRA (SGLang "LoRA Layers" page, VocabParallelEmbeddingWithLoRA):
+ * the A side is an embedding lookup, A_i (rank, vocab) read by token id; the
+ * B side is the usual expand with B_i (emb, rank) into the base embedding
+ * rows.  The table is a lora_weights_t with K = vocab, one slice of width
+ * emb, planned with lora_table_plan as usual, and filled by
+ * lora_pack_embedding_adapter, which stores A transposed so that a lookup
+ * reads one contiguous row:
+ *   A rows  A + a_off[i] : [vocab, rank_pad] row-major, row t = column t of
+ *                          A_i, zero past the true rank;
+ *   B rows  B + b_off[i] : [emb, rank_pad] row-major (as lora_pack_adapter).
+ *   A_src device [rank, vocab] row-major; B_src device [emb, rank].
+ * rank == 0 writes nothing.  vocab must be a multiple of 8 (as every K).
+ */
+lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t emb, int32_t rank,
+                                        int32_t rank_pad, const void* A_src, const void* B_src,
+                                        void* A_dst, void* B_dst, hipStream_t stream);
+
+/*
+ * lora_embedding_shrink: the lookup side (the page's run_lora_a_embedding).
+ * For sorted position p of segment s (adapter i, padded rank rp) and token
+ * m = sorted_idx[p] with token id t = tokens[m]:
+ *     S[p, j] = A_i[j, t]      (j < rp)
+ *     S[p, j] = 0              (rp <= j < r_max, and every j when t lies
+ *                               outside [0, vocab): the page masks such added
+ *                               tokens and has no LoRA for them)
+ * tokens device [M] int32; S device fp32 [M, r_max], rows in sorted order;
+ * rows past the last segment are not written.  w must have n_slices == 1.
+ * lora_expand_add(w, S, M, seg, y, ldy, stream) then adds S B_i^T to the
+ * base embedding rows y [M, emb].
+ */
+lora_status lora_embedding_shrink(const lora_weights_t* w, const int32_t* tokens, int32_t M,
+                                  const lora_segments_t* seg, float* S, hipStream_t stream);
+
 /* ---------------------------------------------------------------- MoE LoRA */
 
 /*
