@@ -22,7 +22,7 @@ __all__ = [
     "MoeWeights", "MoeAlign",
     "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",
     "lora_shrink_expand_add", "lora_fused_decode",
-    "lora_pack_embedding_adapter", "lora_embedding_shrink",
+    "lora_pack_embedding_adapter", "lora_embedding_shrink", "lora_embedding_decode",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
     "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
@@ -248,6 +248,32 @@ def lora_embedding_shrink(table: LoraTable, tokens: torch.Tensor, seg: Segments,
         raise LoraError("S must be a contiguous fp32 [M, r_max] tensor")
     check(lib.lora_embedding_shrink(ctypes.byref(table.c), _ptr(tokens), M, ctypes.byref(seg.c),
                                     _ptr(S), stream_handle(stream)), "lora_embedding_shrink")
+
+
+def lora_embedding_decode(table: LoraTable, ids: torch.Tensor, tokens: torch.Tensor,
+                          y: torch.Tensor, seg: Optional[Segments] = None,
+                          adapter_enabled: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One launch: y += B_i A_i[:, token] for up to 64 tokens (embedding
+    LoRA), grouped by adapter on chip; writes the segment table into `seg`
+    when given."""
+    M = _ids_arg(ids)
+    if _ids_arg(tokens) != M or y.shape[0] != M:
+        raise LoraError("ids, tokens and y must have the same number of rows")
+    ldy = _rows(y, "y")
+    if seg is not None:
+        if seg.L != table.L or M > seg.sorted_idx.shape[0]:
+            raise LoraError("segment buffers do not match the table or the batch")
+        outs = [_ptr(seg.sorted_idx), _ptr(seg.seg_indptr), _ptr(seg.req_to_lora),
+                _ptr(seg.num_segments), _ptr(seg.tile_info), _ptr(seg.tile_rows),
+                _ptr(seg.num_tiles)]
+        cap = seg.max_tiles
+    else:
+        outs = [_ptr(None)] * 7
+        cap = 0
+    check(lib.lora_embedding_decode(ctypes.byref(table.c), _ptr(ids),
+                                    _mask_arg(adapter_enabled, table.L), _ptr(tokens), M, _ptr(y),
+                                    ldy, *outs, cap, stream_handle(stream)),
+          "lora_embedding_decode")
 
 
 def lora_expand_add(table: LoraTable, S: torch.Tensor, seg: Segments, y: torch.Tensor,

@@ -84,6 +84,7 @@ SIGNATURES = {
                                 P]),
     "lora_pack_embedding_adapter": (I32, [I32, I32, I64, I32, I32, P, P, P, P, P]),
     "lora_embedding_shrink": (I32, [PW, P, I32, PS, P, P]),
+    "lora_embedding_decode": (I32, [PW, P, P, P, I32, P, I64, P, P, P, P, P, P, P, I32, P]),
     "lora_moe_align_capacity": (I32, [I32, I32, I32, I32]),
     "lora_moe_align_run": (I32, [P, P, P, I32, I32, I32, I32, PMA, P]),
     "lora_moe_workspace_size": (SZ, [PMW, I32]),

@@ -359,6 +359,38 @@ lora_status lora_embedding_shrink(const lora_weights_t* w, const int32_t* tokens
     return from_hip(launch_embedding_shrink(a, tokens, S, stream));
 }
 
+lora_status lora_embedding_decode(const lora_weights_t* w, const int32_t* ids,
+                                  const int32_t* adapter_enabled, const int32_t* tokens,
+                                  int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                                  int32_t* seg_indptr, int32_t* req_to_lora,
+                                  int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
+                                  int32_t* num_tiles, int32_t max_tiles, hipStream_t stream) {
+    lora_status st = check_weights(w);
+    if (st != LORA_OK) return st;
+    if (w->n_slices != 1) return LORA_INVALID_ARG;
+    if (M < 0) return LORA_INVALID_ARG;
+    if (M > LORA_DECODE_MAX_M) return LORA_UNSUPPORTED;
+    const bool table = sorted_idx != nullptr;
+    if (table) {
+        if (!seg_indptr || !req_to_lora || !num_segments || !tile_info || !tile_rows || !num_tiles)
+            return LORA_INVALID_ARG;
+        if (max_tiles < lora_tile_capacity(M, w->L)) return LORA_INVALID_ARG;
+    }
+    if (M == 0) {
+        if (!table) return LORA_OK;
+        return from_hip(launch_build_segments(nullptr, nullptr, 0, w->L, sorted_idx, seg_indptr,
+                                              req_to_lora, num_segments, tile_info, tile_rows,
+                                              num_tiles, max_tiles, stream));
+    }
+    if (!ids || !tokens) return LORA_INVALID_ARG;
+    if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;
+    lora_segments_t none{};
+    const LinearArgs a = make_args(w, &none, M);
+    const SegOut out{sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
+                     num_tiles};
+    return from_hip(launch_embedding_decode(a, ids, adapter_enabled, tokens, out, y, ldy, stream));
+}
+
 // ------------------------------------------------------------------ MoE
 int32_t lora_moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t block_size_m) {
     if (M < 0 || topk < 1 || E < 1 || block_size_m < 1) return 0;

@@ -48,6 +48,8 @@ struct DecodeParams {
     const int32_t* enabled;  // adapter mask for that grouping (may be null)
     SegOut out;              // segment table written by the last workgroup (ids mode)
     int writer;              // 1 when the last workgroup writes `out`
+    const int32_t* tokens;   // non-null: embedding lookup, S rows read from the
+                             // transposed A table by token id (a.K = vocab); no producers
 };
 
 // ---------------------------------------------------------------- shared view
@@ -61,6 +63,8 @@ struct DecodeParams {
 struct SegView {
     int nseg, id, rp, p0, ms, my_idx;
     int64_t off;
+    int tok;                   // lane p: token id at sorted position p (embedding lookup)
+    int64_t off2;              // the adapter's A offset as well (embedding lookup)
 };
 
 // Exchange slot of K chunk c, consumer tile t (its own copy), sorted
@@ -78,6 +82,8 @@ struct ViewArgs {
     const int32_t* rank;
     const int64_t* offs;       // a_off for producers, b_off for consumers
     int M, L;
+    const int32_t* tokens;     // embedding lookup: token ids (else null)
+    const int64_t* offs2;      // embedding lookup: a_off (else null)
 };
 
 __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArgs& va, int s) {
@@ -88,6 +94,7 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
     SegView v;
     TokenLoad tl;
     int p1 = 0;
+    const int tk = va.tokens ? va.tokens[min(lane, M - 1)] : 0;
     if (va.ids) {
         tl = load_token(va.ids, p.enabled, M, L);
     } else {
@@ -100,7 +107,7 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
         v.my_idx = a.sorted_idx[min(lane, M - 1)];
     }
     int rk[4];
-    int64_t of[4];
+    int64_t of[4], of2[4];
     const bool small = L <= 4 * kWave;
     if (small) {
 #pragma unroll
@@ -109,9 +116,11 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
                 const int j = min(q * kWave + lane, L - 1);
                 rk[q] = va.rank[j];
                 of[q] = offs[j];
+                of2[q] = va.offs2 ? va.offs2[j] : 0;
             } else {
                 rk[q] = 0;
                 of[q] = 0;
+                of2[q] = 0;
             }
         }
     }
@@ -133,10 +142,17 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
         const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)o_sel, src);
         const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)o_sel >> 32), src);
         v.off = (int64_t)(((uint64_t)hi << 32) | lo);
+        const int64_t o2 = q == 0 ? of2[0] : q == 1 ? of2[1] : q == 2 ? of2[2] : of2[3];
+        const uint32_t lo2 = __builtin_amdgcn_readlane((uint32_t)o2, src);
+        const uint32_t hi2 = __builtin_amdgcn_readlane((uint32_t)((uint64_t)o2 >> 32), src);
+        v.off2 = (int64_t)(((uint64_t)hi2 << 32) | lo2);
     } else {
         v.rp = va.rank[id];
         v.off = offs[id];
+        v.off2 = va.offs2 ? va.offs2[id] : 0;
     }
+    // token id at each sorted position (lane p reads token my_idx of lane p)
+    v.tok = va.tokens ? __shfl(tk, v.my_idx & (kWave - 1), kWave) : 0;
     v.ms = p1 - v.p0;
     return v;
 }
@@ -370,7 +386,27 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     float* sS = reinterpret_cast<float*>(lds);
     bool ok = true;
     const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * a.r_max;
-    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
+    if (p.tokens) {
+        // embedding lookup: the S row of sorted position p0 + t is row `tok`
+        // of the adapter's transposed A table; wave w takes tokens w, w + 4, ...
+        // (the token is wave-uniform, so it is read with readlane)
+        const T* At = reinterpret_cast<const T*>(a.A) + v.off2;
+        const int lane = lane_id();
+        for (int t = tid / kWave; t < v.ms; t += kDecWaves) {
+            const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
+            const bool on = tok >= 0 && tok < a.K;
+            if (lane < rp) {
+                const float val = on ? Io<T>::ld(At + (int64_t)tok * rp + lane) : 0.f;
+                if constexpr (sizeof(T) == 2) {
+                    sHi[t * SLD + lane] = (uint16_t)f32_to_bf16(val);   // exact: val is bf16
+                    sLo[t * SLD + lane] = 0;
+                } else {
+                    sS[t * SLD + lane] = val;
+                }
+            }
+        }
+    }
+    for (int e = p.tokens ? v.ms * rp : threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
         slot_t* sp = slot_at(p, 0, tile, v.p0 + t, j);
         float acc = 0.f;
@@ -440,6 +476,13 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     //    The first kTokGroup tokens take every prefetched y value before the
     //    first store: the wait for a load counts the stores issued after it,
     //    so a store in between would add its whole latency to the next token.
+    //    A looked-up token outside the vocabulary has no delta: its row is
+    //    not stored at all.
+    auto row_on = [&](int t) {
+        if (!p.tokens) return true;
+        const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
+        return tok >= 0 && tok < a.K;
+    };
     float res[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
@@ -450,20 +493,22 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     for (int u = 0; u < kTokGroup; ++u) {
         if (u >= v.ms) break;
         const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + u);
-        if (nin) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, res[u]);
+        if (nin && row_on(u)) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, res[u]);
     }
     for (int t = kTokGroup; t < v.ms; ++t) {
         const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + t);
         const float old = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
         const float r = old + delta(t);
-        if (nin) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, r);
+        if (nin && row_on(t)) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, r);
     }
     // 4. this workgroup is its slot copy's only reader: empty it for the next
     //    call.  Issued after the y stores, so that no wait for a prefetched y
     //    value has to count these stores as well.
-    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
-        slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
-        for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
+    if (!p.tokens) {
+        for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
+            slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
+            for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
+        }
     }
 }
 
@@ -487,7 +532,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
         return;
     }
     if ((int)blockIdx.x < p.grid1) {
-        const ViewArgs va{ids, rank, a_off, M, L};
+        const ViewArgs va{ids, rank, a_off, M, L, nullptr, nullptr};
         if constexpr (sizeof(T) == 2)
             dec_produce_mfma(p, va, blockIdx.x, reinterpret_cast<float*>(lds));
         else
@@ -498,7 +543,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
     const int u = blockIdx.x - p.grid1;
     const int s = u / p.n_tiles;
     const int t = u % p.n_tiles;
-    const SegView v = seg_view(p, ViewArgs{ids, rank, b_off, M, L}, s);
+    const SegView v = seg_view(p, ViewArgs{ids, rank, b_off, M, L, p.tokens,
+                                           p.tokens ? a_off : nullptr}, s);
     if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
     int sl = 0;
     while (sl + 1 < a.n_sl && t >= p.tile_start[sl + 1]) ++sl;
@@ -510,6 +556,48 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
         dec_consume<T, 32>(p, v, t, n0, n1, lds);
     else
         dec_consume<T, 64>(p, v, t, n0, n1, lds);
+}
+
+static hipError_t launch_decode(DecodeParams& p, unsigned grid, hipStream_t st) {
+    const LinearArgs& a = p.a;
+    if (a.dtype == LORA_BF16) {
+        hipLaunchKernelGGL(k_decode_fused<uint16_t>, dim3(grid), dim3(kDecThreads), 0, st, p.ids,
+                           a.rank, a.a_off, a.b_off, a.M, a.L, p);
+    } else {
+        hipLaunchKernelGGL(k_decode_fused<float>, dim3(grid), dim3(kDecThreads), 0, st, p.ids,
+                           a.rank, a.a_off, a.b_off, a.M, a.L, p);
+    }
+    return hipGetLastError();
+}
+
+static void set_tiles(DecodeParams& p) {
+    const LinearArgs& a = p.a;
+    int t = 0;
+    for (int s = 0; s < a.n_sl; ++s) {
+        p.tile_start[s] = t;
+        t += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+    }
+    p.tile_start[a.n_sl] = t;
+    p.n_tiles = t;
+}
+
+hipError_t launch_embedding_decode(const LinearArgs& a, const int32_t* ids,
+                                   const int32_t* enabled, const int32_t* tokens,
+                                   const SegOut& out, void* y, int64_t ldy, hipStream_t st) {
+    DecodeParams p{};
+    p.a = a;
+    p.y = y;
+    p.ldy = ldy;
+    p.ids = ids;
+    p.enabled = ids ? enabled : nullptr;
+    p.out = out;
+    p.writer = (ids && out.sorted_idx) ? 1 : 0;
+    p.tokens = tokens;
+    p.C = 0;
+    p.jb_max = a.cols / 16;
+    p.grid1 = 0;                        // consumers only: S comes from the lookup
+    set_tiles(p);
+    return launch_decode(p, (unsigned)(a.s_max * p.n_tiles + p.writer), st);
 }
 
 hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
@@ -534,22 +622,8 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     p.C = (a.K + kDecKChunk - 1) / kDecKChunk;
     p.jb_max = a.cols / 16;
     p.grid1 = a.s_max * p.jb_max * p.C;
-    int t = 0;
-    for (int s = 0; s < a.n_sl; ++s) {
-        p.tile_start[s] = t;
-        t += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
-    }
-    p.tile_start[a.n_sl] = t;
-    p.n_tiles = t;
-    const unsigned grid = (unsigned)(p.grid1 + a.s_max * p.n_tiles + p.writer);
-    if (a.dtype == LORA_BF16) {
-        hipLaunchKernelGGL(k_decode_fused<uint16_t>, dim3(grid), dim3(kDecThreads), 0, st, p.ids,
-                           a.rank, a.a_off, a.b_off, a.M, a.L, p);
-    } else {
-        hipLaunchKernelGGL(k_decode_fused<float>, dim3(grid), dim3(kDecThreads), 0, st, p.ids,
-                           a.rank, a.a_off, a.b_off, a.M, a.L, p);
-    }
-    return hipGetLastError();
+    set_tiles(p);
+    return launch_decode(p, (unsigned)(p.grid1 + a.s_max * p.n_tiles + p.writer), st);
 }
 
 }  // namespace mlora

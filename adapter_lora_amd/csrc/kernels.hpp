@@ -107,6 +107,14 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
                                const SegOut& out, const void* x, int64_t ldx, void* y,
                                int64_t ldy, void* ws, hipStream_t st);
 
+// Single-launch embedding decode (M <= LORA_DECODE_MAX_M): the fused decode
+// kernel's consumers only, with S rows looked up from the transposed A table
+// by token id; segments grouped from `ids` on chip (table written to `out`
+// when out.sorted_idx is not null).
+hipError_t launch_embedding_decode(const LinearArgs& a, const int32_t* ids,
+                                   const int32_t* enabled, const int32_t* tokens,
+                                   const SegOut& out, void* y, int64_t ldy, hipStream_t st);
+
 // S (fp32 [M][cols], sorted rows) from x; `ws` holds the partial sums.
 hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float* S, void* ws,
                          hipStream_t st);

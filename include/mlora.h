@@ -317,6 +317,30 @@ lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t em
 lora_status lora_embedding_shrink(const lora_weights_t* w, const int32_t* tokens, int32_t M,
                                   const lora_segments_t* seg, float* S, hipStream_t stream);
 
+/*
+ * lora_embedding_decode: the whole embedding-LoRA path for a small batch in
+ * one kernel launch (the lookup of lora_embedding_shrink and the expand of
+ * lora_expand_add, with the grouping of lora_fused_decode).  For
+ * 1 <= M <= LORA_DECODE_MAX_M:
+ *     y[m, n] += sum_j A_i[j, t] B_i[n, j]     i = ids[m], t = tokens[m]
+ * for tokens with an (enabled, non-empty) adapter and 0 <= t < vocab; other
+ * rows are not written.  Every workgroup groups the batch by adapter itself
+ * and reads its tokens' S rows straight from the transposed A table, so no
+ * workgroup waits for another and no workspace is needed.  When sorted_idx
+ * is not NULL the launch also writes the segment table and tile schedule
+ * (as lora_fused_decode).  w must be an embedding table (n_slices == 1, A
+ * packed by lora_pack_embedding_adapter).  M == 0 writes the empty table
+ * (when asked) and nothing else; M > LORA_DECODE_MAX_M returns
+ * LORA_UNSUPPORTED (use lora_build_segments, lora_embedding_shrink and
+ * lora_expand_add).
+ */
+lora_status lora_embedding_decode(const lora_weights_t* w, const int32_t* ids,
+                                  const int32_t* adapter_enabled, const int32_t* tokens,
+                                  int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                                  int32_t* seg_indptr, int32_t* req_to_lora,
+                                  int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
+                                  int32_t* num_tiles, int32_t max_tiles, hipStream_t stream);
+
 /* ---------------------------------------------------------------- MoE LoRA */
 
 /*

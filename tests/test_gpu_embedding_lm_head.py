@@ -3,7 +3,8 @@ VocabParallelEmbeddingWithLoRA, ParallelLMHeadWithLoRA) through the C ABI
 against the fp64 oracle.
 
 Embedding: segment table -> lora_embedding_shrink (lookup of the token's
-column of A, into S) -> lora_expand_add.  The looked-up S values are bf16 or
+column of A, into S) -> lora_expand_add, and the single launch
+lora_embedding_decode (lookup inside the decode kernel's consumers).  The looked-up S values are bf16 or
 fp32 weights widened to fp32, so S is compared bit for bit; y meets the
 spec tolerance and the element-wise bound; rows without a delta (no
 adapter, disabled adapter, rank 0, token id past the vocabulary) are
@@ -170,3 +171,55 @@ def test_lm_head_larger_batch(ml):
     keep = ~O.delta_rows(case.ids, case.ranks)
     assert np.array_equal(got[keep], case.y_base.values[keep])
     assert_close(got, oracle_y(case), case.dtype, case.y_base.values, case.name)
+
+
+# ---------------------------------------------------------------- embedding, one launch
+def run_embedding_decode(ml, case, enabled=None, reps=1):
+    dt = torch_dtype(case.dtype)
+    table = ml.LoraTable([to_dev(a) for a in case.A], [to_dev(b) for b in case.B], case.ranks,
+                         [case.emb], case.vocab, dt, embedding=True)
+    ids = torch.from_numpy(case.ids).cuda()
+    toks = torch.from_numpy(case.tokens).cuda()
+    en = None if enabled is None else torch.from_numpy(enabled).cuda()
+    seg = ml.Segments(case.M, case.L)
+    y = to_dev(case.y_base)
+    for _ in range(reps):
+        ml.lora_embedding_decode(table, ids, toks, y, seg=seg, adapter_enabled=en)
+    torch.cuda.synchronize()
+    return to_f64(y), seg
+
+
+EMB_DECODE_CASES = [
+    ("decode_vocab32000", lambda: W.embedding_bf16(0), None),
+    ("outside_tokens_masked", lambda: W.embedding_bf16(1, M=48, vocab=5000, emb=1024, L=9,
+                                                       p_outside=0.25),
+     np.array([1, 1, 0, 1, 1, 1, 0, 1, 1], np.int32)),
+    ("fp32_ragged", lambda: W.embedding_bf16(3, M=40, vocab=2000, emb=264, ranks=[16, 5, 33, 0],
+                                             dtype=W.F32, p_outside=0.1), None),
+    ("M64_one_adapter", lambda: W.embedding_bf16(7, M=64, vocab=1000, emb=512, ranks=[64],
+                                                 p_none=0.0), None),
+    ("M1", lambda: W.embedding_bf16(4, M=1, vocab=800, emb=128, ranks=[64], p_none=0.0), None),
+]
+
+
+@pytest.mark.parametrize("name,mk,enabled", EMB_DECODE_CASES,
+                         ids=[c[0] for c in EMB_DECODE_CASES])
+def test_embedding_decode_single_launch(ml, name, mk, enabled):
+    case = mk()
+    log(f"embedding decode {name} M={case.M} vocab={case.vocab} emb={case.emb} L={case.L}")
+    reps = 2 if name == "fp32_ragged" else 1
+    got, seg = run_embedding_decode(ml, case, enabled, reps)
+    A = [a.values for a in case.A]
+    B = [b.values for b in case.B]
+    ref = O.embedding_add(case.tokens, case.ids, A, B, case.ranks, case.vocab,
+                          case.y_base.values, enabled)
+    if reps > 1:
+        ref = case.y_base.values + reps * (ref - case.y_base.values)
+    keep = ~O.delta_rows(case.ids, case.ranks, enabled)
+    keep |= (case.tokens < 0) | (case.tokens >= case.vocab)
+    assert np.array_equal(got[keep], case.y_base.values[keep]), "pass-through rows changed"
+    assert_close(got, ref, case.dtype, case.y_base.values, name, roundings=reps)
+    si, sp, req, n = O.build_segments(case.ids, case.L, enabled)
+    assert np.array_equal(seg.sorted_idx[:case.M].cpu().numpy(), si)
+    assert np.array_equal(seg.seg_indptr.cpu().numpy(), sp)
+    assert int(seg.num_segments.cpu()[0]) == n
