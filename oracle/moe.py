@@ -27,7 +27,11 @@ Readings where the page is silent (each listed in the design doc):
   * tokens with id -1 belong to no list;
   * gate_up A is shared by the gate and up halves; gate is the first half
     (columns [0, I)) of the 2I outputs;
-  * routing weights are applied in the reduce, after both deltas.
+  * routing weights are applied in the reduce, after both deltas;
+  * experts_shared_outer_loras: the stacks whose LoRAInfo shape carries
+    "num_experts_or_1" -- gate_up A and down B, the matrices on the hidden
+    side -- have one expert slot shared by every expert; gate_up B and down
+    A stay per expert.
 """
 from __future__ import annotations
 
@@ -92,9 +96,11 @@ def _pair_adapter(ids, adapter_enabled, L, m):
     return l
 
 
-def moe_gate_up_add(x, cache1, topk_ids, ids, adapter_enabled, A_gu, B_gu) -> np.ndarray:
-    """Stage 1.5: cache1[f] += B_gu[l, e] @ (A_gu[l, e] @ x[m]) for every pair
-    f = m*topk + k with an enabled adapter l = ids[m], e = topk_ids[m, k]."""
+def moe_gate_up_add(x, cache1, topk_ids, ids, adapter_enabled, A_gu, B_gu,
+                    shared_outer: bool = False) -> np.ndarray:
+    """Stage 1.5: cache1[f] += B_gu[l, e] @ (A_gu[l, e'] @ x[m]) for every pair
+    f = m*topk + k with an enabled adapter l = ids[m], e = topk_ids[m, k];
+    e' = e, or 0 when the outer stacks are shared (A_gu [L, 1, r, H])."""
     x = _f64(x)
     c1 = np.array(cache1, dtype=np.float64, copy=True)
     A_gu = _f64(A_gu)
@@ -107,7 +113,7 @@ def moe_gate_up_add(x, cache1, topk_ids, ids, adapter_enabled, A_gu, B_gu) -> np
             continue
         for k in range(topk):
             e = int(topk_ids[m, k])
-            s = A_gu[l, e] @ x[m]
+            s = A_gu[l, 0 if shared_outer else e] @ x[m]
             c1[m * topk + k] = c1[m * topk + k] + B_gu[l, e] @ s
     return c1
 
@@ -127,8 +133,10 @@ def silu_and_mul(cache1) -> np.ndarray:
     return out
 
 
-def moe_down_add(cache2, cache3, topk_ids, ids, adapter_enabled, A_d, B_d) -> np.ndarray:
-    """Stage 3.5: cache3[f] += B_d[l, e] @ (A_d[l, e] @ cache2[f])."""
+def moe_down_add(cache2, cache3, topk_ids, ids, adapter_enabled, A_d, B_d,
+                 shared_outer: bool = False) -> np.ndarray:
+    """Stage 3.5: cache3[f] += B_d[l, e'] @ (A_d[l, e] @ cache2[f]), e' = e, or 0
+    when the outer stacks are shared (B_d [L, 1, H, r])."""
     c2 = _f64(cache2)
     c3 = np.array(cache3, dtype=np.float64, copy=True)
     A_d = _f64(A_d)
@@ -142,7 +150,7 @@ def moe_down_add(cache2, cache3, topk_ids, ids, adapter_enabled, A_d, B_d) -> np
         for k in range(topk):
             e = int(topk_ids[m, k])
             f = m * topk + k
-            c3[f] = c3[f] + B_d[l, e] @ (A_d[l, e] @ c2[f])
+            c3[f] = c3[f] + B_d[l, 0 if shared_outer else e] @ (A_d[l, e] @ c2[f])
     return c3
 
 

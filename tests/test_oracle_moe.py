@@ -124,11 +124,11 @@ def test_silu():
     assert np.allclose(O.silu(-z), O.silu(z) - z, atol=1e-12)
 
 
-def tiny_moe(seed=0):
+def tiny_moe(seed=0, shared_outer=False):
     rng = np.random.default_rng(seed)
     M, H, I, E, topk, L, r = 16, 64, 128, 4, 2, 3, 16
     case = W.moe_case(seed, M=M, H=H, I=I, E=E, topk=topk, L=L, rank=r, block_size_m=8,
-                      p_none=0.2, dtype=W.F32)
+                      p_none=0.2, dtype=W.F32, shared_outer=shared_outer)
     W13 = rng.standard_normal((E, 2 * I, H)) * 0.1
     W2 = rng.standard_normal((E, H, I)) * 0.1
     return case, W13, W2
@@ -144,12 +144,13 @@ def staged(case, W13, W2, gate_up_after_act=False, down_after_reduce=False):
     if gate_up_after_act:
         c2 = O.silu_and_mul(c1)
         d = O.moe_gate_up_add(x, np.zeros_like(c1), case.topk_ids, case.ids,
-                              case.adapter_enabled, case.A_gu.values, case.B_gu.values)
+                              case.adapter_enabled, case.A_gu.values, case.B_gu.values,
+                              case.shared_outer)
         I = c2.shape[1]
         c2 = c2 + d[:, :I] * d[:, I:]
     else:
         c1 = O.moe_gate_up_add(x, c1, case.topk_ids, case.ids, case.adapter_enabled,
-                               case.A_gu.values, case.B_gu.values)
+                               case.A_gu.values, case.B_gu.values, case.shared_outer)
         c2 = O.silu_and_mul(c1)
     c3 = np.zeros((M * topk, W2.shape[1]))
     for m in range(M):
@@ -158,12 +159,13 @@ def staged(case, W13, W2, gate_up_after_act=False, down_after_reduce=False):
     if down_after_reduce:
         out = O.topk_reduce(c3, case.topk_weights)
         d = O.moe_down_add(c2, np.zeros_like(c3), case.topk_ids, case.ids,
-                           case.adapter_enabled, case.A_d.values, case.B_d.values)
+                           case.adapter_enabled, case.A_d.values, case.B_d.values,
+                           case.shared_outer)
         for m in range(M):
             out[m] += d[m * topk:(m + 1) * topk].sum(axis=0)
         return out
     c3 = O.moe_down_add(c2, c3, case.topk_ids, case.ids, case.adapter_enabled,
-                        case.A_d.values, case.B_d.values)
+                        case.A_d.values, case.B_d.values, case.shared_outer)
     return O.topk_reduce(c3, case.topk_weights)
 
 
@@ -178,17 +180,19 @@ def merged(case, W13, W2):
         on = 0 <= l < case.L and case.adapter_enabled[l]
         for k in range(topk):
             e = int(case.topk_ids[m, k])
-            w13 = W13[e] + (case.B_gu.values[l, e] @ case.A_gu.values[l, e] if on else 0)
-            w2 = W2[e] + (case.B_d.values[l, e] @ case.A_d.values[l, e] if on else 0)
+            eo = 0 if case.shared_outer else e        # outer stacks: one shared slot
+            w13 = W13[e] + (case.B_gu.values[l, e] @ case.A_gu.values[l, eo] if on else 0)
+            w2 = W2[e] + (case.B_d.values[l, eo] @ case.A_d.values[l, e] if on else 0)
             h = w13 @ x[m]
             a = h[:I] / (1 + np.exp(-h[:I])) * h[I:]
             out[m] += case.topk_weights[m, k] * (w2 @ a)
     return out
 
 
+@pytest.mark.parametrize("shared_outer", [False, True])
 @pytest.mark.parametrize("seed", range(3))
-def test_pipeline_equals_merged_weights(seed):
-    case, W13, W2 = tiny_moe(seed)
+def test_pipeline_equals_merged_weights(seed, shared_outer):
+    case, W13, W2 = tiny_moe(seed, shared_outer)
     got = staged(case, W13, W2)
     ref = merged(case, W13, W2)
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
@@ -220,3 +224,49 @@ def test_topk_reduce_weights():
     w = rng.random((5, 2))
     out = O.topk_reduce(c3, w)
     assert np.allclose(out, w[:, :1] * c3[0::2] + w[:, 1:] * c3[1::2], rtol=1e-14)
+
+
+def _replicated(case):
+    """The same adapters with the shared outer stacks copied into every
+    expert slot (an unshared case)."""
+    import dataclasses
+    rep = lambda t: W.Tensor(t.dtype, np.repeat(t.values, case.E, axis=1),
+                             np.repeat(t.storage, case.E, axis=1))
+    return dataclasses.replace(case, A_gu=rep(case.A_gu), B_d=rep(case.B_d), shared_outer=False)
+
+
+def _chain(case, gate_up=None, down=None):
+    gate_up = gate_up or O.moe_gate_up_add
+    down = down or O.moe_down_add
+    c1 = gate_up(case.x.values, case.cache1.values, case.topk_ids, case.ids,
+                 case.adapter_enabled, case.A_gu.values, case.B_gu.values, case.shared_outer)
+    c3 = down(O.silu_and_mul(c1), case.cache3.values, case.topk_ids, case.ids,
+              case.adapter_enabled, case.A_d.values, case.B_d.values, case.shared_outer)
+    return c1, c3
+
+
+def test_shared_outer_equals_replicated_stacks():
+    """experts_shared_outer_loras (SGLang "LoRA + MoE" page): sharing the
+    gate_up A and down B slot equals copying it into every expert slot."""
+    case = W.moe_case(4, M=20, H=32, I=48, E=4, topk=2, L=3, rank=8, block_size_m=4,
+                      p_none=0.1, dtype=W.F32, shared_outer=True)
+    assert case.A_gu.shape[1] == 1 and case.B_d.shape[1] == 1 and case.B_gu.shape[1] == 4
+    got = _chain(case)
+    ref = _chain(_replicated(case))
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_shared_outer_mutant_caught():
+    """Planted slip: the inner stacks (gate_up B, down A) shared instead of the
+    outer ones; the replicated-stack pin rejects it."""
+    case = W.moe_case(5, M=20, H=32, I=48, E=4, topk=2, L=2, rank=8, block_size_m=4,
+                      dtype=W.F32, shared_outer=True)
+
+    def gate_up_inner(x, c1, tid, ids, en, A, B, shared):
+        Bs = np.repeat(B[:, :1], B.shape[1], axis=1)          # inner slot 0 for all
+        As = np.repeat(A, B.shape[1], axis=1)
+        return O.moe_gate_up_add(x, c1, tid, ids, en, As, Bs)
+
+    got = _chain(case, gate_up=gate_up_inner)
+    ref = _chain(_replicated(case))
+    assert not np.allclose(got[0], ref[0])

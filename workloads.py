@@ -250,9 +250,6 @@ def integer_linear(seed: int, M: int, K: int, slice_sizes, ranks, dtype: str) ->
 
 
 # ----------------------------------------------------------------------------
-# MoE LoRA case
-# ----------------------------------------------------------------------------
-# ----------------------------------------------------------------------------
 # embedding and LM-head LoRA (SGLang "LoRA Layers" page: the embedding's A
 # side is a lookup of A (r, vocab), its B is (emb, r); the LM head is a dense
 # LoRA linear whose output width is the vocabulary)
@@ -317,6 +314,9 @@ def lm_head_bf16(seed: int = 0, M: int = 32, K: int = 4096, vocab: int = 32000,
     return case
 
 
+# ----------------------------------------------------------------------------
+# MoE LoRA case
+# ----------------------------------------------------------------------------
 @dataclasses.dataclass
 class MoECase:
     name: str
@@ -334,12 +334,13 @@ class MoECase:
     topk_ids: np.ndarray            # int32 [M, topk]
     topk_weights: np.ndarray        # float32 [M, topk]
     x: Tensor                       # [M, H]
-    A_gu: Tensor                    # [L, E, r, H]
+    A_gu: Tensor                    # [L, E, r, H]  ([L, 1, r, H] when shared_outer)
     B_gu: Tensor                    # [L, E, 2I, r]
     A_d: Tensor                     # [L, E, r, I]
-    B_d: Tensor                     # [L, E, H, r]
+    B_d: Tensor                     # [L, E, H, r]  ([L, 1, H, r] when shared_outer)
     cache1: Tensor                  # [M*topk, 2I]   base gate/up output
     cache3: Tensor                  # [M*topk, H]    base down output
+    shared_outer: bool = False      # outer (hidden-side) matrices shared by the experts
 
 
 def _route(rng, M, E, topk):
@@ -356,10 +357,13 @@ def _route(rng, M, E, topk):
 
 def moe_case(seed: int = 0, M: int = 256, H: int = 4096, I: int = 14336, E: int = 8,
              topk: int = 2, L: int = 4, rank: int = 16, block_size_m: int = 64,
-             p_none: float = 0.0, dtype: str = BF16, enabled=None) -> MoECase:
+             p_none: float = 0.0, dtype: str = BF16, enabled=None,
+             shared_outer: bool = False) -> MoECase:
     """MoE-LoRA: top-2 routing over 8 experts, 4 adapters of rank 16 with
     per-expert gate_up and down A/B; cache1/cache3 stand in for the base
-    expert GEMM outputs, ~N(0,1)."""
+    expert GEMM outputs, ~N(0,1).  shared_outer: the gate_up A and down B
+    stacks have one expert slot, shared by all experts (SGLang "LoRA + MoE"
+    page, experts_shared_outer_loras)."""
     rng = np.random.default_rng(seed)
     topk_ids, topk_w = _route(rng, M, E, topk)
     ids = rng.integers(0, L, size=M).astype(np.int32)
@@ -368,14 +372,16 @@ def moe_case(seed: int = 0, M: int = 256, H: int = 4096, I: int = 14336, E: int 
     en = np.ones(L, np.int32) if enabled is None else np.asarray(enabled, np.int32)
     f = lambda shape, s: rng.standard_normal(shape, dtype=np.float32) * s
     x = make_tensor(f((M, H), 1.0), dtype)
-    A_gu = make_tensor(f((L, E, rank, H), 0.02), dtype)
+    Eo = 1 if shared_outer else E
+    A_gu = make_tensor(f((L, Eo, rank, H), 0.02), dtype)
     B_gu = make_tensor(f((L, E, 2 * I, rank), 0.02), dtype)
     A_d = make_tensor(f((L, E, rank, I), 0.02), dtype)
-    B_d = make_tensor(f((L, E, H, rank), 0.02), dtype)
+    B_d = make_tensor(f((L, Eo, H, rank), 0.02), dtype)
     c1 = make_tensor(f((M * topk, 2 * I), 1.0), dtype)
     c3 = make_tensor(f((M * topk, H), 1.0), dtype)
-    return MoECase(f"moe_{dtype}", dtype, M, H, I, E, topk, L, rank, block_size_m, ids, en,
-                   topk_ids, topk_w, x, A_gu, B_gu, A_d, B_d, c1, c3)
+    name = f"moe_shared_outer_{dtype}" if shared_outer else f"moe_{dtype}"
+    return MoECase(name, dtype, M, H, I, E, topk, L, rank, block_size_m, ids, en,
+                   topk_ids, topk_w, x, A_gu, B_gu, A_d, B_d, c1, c3, shared_outer)
 
 
 # ----------------------------------------------------------------------------
