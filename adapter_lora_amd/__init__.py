@@ -324,20 +324,26 @@ def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: t
 
 # ------------------------------------------------------------------------- MoE
 class MoeWeights:
-    """Dense per-expert LoRA stacks [L, E, r, H] / [L, E, 2I, r] / [L, E, r, I] / [L, E, H, r]."""
+    """Dense per-expert LoRA stacks [L, E, r, H] / [L, E, 2I, r] / [L, E, r, I] / [L, E, H, r].
+    Outer stacks shared by the experts (gate_up A [L, 1, r, H] and down B
+    [L, 1, H, r]) are recognised from their single expert slot."""
 
     def __init__(self, A_gu, B_gu, A_d, B_d, adapter_enabled):
         self.A_gu, self.B_gu = A_gu.contiguous(), B_gu.contiguous()
         self.A_d, self.B_d = A_d.contiguous(), B_d.contiguous()
         self.enabled = adapter_enabled.to(torch.int32).contiguous()
-        L, E, r, H = self.A_gu.shape
-        I = self.A_d.shape[3]
-        if tuple(self.B_gu.shape) != (L, E, 2 * I, r) or tuple(self.A_d.shape) != (L, E, r, I) \
-                or tuple(self.B_d.shape) != (L, E, H, r):
+        L, E, I2, r = self.B_gu.shape
+        I = I2 // 2
+        H = self.A_gu.shape[3]
+        eo = self.A_gu.shape[1]
+        self.shared_outer = eo == 1 and E > 1
+        if tuple(self.A_gu.shape) != (L, eo, r, H) or eo not in (1, E) \
+                or tuple(self.A_d.shape) != (L, E, r, I) or tuple(self.B_d.shape) != (L, eo, H, r):
             raise LoraError("inconsistent MoE LoRA shapes")
         self.L, self.E, self.r, self.H, self.I = L, E, r, H, I
         self.dtype = self.A_gu.dtype
-        self.c = lora_moe_weights_t(_dtype_code(self.dtype), L, E, H, I, r, _ptr(self.A_gu),
+        self.c = lora_moe_weights_t(_dtype_code(self.dtype), L, E, H, I, r,
+                                    1 if self.shared_outer else 0, _ptr(self.A_gu),
                                     _ptr(self.B_gu), _ptr(self.A_d), _ptr(self.B_d),
                                     ctypes.cast(_ptr(self.enabled), ctypes.POINTER(ctypes.c_int32)))
 

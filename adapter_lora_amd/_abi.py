@@ -17,7 +17,7 @@ LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
 LORA_TILE_ROWS = 64
-MLORA_ABI_VERSION = 2
+MLORA_ABI_VERSION = 3
 
 
 class LoraError(RuntimeError):
@@ -53,6 +53,7 @@ class lora_segments_t(ctypes.Structure):
 
 class lora_moe_weights_t(ctypes.Structure):
     _fields_ = [("dtype", I32), ("L", I32), ("E", I32), ("H", I32), ("I", I32), ("r", I32),
+                ("shared_outer", I32),
                 ("A_gu", P), ("B_gu", P), ("A_d", P), ("B_d", P), ("adapter_enabled", PI32)]
 
 

@@ -444,6 +444,7 @@ static MoeArgs make_moe(const lora_moe_weights_t* w, int M, int topk, const lora
     MoeArgs a{};
     a.dtype = w->dtype;
     a.L = w->L; a.E = w->E; a.H = w->H; a.I = w->I; a.r = w->r;
+    a.shared_outer = w->shared_outer != 0;
     a.M = M; a.topk = topk;
     a.max_tokens_padded = al->max_tokens_padded;
     a.block_size_m = al->block_size_m;

@@ -131,6 +131,7 @@ hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, f
 struct MoeArgs {
     int dtype;
     int L, E, H, I, r;
+    int shared_outer;   // gate_up A and down B: one slot per adapter, shared by the experts
     int M, topk;
     int max_tokens_padded, block_size_m;
     const void* A_gu;

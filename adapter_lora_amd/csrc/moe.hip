@@ -130,6 +130,12 @@ hipError_t launch_moe_align(const int32_t* topk_ids, const int32_t* ids,
 }
 
 // ---------------------------------------------------------------- deltas
+// Weight slot of adapter l and expert e in a [L, E, ...] stack; an outer
+// (hidden-side) stack shared by the experts has one slot per adapter.
+__device__ __forceinline__ int64_t moe_slot(const MoeArgs& a, bool outer, int l, int e) {
+    return (outer && a.shared_outer) ? (int64_t)l : (int64_t)l * a.E + e;
+}
+
 struct MoeUnit {
     bool ok;
     int e;
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
     __shared__ int s_wlast[kTileWaves];
     const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
-    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const int64_t ew = moe_slot(a, which == 0, l, mu.e);
     const T* A = reinterpret_cast<const T*>(which == 0 ? a.A_gu : a.A_d) + ew * a.r * K;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int rows = a.L * a.max_tokens_padded;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, i
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int lr = lane % 16, lq = lane / 16;
-    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const int64_t ew = moe_slot(a, which == 0, l, mu.e);
     const uint16_t* A = reinterpret_cast<const uint16_t*>(which == 0 ? a.A_gu : a.A_d) +
                         (ew * a.r + cb * 16 + lr) * K;
     const int kw = c * kNarrowK + wave * 256 + lq * 8;     // this lane's first K value
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
     __shared__ int s_wlast[kTileWaves];
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
-    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const int64_t ew = moe_slot(a, which == 1, l, mu.e);
     const T* B = reinterpret_cast<const T*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int n_begin = g * tpw * kNTile;
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4)
     const int l = blk / nblk, b = blk % nblk;
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
-    const int64_t ew = (int64_t)l * a.E + mu.e;
+    const int64_t ew = moe_slot(a, which == 1, l, mu.e);
     const uint16_t* B =
         reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};

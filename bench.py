@@ -59,7 +59,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only", default="",
-                   help="comma list: decode,prefill,qkv,gate_up,moe,lm_head,embedding")
+                   help="comma list: decode,prefill,qkv,gate_up,moe,moe_shared,lm_head,embedding")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -319,7 +319,12 @@ def bench_moe(case, steps, warmup):
              for k in range(case.topk) if case.ids[m] >= 0 and case.adapter_enabled[case.ids[m]]]
     buckets = set(pairs)
     r, H, I = case.rank, case.H, case.I
-    w_bytes = len(buckets) * r * (H + 2 * I + I + H) * es
+    if case.shared_outer:
+        # gate_up A and down B once per adapter; gate_up B and down A per bucket
+        adapters = set(l for l, _ in buckets)
+        w_bytes = len(buckets) * r * (2 * I + I) * es + len(adapters) * r * (H + H) * es
+    else:
+        w_bytes = len(buckets) * r * (H + 2 * I + I + H) * es
     act = len(pairs) * (H + 2 * 2 * I + I + 2 * H) * es
     nbytes = w_bytes + act
     flops = len(pairs) * 2 * r * (H + 2 * I + I + H)
@@ -425,6 +430,9 @@ def main():
                                                        args.warmup, "shrink + reduce + expand")
     if want("moe"):
         results["moe_bf16"] = bench_moe(W.moe_case(0), args.steps, args.warmup)
+    if want("moe_shared"):
+        results["moe_shared_outer_bf16"] = bench_moe(W.moe_case(0, shared_outer=True),
+                                                     args.steps, args.warmup)
     if want("lm_head"):
         results["lm_head_decode_bf16"] = bench_linear(W.lm_head_bf16(0), args.steps, args.warmup,
                                                       "k_decode_fused<uint16_t>",

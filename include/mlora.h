@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLORA_ABI_VERSION 2
+#define MLORA_ABI_VERSION 3
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -348,11 +348,16 @@ lora_status lora_embedding_decode(const lora_weights_t* w, const int32_t* ids,
  * (multiple of 16, <= 64) shared by every adapter; rows past an adapter's
  * true rank are zero.
  *   A_gu [L, E, r, H]   B_gu [L, E, 2I, r]   A_d [L, E, r, I]   B_d [L, E, H, r]
+ * shared_outer != 0 (the page's experts_shared_outer_loras): the outer,
+ * hidden-side stacks have one expert slot shared by every expert,
+ *   A_gu [L, 1, r, H]   B_d [L, 1, H, r],
+ * while B_gu and A_d stay per expert.
  * adapter_enabled device [L]: 0 turns an adapter's deltas off.
  */
 typedef struct lora_moe_weights {
     int32_t dtype;   /* lora_dtype */
     int32_t L, E, H, I, r;
+    int32_t shared_outer;
     const void* A_gu;
     const void* B_gu;
     const void* A_d;

@@ -80,6 +80,13 @@ MOE_CASES = [
     # 32 rows with up to 2 row groups of 16
     ("wide_ragged_bf16", lambda: W.moe_case(7, M=150, H=264, I=4104, E=3, topk=2, L=2, rank=64,
                                             block_size_m=32)),
+    # experts_shared_outer_loras: gate_up A and down B with one expert slot
+    ("cfg5_shared_outer", lambda: W.moe_case(0, shared_outer=True)),
+    ("shared_outer_fp32", lambda: W.moe_case(8, M=40, H=128, I=96, E=4, topk=2, L=3, rank=16,
+                                             block_size_m=16, p_none=0.1, dtype=W.F32,
+                                             shared_outer=True)),
+    ("shared_outer_wide", lambda: W.moe_case(9, M=64, H=264, I=4104, E=6, topk=2, L=2, rank=32,
+                                             block_size_m=16, shared_outer=True)),
 ]
 
 
@@ -96,7 +103,7 @@ def test_moe_stages_and_chain(ml, name, mk):
     ml.lora_moe_gate_up_add(w, x, case.topk, al, c1, ws)
     torch.cuda.synchronize()
     ref1 = O.moe_gate_up_add(case.x.values, case.cache1.values, tid, ids, en, case.A_gu.values,
-                             case.B_gu.values)
+                             case.B_gu.values, case.shared_outer)
     got1 = to_f64(c1)
     assert_close(got1, ref1, dt, case.cache1.values, "gate_up")
     # stage 2 on the oracle's cache1, rounded to the storage dtype
@@ -112,7 +119,7 @@ def test_moe_stages_and_chain(ml, name, mk):
     ml.lora_moe_down_add(w, to_dev(c2_in), case.M, case.topk, al, c3, ws)
     torch.cuda.synchronize()
     ref3 = O.moe_down_add(c2_in.values, case.cache3.values, tid, ids, en, case.A_d.values,
-                          case.B_d.values)
+                          case.B_d.values, case.shared_outer)
     assert_close(to_f64(c3), ref3, dt, case.cache3.values, "down")
     # reduce on the oracle's cache3
     c3_in = store(ref3, dt)
@@ -132,7 +139,7 @@ def test_moe_stages_and_chain(ml, name, mk):
     torch.cuda.synchronize()
     r1 = ref1
     r3 = O.moe_down_add(O.silu_and_mul(r1), case.cache3.values, tid, ids, en, case.A_d.values,
-                        case.B_d.values)
+                        case.B_d.values, case.shared_outer)
     r4 = O.topk_reduce(r3, case.topk_weights.astype(np.float64))
     assert_close(to_f64(out), r4, dt, None, "chain")
 
