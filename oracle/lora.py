@@ -236,3 +236,14 @@ def embedding_add(tokens, ids, A: Sequence, B: Sequence, ranks: Sequence[int], v
         S = _f64(A[i])[:r, t]                  # the lookup: column t of A_i
         y[m] = y[m] + _f64(B[i])[:, :r] @ S
     return y
+
+
+def linear_with_base(x, W, ids, A: Sequence, B: Sequence, ranks: Sequence[int],
+                     slice_sizes: Sequence[int], enabled=None) -> np.ndarray:
+    """The base layer and its LoRA delta together (Ascend walkthrough section
+    1.1: y = x W^T + (x A^T) B^T; SGLang "LoRA Layers" page, structure
+    diagram: base_output + lora_delta).  W is [N_tot, K].  The base product
+    is one float64 matrix product; the delta is lora_linear's per-token loop
+    on top of it."""
+    y_base = _f64(x) @ _f64(W).T
+    return lora_linear(x, ids, A, B, ranks, slice_sizes, y_base, enabled)
