@@ -296,6 +296,21 @@ def lora_shrink_expand_add(table: LoraTable, x: torch.Tensor, seg: Segments, y: 
           "lora_shrink_expand_add")
 
 
+def lora_linear_fused(table: LoraTable, W: torch.Tensor, x: torch.Tensor, seg: Segments,
+                      y: torch.Tensor, ws: Workspace, stream=None) -> None:
+    """y = x W^T + (x A_i^T) B_i^T per token (bf16), y overwritten; W is the
+    base weight [N, K] with the table's slices stacked in order."""
+    ldw, ldx, ldy = _rows(W, "W"), _rows(x, "x"), _rows(y, "y")
+    if x.shape[0] != y.shape[0]:
+        raise LoraError("x and y must have the same number of rows")
+    if W.shape[0] != table.N:
+        raise LoraError("W must have one row per output column of the table")
+    check(lib.lora_linear_fused(ctypes.byref(table.c), _ptr(W), ldw, _ptr(x), ldx, x.shape[0],
+                                ctypes.byref(seg.c), _ptr(y), ldy, _ptr(ws.buf), ws.buf.numel(),
+                                stream_handle(stream)),
+          "lora_linear_fused")
+
+
 def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: torch.Tensor,
                       ws: Workspace, seg: Optional[Segments] = None,
                       adapter_enabled: Optional[torch.Tensor] = None, stream=None) -> None:

@@ -17,7 +17,7 @@ LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
 LORA_TILE_ROWS = 64
-MLORA_ABI_VERSION = 3
+MLORA_ABI_VERSION = 4
 
 
 class LoraError(RuntimeError):
@@ -81,6 +81,7 @@ SIGNATURES = {
     "lora_shrink": (I32, [PW, P, I64, I32, PS, P, P, SZ, P]),
     "lora_expand_add": (I32, [PW, P, I32, PS, P, I64, P]),
     "lora_shrink_expand_add": (I32, [PW, P, I64, I32, PS, P, I64, P, SZ, P]),
+    "lora_linear_fused": (I32, [PW, P, I64, P, I64, I32, PS, P, I64, P, SZ, P]),
     "lora_fused_decode": (I32, [PW, P, P, P, I64, I32, P, I64, P, P, P, P, P, P, P, I32, P, SZ,
                                 P]),
     "lora_pack_embedding_adapter": (I32, [I32, I32, I64, I32, I32, P, P, P, P, P]),

@@ -294,6 +294,30 @@ lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64
     return from_hip(launch_expand(a, S, y, ldy, stream));
 }
 
+lora_status lora_linear_fused(const lora_weights_t* w, const void* W, int64_t ldw,
+                              const void* x, int64_t ldx, int32_t M, const lora_segments_t* seg,
+                              void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    lora_status st = check_weights(w);
+    if (st != LORA_OK) return st;
+    if (w->dtype != LORA_BF16) return LORA_UNSUPPORTED;
+    if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
+    if ((st = check_segments(seg, w, M)) != LORA_OK) return st;
+    if (M == 0) return LORA_OK;
+    if ((st = check_rows(W, ldw, w->K)) != LORA_OK) return st;
+    if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
+    if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+        return LORA_INVALID_ARG;
+    const LinearWs L = layout_for(w, M);
+    if (workspace_bytes < L.total) return LORA_INVALID_ARG;
+    const LinearArgs a = make_args(w, seg, M);
+    float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.S);
+    hipError_t e = launch_shrink(a, x, ldx, S, workspace, stream);
+    if (e != hipSuccess) return LORA_HIP_ERROR;
+    return from_hip(launch_gemm_lora(a, x, ldx, W, ldw, S, y, ldy, stream));
+}
+
 lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
                               const int32_t* adapter_enabled, const void* x, int64_t ldx,
                               int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,

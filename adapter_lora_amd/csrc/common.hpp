@@ -104,6 +104,19 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// bf16 MFMA, 32 x 32 output, K = 16 (v_mfma_f32_32x32x16_bf16).  Lane l
+// supplies row (l % 32) of the first operand and column (l % 32) of the
+// second, eight consecutive K values starting at 8 * (l / 32) for both; it
+// receives rows 8 * (q / 4) + 4 * (l / 32) + q % 4, q = 0..15, of column
+// l % 32 of the result.  One wave issuing these back to back keeps the matrix
+// unit busy; the 16 x 16 form needs two waves per SIMD for that.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(const uint4& a, const uint4& b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // ----------------------------------------------------------------------------
 // wavefront reductions
 // ----------------------------------------------------------------------------

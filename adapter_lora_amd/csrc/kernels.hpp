@@ -122,6 +122,10 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st);
 
+// y = x W^T + S B_i^T per row tile (bf16 MFMA; S fp32 [M][cols], sorted rows).
+hipError_t launch_gemm_lora(const LinearArgs& a, const void* x, int64_t ldx, const void* W,
+                            int64_t ldw, const float* S, void* y, int64_t ldy, hipStream_t st);
+
 // Embedding lookup: S (fp32 [M][r_max], sorted rows) = rows of the
 // transposed A table selected by token id (a.K is the vocabulary).
 hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, float* S,

@@ -59,7 +59,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--only", default="",
-                   help="comma list: decode,prefill,qkv,gate_up,moe,moe_shared,lm_head,embedding")
+                   help="comma list: decode,prefill,qkv,gate_up,moe,moe_shared,lm_head,embedding,"
+                        "linear_fused")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -252,6 +253,63 @@ def bench_linear(case, steps, warmup, fused_kernel_name, single_launch=False):
     return res
 
 
+# ----------------------------------------------------------------------------- base + delta
+def bench_linear_fused(case, steps, warmup):
+    """The base layer fused with its delta on the prefill batch: step =
+    lora_linear_fused (lora_shrink, then one MFMA product whose epilogue adds
+    S B^T), segment table prebuilt.  FLOPs: 2 M K N for the base plus the
+    delta's.  Context: the unfused form, torch.matmul (hipBLASLt) for the base
+    product followed by lora_shrink_expand_add, and torch.matmul alone."""
+    import torch
+    import adapter_lora_amd as ml
+    import workloads as W
+    _, dflops, m_valid, touched = linear_bytes_flops(case)
+    flops = 2.0 * case.M * case.K * case.N + dflops
+    Wt = dev_tensor(W.base_weight(0, case.N, case.K))
+    per_copy = (case.N * case.K + case.M * case.K + case.M * case.N) * 2
+    R = max(2, int(np.ceil(2 * MALL_BYTES / per_copy)))
+    A = [dev_tensor(a) for a in case.A]
+    B = [dev_tensor(b) for b in case.B]
+    table = ml.LoraTable(A, B, case.ranks, case.slice_sizes, case.K, torch.bfloat16)
+    ids = torch.from_numpy(case.ids).cuda()
+    seg = ml.Segments(case.M, case.L)
+    ml.lora_build_segments(ids, seg)
+    copies = [(Wt if r == 0 else Wt.clone(), dev_tensor(case.x),
+               torch.empty((case.M, case.N), dtype=torch.bfloat16, device="cuda"))
+              for r in range(R)]
+    ws = ml.Workspace.for_table(table, case.M)
+    torch.cuda.synchronize()
+
+    def fused(i):
+        w, x, y = copies[i % R]
+        ml.lora_linear_fused(table, w, x, seg, y, ws)
+
+    def unfused(i):
+        w, x, y = copies[i % R]
+        torch.matmul(x, w.t(), out=y)
+        ml.lora_shrink_expand_add(table, x, seg, y, ws)
+
+    def base_only(i):
+        w, x, y = copies[i % R]
+        torch.matmul(x, w.t(), out=y)
+
+    ms_step, _ = run_timed(fused, steps, warmup)
+    ms_unfused, _ = run_timed(unfused, steps, warmup)
+    ms_base, _ = run_timed(base_only, steps, warmup)
+    res = {
+        "ms_per_step": ms_step, "ms_unfused_matmul_plus_delta": ms_unfused,
+        "ms_matmul_base_only": ms_base, "M": case.M, "m_valid": m_valid,
+        "adapters_touched": touched, "alg_flops": flops, "rotation_copies": R,
+        "kernel": "k_shrink_dense + k_reduce_partials + k_gemm_lora",
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "tokens_per_s": case.M / (ms_step * 1e-3),
+    }
+    res["mfma_frac"] = res["tflops"] / BF16_MFMA_PEAK_TFLOPS
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- embedding
 def bench_embedding(case, steps, warmup):
     """Embedding LoRA on a decode batch: step = lora_embedding_decode, one
@@ -437,6 +495,9 @@ def main():
         results["lm_head_decode_bf16"] = bench_linear(W.lm_head_bf16(0), args.steps, args.warmup,
                                                       "k_decode_fused<uint16_t>",
                                                       single_launch=True)
+    if want("linear_fused"):
+        results["prefill_base_fused_bf16"] = bench_linear_fused(W.prefill_bf16(0), args.steps,
+                                                                args.warmup)
     if want("embedding"):
         results["embedding_decode_bf16"] = bench_embedding(W.embedding_bf16(0), args.steps,
                                                            args.warmup)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLORA_ABI_VERSION 3
+#define MLORA_ABI_VERSION 4
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -246,6 +246,27 @@ lora_status lora_expand_add(const lora_weights_t* w, const float* S, int32_t M,
 lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64_t ldx,
                                    int32_t M, const lora_segments_t* seg, void* y, int64_t ldy,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lora_linear_fused: the base layer and its LoRA delta written together
+ * (Ascend walkthrough s1.1, the layer output x W^T + (x A^T) B^T; SGLang
+ * "LoRA Layers" page, structure diagram: base output plus LoRA delta):
+ *     y[m, n] = sum_k x[m, k] W[n, k] + sum_{j < rp} S[p, sl, j] B_i[n, j]
+ * for every token m (sorted position p, adapter i, slice sl holding n); the
+ * delta term is absent for tokens without an adapter and for rank-0 slots.
+ * Two launches: lora_shrink into `workspace`, then one bf16 MFMA product
+ * whose epilogue adds S B_i^T before the single bf16 rounding of y.
+ * W  device bf16 [n_total, ldw] row-major (row n = output column n, the
+ *    slices of w stacked in order); ldw >= K, ldw % 8 == 0, 16-byte aligned.
+ * x  device bf16 [M, ldx]; y device bf16 [M, ldy], overwritten (never read).
+ * seg  segment table of the batch (lora_build_segments).
+ * workspace  lora_workspace_size(w, M) bytes, as lora_shrink.
+ * Only bf16 tables: LORA_UNSUPPORTED for fp32.
+ */
+lora_status lora_linear_fused(const lora_weights_t* w, const void* W, int64_t ldw,
+                              const void* x, int64_t ldx, int32_t M, const lora_segments_t* seg,
+                              void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * lora_fused_decode: the whole decode path in one kernel launch (Ascend

@@ -249,6 +249,16 @@ def integer_linear(seed: int, M: int, K: int, slice_sizes, ranks, dtype: str) ->
                       x, A, B, y)
 
 
+def base_weight(seed: int, N: int, K: int, dtype: str = BF16, std: float = 0.02,
+                integer: bool = False) -> Tensor:
+    """Base layer weight W [N, K] (row n = output column n), N(0, std^2), or
+    values in {-1, 0, 1} for the exact-arithmetic cases."""
+    rng = np.random.default_rng([seed, 11])
+    if integer:
+        return make_tensor(rng.integers(-1, 2, size=(N, K)).astype(np.float32), dtype)
+    return make_tensor(rng.standard_normal((N, K), dtype=np.float32) * std, dtype)
+
+
 # ----------------------------------------------------------------------------
 # embedding and LM-head LoRA (SGLang "LoRA Layers" page: the embedding's A
 # side is a lookup of A (r, vocab), its B is (emb, r); the LM head is a dense
