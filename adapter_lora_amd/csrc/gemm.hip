@@ -28,7 +28,8 @@
 // Epilogue: for each segment that meets the unit's rows (and has a nonzero
 // rank), the unit's S rows of that segment are staged in LDS as a bf16
 // hi / lo pair (zero elsewhere) and multiplied with the adapter's B rows on
-// the same MFMA blocks; then one bf16 rounding and the store by token index.
+// the same MFMA blocks; then one bf16 rounding, staged through LDS so that
+// each output row is written in 16-byte pieces by token index.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,6 +47,7 @@ constexpr int kGXL = kGM / 32;           // x rows loaded per thread and stage
 constexpr int kGWL = kGN / 32;           // W rows loaded per thread and stage
 constexpr int kSLD = LORA_MAX_RANK + 8;  // bf16 row stride of the staged S
 static_assert(kGM * kSLD * 2 * 2 <= kGRing * kGStage * 16, "staged S must fit the ring");
+static_assert(4 * kGM * 72 * 2 <= kGRing * kGStage * 16, "staged output must fit the ring");
 
 // Position of 16-byte chunk c of row r (rows of 128 bytes): the chunk is
 // permuted by (r ^ (r / 8)) % 8, which gives 8 consecutive rows distinct
@@ -274,20 +276,30 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
         }
     }
 
-    // ---- store: acc[rb][cb][q] is row 32 rb + 8 (q / 4) + 4 lh + q % 4,
-    // column 64 w + 32 cb + lr
+    // ---- store through LDS (the ring is free: every wave has passed the last
+    // barrier): each wave stages its 128 x 64 block as bf16, rows of 72
+    // values, then writes whole 16-byte row pieces.  acc[rb][cb][q] is row
+    // 32 rb + 8 (q / 4) + 4 lh + q % 4, column 64 w + 32 cb + lr.  A wave reads
+    // back only what it wrote itself, so no barrier is needed.
+    {
+        constexpr int OLD = 72;
+        uint16_t* so = reinterpret_cast<uint16_t*>(smem) + wave * kGM * OLD;
 #pragma unroll
-    for (int rb = 0; rb < kGRB; ++rb) {
+        for (int rb = 0; rb < kGRB; ++rb)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int m = s_tok[rb * 32 + (q / 4) * 8 + lh * 4 + q % 4];
-            if (m < 0) continue;
-            uint16_t* yr = p.y + (int64_t)m * p.ldy;
+            for (int cb = 0; cb < kGCB; ++cb)
 #pragma unroll
-            for (int cb = 0; cb < kGCB; ++cb) {
-                const int n = n0 + wave * 64 + cb * 32 + lr;
-                if (n < n1) yr[n] = (uint16_t)f32_to_bf16(acc[rb][cb][q]);
-            }
+                for (int q = 0; q < 16; ++q)
+                    so[(rb * 32 + (q / 4) * 8 + lh * 4 + q % 4) * OLD + cb * 32 + lr] =
+                        (uint16_t)f32_to_bf16(acc[rb][cb][q]);
+        const int c = lane % 8;
+        const int n = n0 + wave * 64 + c * 8;       // slices are multiples of 8 wide
+#pragma unroll
+        for (int j = 0; j < kGM / 8; ++j) {
+            const int row = j * 8 + lane / 8;
+            const int m = s_tok[row];
+            const uint4 v = *reinterpret_cast<const uint4*>(so + row * OLD + c * 8);
+            if (m >= 0 && n < n1) *reinterpret_cast<uint4*>(p.y + (int64_t)m * p.ldy + n) = v;
         }
     }
 }
