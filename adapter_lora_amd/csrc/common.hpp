@@ -108,8 +108,9 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
 // supplies row (l % 32) of the first operand and column (l % 32) of the
 // second, eight consecutive K values starting at 8 * (l / 32) for both; it
 // receives rows 8 * (q / 4) + 4 * (l / 32) + q % 4, q = 0..15, of column
-// l % 32 of the result.  One wave issuing these back to back keeps the matrix
-// unit busy; the 16 x 16 form needs two waves per SIMD for that.
+// l % 32 of the result.  Issued back to back from one wave per SIMD on 2-8
+// accumulators, this form kept the matrix unit near its peak in a probe; the
+// 16 x 16 form on 4-16 accumulators did not (0.9-1.5 PFLOP/s).
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16_t mfma32_bf16(const uint4& a, const uint4& b, f32x16_t c) {
