@@ -133,6 +133,21 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < kGWL; ++i) st[kGM * 8 + gsw(tr + 32 * i, tc)] = rs[slot][kGXL + i];
     };
+    // one load or one LDS write of the twelve per thread and stage
+    // (i < 4: x rows, else W rows); `i` is a literal at every call
+    auto gload1 = [&](int s, int slot, int i) {
+        rs[slot][i] = ld16((i < kGXL ? xrow[i] : wrow[i - kGXL]) + kx(s));
+    };
+    auto lstore1 = [&](int s, int slot, int i) {
+        uint4* st = smem + (s % kGRing) * kGStage;
+        if (i < kGXL) {
+            const uint32_t m = opaque_mask(s * kGK + tc * 8 < K);
+            const uint4 v = rs[slot][i];
+            st[gsw(tr + 32 * i, tc)] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+        } else {
+            st[kGM * 8 + gsw(tr + 32 * (i - kGXL), tc)] = rs[slot][i];
+        }
+    };
     // MFMA operands of K step t (16 wide) of stage s
     struct Ops {
         uint4 a[kGRB];
@@ -149,6 +164,13 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
         return o;
     };
 
+    // one of the six operand reads of K step t (j < 4: x rows, else W rows)
+    auto oread1 = [&](Ops& o, int s, int t, int j) {
+        const uint4* st = smem + (s % kGRing) * kGStage;
+        if (j < kGRB) o.a[j] = st[gsw(j * 32 + lr, 2 * t + lh)];
+        else o.b[j - kGRB] = st[kGM * 8 + gsw(wave * 64 + (j - kGRB) * 32 + lr, 2 * t + lh)];
+    };
+
     f32x16_t acc[kGRB][kGCB];
 #pragma unroll
     for (int rb = 0; rb < kGRB; ++rb)
@@ -156,11 +178,9 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
         for (int cb = 0; cb < kGCB; ++cb)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[rb][cb][q] = 0.f;
-    auto mfmas = [&](const Ops& o) {
-#pragma unroll
-        for (int rb = 0; rb < kGRB; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < kGCB; ++cb) acc[rb][cb] = mfma32_bf16(o.a[rb], o.b[cb], acc[rb][cb]);
+    auto mfma1 = [&](const Ops& o, int i) {
+        const int rb = i / kGCB, cb = i % kGCB;
+        acc[rb][cb] = mfma32_bf16(o.a[rb], o.b[cb], acc[rb][cb]);
     };
 
     // prologue: stages 0 and 1 in LDS, stages 2 and 3 in flight, the first
@@ -176,26 +196,43 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
 
     // stage ks; `slot` (ks & 1) is a literal at every call.  The ring slot of
     // stage ks + 2 was last read (stage ks - 1) before the previous barrier;
-    // stage ks + 1 was written a stage ago, before that barrier.
+    // stage ks + 1 was written a stage ago, before that barrier.  With one
+    // wave per SIMD, anything issued between MFMAs would leave the matrix
+    // unit idle, so each MFMA (32 cycles) is followed by at most one LDS write
+    // or one global load, and one operand read for the next K step, in a
+    // fixed order: the writes of stage ks + 2 during the first two K steps,
+    // the loads of stage ks + 4 (into the registers just written out) during
+    // the last two.
     auto step = [&](int ks, int slot) {
-        Ops o1 = oread(ks, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(o0);
-        __builtin_amdgcn_sched_barrier(0);
-        Ops o2 = oread(ks, 2);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(o1);
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(ks + 2, slot);
-        gload(ks + 4, slot);
-        Ops o3 = oread(ks, 3);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(o2);
-        __builtin_amdgcn_sched_barrier(0);
-        o0 = oread(ks + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(o3);
-        __builtin_amdgcn_sched_barrier(0);
+        Ops o1, o2, o3;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mfma1(o0, i);
+            if (i < 6) oread1(o1, ks, 1, i);
+            if (i < 6) lstore1(ks + 2, slot, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mfma1(o1, i);
+            if (i < 6) oread1(o2, ks, 2, i);
+            if (i < 6) lstore1(ks + 2, slot, 6 + i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mfma1(o2, i);
+            if (i < 6) oread1(o3, ks, 3, i);
+            if (i < 6) gload1(ks + 4, slot, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mfma1(o3, i);
+            if (i < 6) oread1(o0, ks + 1, 0, i);
+            if (i < 6) gload1(ks + 4, slot, 6 + i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __syncthreads();
     };
     for (int ks = 0; ks < p.nk2; ks += 2) {
