@@ -48,6 +48,7 @@ struct DecodeParams {
     const int32_t* enabled;  // adapter mask for that grouping (may be null)
     SegOut out;              // segment table written by the last workgroup (ids mode)
     int writer;              // 1 when the last workgroup writes `out`
+    int by_slot;             // ids mode with L <= M: unit s is adapter slot s (see slot_head)
     const int32_t* tokens;   // non-null: embedding lookup, S rows read from the
                              // transposed A table by token id (a.K = vocab); no producers
 };
@@ -157,6 +158,37 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
     return v;
 }
 
+// Slot mode (ids mode with L <= M, so that there is a unit for every slot):
+// unit s serves adapter slot s rather than the s-th segment.  Its rank and
+// weight offset are then two scalar loads issued together with the ids, and
+// once both are in, one ballot over the token buckets tells whether any
+// token uses the slot; the weight loads are issued before the grouping is
+// computed, which afterwards gives the slot's token rows.
+__device__ __forceinline__ SegView slot_head(const ViewArgs& va, int s) {
+    SegView v{};
+    v.id = s;
+    v.rp = va.rank[s];
+    v.off = va.offs[s];
+    return v;
+}
+
+// Whether any of the batch's tokens (bucket b of lane m < M) uses slot s.
+__device__ __forceinline__ bool slot_used(int b, int M, int s) {
+    return __ballot(lane_id() < M && b == s) != 0ull;
+}
+
+// The grouping part of slot s's view: sorted token order (my_idx), and the
+// first sorted position and count of the slot's tokens.
+__device__ __forceinline__ void slot_group(int b, int M, int L, SegView& v) {
+    const int lane = lane_id();
+    const WaveGroups g = wave_group(b, M, L);
+    const bool valid = lane < M;
+    v.my_idx = g.key & 63;
+    v.p0 = __popcll(__ballot(valid && b < v.id));
+    v.ms = __popcll(__ballot(valid && b == v.id));
+    v.nseg = g.nseg;
+}
+
 // ---------------------------------------------------------------- producers
 // Unit = (segment, 16 rows of A, K chunk of 512 x dec_steps values).  Wave w owns rows
 // 4w..4w+3; per step a lane loads 8 consecutive K values of each row (one
@@ -232,8 +264,17 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
     const int s = unit / per_s;
     const int jb = (unit % per_s) / p.C;
     const int c = unit % p.C;
-    const SegView v = seg_view(p, va, s);
-    if (s >= v.nseg || v.id < 0) return;
+    SegView v;
+    int b = 0;
+    if (p.by_slot) {
+        const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
+        v = slot_head(va, s);
+        b = token_bucket(tl, p.enabled, va.L);
+        if (!slot_used(b, va.M, s)) return;
+    } else {
+        v = seg_view(p, va, s);
+        if (s >= v.nseg || v.id < 0) return;
+    }
     const int nb = v.rp / 16;
     if (nb == 0 || jb >= nb * a.n_sl) return;
     const int sl = jb / nb, jj = jb % nb;
@@ -252,6 +293,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
             ar[st][i] = ld_raw8_if(A + (int64_t)i * a.K + k, k < a.K, A);
         }
     }
+    if (p.by_slot) slot_group(b, va.M, va.L, v);
     const T* X = reinterpret_cast<const T*>(p.x);
     const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += kTokGroup) {
@@ -305,8 +347,17 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
     const int s = unit / per_s;
     const int jb = (unit % per_s) / p.C;
     const int c = unit % p.C;
-    const SegView v = seg_view(p, va, s);
-    if (s >= v.nseg || v.id < 0) return;
+    SegView v;
+    int b = 0;
+    if (p.by_slot) {
+        const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
+        v = slot_head(va, s);
+        b = token_bucket(tl, p.enabled, va.L);
+        if (!slot_used(b, va.M, s)) return;
+    } else {
+        v = seg_view(p, va, s);
+        if (s >= v.nseg || v.id < 0) return;
+    }
     const int nb = v.rp / 16;
     if (nb == 0 || jb >= nb * a.n_sl) return;
     const int sl = jb / nb, jj = jb % nb;
@@ -320,6 +371,7 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
     uint4 av[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < a.K, A);
+    if (p.by_slot) slot_group(b, va.M, va.L, v);
     const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += 16) {
         const int nt = min(16, v.ms - t0);
@@ -353,7 +405,7 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
 constexpr int kPollBatch = 8;    // exchange slots polled together
 
 template <typename T, int RCAP>
-__device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView& v, int tile,
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, int b, int tile,
                                             int n0, int n1, uint4* lds) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
@@ -373,6 +425,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, const SegView
     uint4 brow[CPR];
 #pragma unroll
     for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
+    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
     float yv[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
@@ -543,19 +596,28 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
     const int u = blockIdx.x - p.grid1;
     const int s = u / p.n_tiles;
     const int t = u % p.n_tiles;
-    const SegView v = seg_view(p, ViewArgs{ids, rank, b_off, M, L, p.tokens,
-                                           p.tokens ? a_off : nullptr}, s);
-    if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
+    const ViewArgs va{ids, rank, b_off, M, L, p.tokens, p.tokens ? a_off : nullptr};
+    SegView v;
+    int b = 0;
+    if (p.by_slot) {
+        const TokenLoad tl = load_token(ids, p.enabled, M, L);
+        v = slot_head(va, s);
+        b = token_bucket(tl, p.enabled, L);
+        if (v.rp == 0 || !slot_used(b, M, s)) return;
+    } else {
+        v = seg_view(p, va, s);
+        if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
+    }
     int sl = 0;
     while (sl + 1 < a.n_sl && t >= p.tile_start[sl + 1]) ++sl;
     const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
     const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
     if (v.rp <= 16)
-        dec_consume<T, 16>(p, v, t, n0, n1, lds);
+        dec_consume<T, 16>(p, v, b, t, n0, n1, lds);
     else if (v.rp <= 32)
-        dec_consume<T, 32>(p, v, t, n0, n1, lds);
+        dec_consume<T, 32>(p, v, b, t, n0, n1, lds);
     else
-        dec_consume<T, 64>(p, v, t, n0, n1, lds);
+        dec_consume<T, 64>(p, v, b, t, n0, n1, lds);
 }
 
 static hipError_t launch_decode(DecodeParams& p, unsigned grid, hipStream_t st) {
@@ -613,6 +675,7 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     p.ldx = ldx;
     p.y = y;
     p.ldy = ldy;
+    p.by_slot = (ids && a.L <= a.s_max) ? 1 : 0;
     const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.r_max, ntiles_total(a));
     char* base = reinterpret_cast<char*>(ws);
     p.err = reinterpret_cast<int*>(base + L.header);
