@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
-              "lora_fused_decode",
+              "lora_fused_decode", "lora_linear_fused",
               "lora_moe_align_run", "lora_moe_gate_up_add", "lora_moe_silu_and_mul",
               "lora_moe_down_add", "lora_moe_topk_reduce", "lora_workspace_size",
               "lora_status_string", "lora_read_device_error", "lora_table_plan",
@@ -98,6 +98,23 @@ def test_argument_checks_fail_before_any_launch():
                                  null, null, null, null, null, null, 8, null, 0, null) == INV
     assert lib.lora_fused_decode(ctypes.byref(w2), null, null, null, 128, 8, null, 128, *args, 0,
                                  null, 0, null) == INV                            # ids null
+    # fused base GEMM: fp32 tables are not on this path; a null base weight
+    # or a short workspace is rejected before any launch
+    w2.dtype = 0
+    assert lib.lora_linear_fused(ctypes.byref(w2), some, 128, some, 128, 8, None, some, 128,
+                                 some, 1 << 20, null) == _abi.LORA_UNSUPPORTED
+    w2.dtype = 1
+    seg = _abi.lora_segments_t()
+    for f in ("sorted_idx", "seg_indptr", "req_to_lora", "num_segments", "tile_info",
+              "tile_rows", "num_tiles"):
+        setattr(seg, f, ctypes.cast(some, ctypes.POINTER(ctypes.c_int32)))
+    seg.L, seg.max_tiles = 4, 8
+    assert lib.lora_linear_fused(ctypes.byref(w2), null, 128, some, 128, 8, ctypes.byref(seg),
+                                 some, 128, some, 1 << 20, null) == INV      # W null
+    assert lib.lora_linear_fused(ctypes.byref(w2), some, 120, some, 128, 8, ctypes.byref(seg),
+                                 some, 128, some, 1 << 20, null) == INV      # ldw < K
+    assert lib.lora_linear_fused(ctypes.byref(w2), some, 128, some, 128, 8, ctypes.byref(seg),
+                                 some, 128, some, 16, null) == INV           # workspace short
     ma = _abi.lora_moe_align_t()
     ma.max_tokens_padded, ma.block_size_m = 100, 64               # not a multiple of the block
     assert lib.lora_moe_align_run(null, null, null, 4, 2, 8, 2, ctypes.byref(ma), null) == INV

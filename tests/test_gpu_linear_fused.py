@@ -32,11 +32,12 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_fused(ml, case, Wt):
+def run_fused(ml, case, Wt, enabled=None):
     table = table_for(case)
     ids = torch.from_numpy(case.ids).cuda()
     seg = ml.Segments(case.M, case.L)
-    ml.lora_build_segments(ids, seg)
+    en = None if enabled is None else torch.from_numpy(enabled).cuda()
+    ml.lora_build_segments(ids, seg, adapter_enabled=en)
     x = to_dev(case.x)
     y = torch.full((case.M, case.N), float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = ml.Workspace.for_table(table, case.M)
@@ -114,6 +115,26 @@ def test_linear_fused_integer_exact(ml):
                              [b.values for b in case.B], case.ranks, case.slice_sizes)
     assert np.max(np.abs(ref)) <= 256
     assert np.array_equal(got, ref)
+
+
+def test_linear_fused_with_enable_mask(ml):
+    """Disabled adapters (segment table built with a mask) give their tokens
+    the base product only."""
+    case = W.random_linear(47, 200, 512, [384], [16, 64, 32, 48, 16], W.BF16)
+    enabled = np.array([1, 0, 1, 0, 1], np.int32)
+    Wt = W.base_weight(47, case.N, case.K)
+    log(f"linear_fused masked M={case.M} K={case.K}")
+    got = run_fused(ml, case, Wt, enabled)
+    ref = O.linear_with_base(case.x.values, Wt.values, case.ids, [a.values for a in case.A],
+                             [b.values for b in case.B], case.ranks, case.slice_sizes, enabled)
+    scale = float(np.max(np.abs(ref)))
+    assert float(np.max(np.abs(got - ref))) <= TOL_BF16 * scale
+    gamma = 2.0 * (case.K + 64) * 2.0 ** -24
+    masked = W.LinearCase(case.name, case.dtype, case.M, case.K, case.slice_sizes, case.ranks,
+                          O.mask_ids(case.ids, enabled, case.L).astype(np.int32), case.x,
+                          case.A, case.B, case.y_base)
+    bound = 2.0 ** -8 * np.abs(ref) + gamma * abs_bound(masked, Wt)
+    assert not (np.abs(got - ref) > bound).any()
 
 
 def test_linear_fused_prefill_full_size(ml):
