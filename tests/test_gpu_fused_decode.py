@@ -107,7 +107,9 @@ def test_fused_decode_with_enable_mask(ml, name, mk):
 
 def test_fused_decode_large_table(ml):
     """L = 300 slots: the mask and the rank / offset tables are read by id
-    (the path for tables of more than 256 slots)."""
+    (the path for tables of more than 256 slots), and with L > M the units
+    are numbered by segment; every other case here has L <= M, where each
+    unit serves one adapter slot."""
     ranks = [16, 0, 32, 64, 8, 48] * 50
     case = W.random_linear(23, 48, 256, [136], ranks, W.BF16, p_none=0.1)
     case.ids[:] = np.random.default_rng(5).integers(-1, 300, size=48).astype(np.int32)
