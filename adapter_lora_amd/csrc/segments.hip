@@ -22,7 +22,7 @@
 
 namespace mlora {
 
-constexpr int kSegThreads = 512;
+constexpr int kSegThreads = 1024;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kCachedTiles = 8;
 
@@ -64,12 +64,33 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
         if (m < M) b = bucket_of(ids[m]);
         bk[i] = b;
     }
+    const int nbits = 32 - __clz(L);          // enough bits for buckets 0..L
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    // lanes of this wavefront (with a token) whose bucket equals b: one
+    // ballot per bucket bit
+    auto peers_of = [&](int b, bool act) {
+        unsigned long long pe = __ballot(act);
+        for (int i = 0; i < nbits; ++i) {
+            const bool bit = (b >> i) & 1;
+            const unsigned long long bb = __ballot(bit);
+            pe &= bit ? bb : ~bb;
+        }
+        return pe;
+    };
+    // histogram: one LDS atomic per distinct bucket and wavefront (a batch
+    // of contiguous segments gives most wavefronts a single bucket)
+    auto count_tile = [&](int t0, int b) {
+        const bool act = t0 + tid < M;
+        const unsigned long long pe = peers_of(b, act);
+        if (act && __popcll(pe & lt) == 0) atomicAdd(&count[b], __popcll(pe));
+    };
 #pragma unroll
-    for (int i = 0; i < kCachedTiles; ++i)
-        if (i * kSegThreads + tid < M) atomicAdd(&count[bk[i]], 1);
-    for (int m = kCachedTiles * kSegThreads + tid; m < M; m += kSegThreads) {
-        atomicAdd(&count[bucket_of(ids[m])], 1);
+    for (int i = 0; i < kCachedTiles; ++i) {
+        if (i * kSegThreads >= M) break;
+        count_tile(i * kSegThreads, bk[i]);
     }
+    for (int t0 = kCachedTiles * kSegThreads; t0 < M; t0 += kSegThreads)
+        count_tile(t0, t0 + tid < M ? bucket_of(ids[t0 + tid]) : L);
     __syncthreads();
 
     if (wave == 0) {
@@ -145,25 +166,20 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
         }
     }
 
-    const int nbits = 32 - __clz(L);          // enough bits for buckets 0..L
-    const unsigned long long lt = (1ull << lane) - 1ull;
     // one tile of kSegThreads tokens in token order; b = this thread's bucket
     auto scatter_tile = [&](int t0, int b) {
         const int m = t0 + tid;
         const bool act = m < M;
-        unsigned long long peers = __ballot(act);
-        for (int i = 0; i < nbits; ++i) {
-            const bool bit = (b >> i) & 1;
-            const unsigned long long bb = __ballot(bit);
-            peers &= bit ? bb : ~bb;
-        }
+        const unsigned long long peers = peers_of(b, act);
         const int rank_w = __popcll(peers & lt);
         const bool leader = act && rank_w == 0;
         if (leader) wcnt[wave * NB + b] = __popcll(peers);
         __syncthreads();
         if (act) {
+            // earlier wavefronts' tokens of the bucket (all reads issued together)
             int pos = base[b] + rank_w;
-            for (int w = 0; w < wave; ++w) pos += wcnt[w * NB + b];
+#pragma unroll
+            for (int w = 0; w < kSegWaves; ++w) pos += w < wave ? wcnt[w * NB + b] : 0;
             sorted_idx[pos] = m;
             if (b < L) {
                 const int rel = pos - bstart[b];
