@@ -2,6 +2,9 @@
 
   python rocprof_summary.py stats DIR "COMMAND" > profiles/<kernel>_<workload>.md
       per-kernel duration table from DIR's *_kernel_stats.csv
+  python rocprof_summary.py mfma DIR "COMMAND" > profiles/<workload>_mfma.md
+      per-kernel MFMA work and utilisation from one counter run of
+      SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
   python rocprof_summary.py traffic FETCH_DIR WRITE_DIR "FETCH_CMD" "WRITE_CMD" [WORKGROUPS] \\
       > profiles/decode_fused_traffic.md
       HBM bytes per launch of the fused decode kernel (only the dispatches with
@@ -104,6 +107,42 @@ def traffic(fetch_dir, write_dir, fetch_cmd, write_cmd, workgroups=None):
     print(f"- source_hash: `{bench.source_hash(bench.DECODE_SOURCES)}`")
 
 
+N_XCD = 8            # GRBM_GUI_ACTIVE is summed over the XCDs
+N_SIMD = 256 * 4     # SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs
+MOPS_FLOP = 512      # one MFMA MOP of SQ_INSTS_VALU_MFMA_MOPS_BF16
+
+
+def mfma(directory, command):
+    rows = _rows(directory, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        key = (short(r["Kernel_Name"]), r["Dispatch_Id"])
+        per.setdefault(key, {})
+        per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + \
+            float(r["Counter_Value"])
+    kern = {}
+    for (name, _), c in per.items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in c or c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0:
+            continue
+        kern.setdefault(name, []).append(c)
+    print("# MFMA work and utilisation per kernel\n")
+    print(f"Counter run (from /tmp, `TMPDIR=/tmp`):\n\n```\n{command}\n```\n")
+    print(f"FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x {MOPS_FLOP}.  Busy = "
+          f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCD} x {N_SIMD} SIMDs): the share "
+          "of the kernel's cycles in which the matrix units were busy.  Clock = "
+          "GRBM_GUI_ACTIVE per XCD over the same cycles, reported as cycles per dispatch.\n")
+    print("| kernel | dispatches | GFLOP / dispatch | cycles / dispatch (per XCD) | MFMA busy % |")
+    print("|---|---:|---:|---:|---:|")
+    for name, cs in sorted(kern.items(), key=lambda kv: -sum(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+                                                             for c in kv[1])):
+        n = len(cs)
+        flop = sum(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for c in cs) / n * MOPS_FLOP
+        gui = sum(c.get("GRBM_GUI_ACTIVE", 0.0) for c in cs) / n / N_XCD
+        busy = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for c in cs) / n
+        pct = 100.0 * busy / (gui * N_SIMD) if gui else float("nan")
+        print(f"| `{name}` | {n} | {flop / 1e9:.3f} | {gui:.0f} | {pct:.1f} |")
+
+
 def _all(rows, counter, match):
     vals = {}
     for r in rows:
@@ -115,6 +154,8 @@ def _all(rows, counter, match):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "mfma":
+        mfma(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
     else:
