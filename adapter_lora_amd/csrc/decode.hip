@@ -404,62 +404,22 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
 // ---------------------------------------------------------------- consumers
 constexpr int kPollBatch = 8;    // exchange slots polled together
 
-template <typename T, int RCAP>
-__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, int b, int tile,
-                                            int n0, int n1, uint4* lds) {
-    constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
-    constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
-    constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
-    const LinearArgs& a = p.a;
+// S of a segment's tokens for one consumer tile: each element is the sum of
+// its K-chunk partials in chunk order, polled kPollBatch exchange slots at a
+// time; written to LDS (bf16 tables: as a hi / lo pair, rows of
+// LORA_MAX_RANK values).  False when a wait ran out (the error word is set by
+// the caller).
+template <typename T>
+__device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& v, int tile,
+                                          uint4* lds) {
+    constexpr int SLD = LORA_MAX_RANK;
     const int rp = v.rp;
-    const int tid = threadIdx.x;
-    const T* B = reinterpret_cast<const T*>(a.B) + v.off;
-    T* Y = reinterpret_cast<T*>(p.y);
-    // thread t owns output column n0 + t and keeps that column's B row
-    // (rank values 0..rp-1) in registers; rows and columns that do not exist
-    // are clamped into range and their results never stored
-    const int n_out = n0 + tid;
-    const bool nin = n_out < n1;
-    const int n_ld = min(n_out, n1 - 1);
-    // 1. B row and the y values this thread will update, issued before any wait
-    uint4 brow[CPR];
-#pragma unroll
-    for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
-    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
-    float yv[kTokGroup];
-#pragma unroll
-    for (int u = 0; u < kTokGroup; ++u) {
-        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + min(u, v.ms - 1));
-        yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
-    }
-    // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
-    //    polled kPollBatch slots at a time, into LDS (bf16: as a hi / lo pair)
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds);
     uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
     float* sS = reinterpret_cast<float*>(lds);
+    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * p.a.r_max;
     bool ok = true;
-    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * a.r_max;
-    if (p.tokens) {
-        // embedding lookup: the S row of sorted position p0 + t is row `tok`
-        // of the adapter's transposed A table; wave w takes tokens w, w + 4, ...
-        // (the token is wave-uniform, so it is read with readlane)
-        const T* At = reinterpret_cast<const T*>(a.A) + v.off2;
-        const int lane = lane_id();
-        for (int t = tid / kWave; t < v.ms; t += kDecWaves) {
-            const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
-            const bool on = tok >= 0 && tok < a.K;
-            if (lane < rp) {
-                const float val = on ? Io<T>::ld(At + (int64_t)tok * rp + lane) : 0.f;
-                if constexpr (sizeof(T) == 2) {
-                    sHi[t * SLD + lane] = (uint16_t)f32_to_bf16(val);   // exact: val is bf16
-                    sLo[t * SLD + lane] = 0;
-                } else {
-                    sS[t * SLD + lane] = val;
-                }
-            }
-        }
-    }
-    for (int e = p.tokens ? v.ms * rp : threadIdx.x; e < v.ms * rp; e += kDecThreads) {
+    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
         slot_t* sp = slot_at(p, 0, tile, v.p0 + t, j);
         float acc = 0.f;
@@ -498,6 +458,75 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
             sS[t * SLD + j] = acc;
         }
     }
+    return ok;
+}
+
+// Empty this consumer tile's slot copies for the next call: the workgroup is
+// their only reader.
+__device__ __forceinline__ void clear_slots(const DecodeParams& p, const SegView& v, int tile) {
+    const int rp = v.rp;
+    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * p.a.r_max;
+    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
+        slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
+        for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
+    }
+}
+
+template <typename T, int RCAP>
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, int b, int tile,
+                                            int n0, int n1, uint4* lds) {
+    constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+    constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
+    constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
+    const LinearArgs& a = p.a;
+    const int rp = v.rp;
+    const int tid = threadIdx.x;
+    const T* B = reinterpret_cast<const T*>(a.B) + v.off;
+    T* Y = reinterpret_cast<T*>(p.y);
+    // thread t owns output column n0 + t and keeps that column's B row
+    // (rank values 0..rp-1) in registers; rows and columns that do not exist
+    // are clamped into range and their results never stored
+    const int n_out = n0 + tid;
+    const bool nin = n_out < n1;
+    const int n_ld = min(n_out, n1 - 1);
+    // 1. B row and the y values this thread will update, issued before any wait
+    uint4 brow[CPR];
+#pragma unroll
+    for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
+    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
+    float yv[kTokGroup];
+#pragma unroll
+    for (int u = 0; u < kTokGroup; ++u) {
+        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + min(u, v.ms - 1));
+        yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
+    }
+    // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
+    //    polled kPollBatch slots at a time, into LDS (bf16: as a hi / lo pair)
+    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds);
+    uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
+    float* sS = reinterpret_cast<float*>(lds);
+    bool ok = true;
+    if (p.tokens) {
+        // embedding lookup: the S row of sorted position p0 + t is row `tok`
+        // of the adapter's transposed A table; wave w takes tokens w, w + 4, ...
+        // (the token is wave-uniform, so it is read with readlane)
+        const T* At = reinterpret_cast<const T*>(a.A) + v.off2;
+        const int lane = lane_id();
+        for (int t = tid / kWave; t < v.ms; t += kDecWaves) {
+            const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
+            const bool on = tok >= 0 && tok < a.K;
+            if (lane < rp) {
+                const float val = on ? Io<T>::ld(At + (int64_t)tok * rp + lane) : 0.f;
+                if constexpr (sizeof(T) == 2) {
+                    sHi[t * SLD + lane] = (uint16_t)f32_to_bf16(val);   // exact: val is bf16
+                    sLo[t * SLD + lane] = 0;
+                } else {
+                    sS[t * SLD + lane] = val;
+                }
+            }
+        }
+    }
+    if (!p.tokens) ok = collect_S<T>(p, v, tile, lds);
     if (!ok) atomicOr(p.err, kErrSpin);
     __syncthreads();
     // 3. delta of column n for each token: B row . S row (read by every lane
@@ -557,12 +586,95 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
     // 4. this workgroup is its slot copy's only reader: empty it for the next
     //    call.  Issued after the y stores, so that no wait for a prefetched y
     //    value has to count these stores as well.
-    if (!p.tokens) {
-        for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
-            slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
-            for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
+    if (!p.tokens) clear_slots(p, v, tile);
+}
+
+// bf16 consumers for ranks above 16: the deltas of 16 tokens x 64 columns
+// per wave as blocks of v_mfma_f32_16x16x32_bf16, the first operand the
+// tokens' S rows (hi / lo pair from LDS, zero past the tokens and past rp),
+// the second the wave's B rows (lane l: column 16 cb + l % 16, rank values
+// 32 t + 8 (l / 16) .. + 8).  acc[cb][q] is token 16 tb + 4 (l / 16) + q of
+// column n0 + 64 w + 16 cb + l % 16.  For a segment with several tokens this
+// replaces 2 rp dot products per token and column by a few MFMAs per wave.
+template <int RCAP>
+__device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView v, int b, int tile,
+                                                 int n0, int n1, uint4* lds) {
+    constexpr int NT = RCAP / 32;              // 32-wide rank steps
+    constexpr int SLD = LORA_MAX_RANK;
+    const LinearArgs& a = p.a;
+    const int rp = v.rp;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int lr = lane % 16, lq = lane / 16;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + v.off;
+    uint16_t* Y = reinterpret_cast<uint16_t*>(p.y);
+    // 1. B operands (clamped into the row and the slice: positions past rp
+    //    meet zero S values, columns past n1 are never stored), then the y
+    //    values of the first 16 tokens, issued before any wait
+    uint4 bop[4][NT];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int n = min(n0 + wave * 64 + cb * 16 + lr, n1 - 1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bop[cb][t] = ld16(B + (int64_t)n * rp + min(t * 32 + lq * 8, rp - 8));
+    }
+    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
+    auto token_row = [&](int u) {                  // token index at sorted position p0 + u
+        return __shfl(v.my_idx, v.p0 + min(u, v.ms - 1), kWave);
+    };
+    float yv[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = token_row(lq * 4 + q);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int n = min(n0 + wave * 64 + cb * 16 + lr, n1 - 1);
+            yv[cb][q] = bf16_to_f32(Y[(int64_t)m * p.ldy + n]);
         }
     }
+    // 2. S of the segment's tokens
+    const bool ok = collect_S<uint16_t>(p, v, tile, lds);
+    if (!ok) atomicOr(p.err, kErrSpin);
+    __syncthreads();
+    // 3. deltas, 16 tokens at a time, and the y update
+    const uint16_t* sHi = reinterpret_cast<const uint16_t*>(lds);
+    const uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
+    for (int tb = 0; tb * 16 < v.ms; ++tb) {
+        f32x4_t acc[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t * 32 >= rp) break;
+            const int row = tb * 16 + lr, k = t * 32 + lq * 8;
+            const uint32_t m = opaque_mask(row < v.ms && k < rp);
+            const uint4 h0 = *reinterpret_cast<const uint4*>(sHi + min(row, LORA_DECODE_MAX_M - 1) * SLD + min(k, SLD - 8));
+            const uint4 l0 = *reinterpret_cast<const uint4*>(sLo + min(row, LORA_DECODE_MAX_M - 1) * SLD + min(k, SLD - 8));
+            const uint4 h = make_uint4(h0.x & m, h0.y & m, h0.z & m, h0.w & m);
+            const uint4 l = make_uint4(l0.x & m, l0.y & m, l0.z & m, l0.w & m);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                acc[cb] = mfma_bf16(h, bop[cb][t], acc[cb]);
+                acc[cb] = mfma_bf16(l, bop[cb][t], acc[cb]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int u = tb * 16 + lq * 4 + q;
+            const int m = token_row(u);
+            if (u >= v.ms) continue;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int n = n0 + wave * 64 + cb * 16 + lr;
+                if (n >= n1) continue;
+                uint16_t* yp = Y + (int64_t)m * p.ldy + n;
+                const float old = tb == 0 ? yv[cb][q] : bf16_to_f32(*yp);
+                *yp = (uint16_t)f32_to_bf16(old + acc[cb][q]);
+            }
+        }
+    }
+    // 4. empty the slot copies (after the y stores, as in dec_consume)
+    clear_slots(p, v, tile);
 }
 
 template <typename T>
@@ -614,7 +726,16 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
     const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
     if (v.rp <= 16)
         dec_consume<T, 16>(p, v, b, t, n0, n1, lds);
-    else if (v.rp <= 32)
+    else if constexpr (sizeof(T) == 2) {
+        if (p.tokens) {
+            if (v.rp <= 32) dec_consume<T, 32>(p, v, b, t, n0, n1, lds);
+            else dec_consume<T, 64>(p, v, b, t, n0, n1, lds);
+        } else if (v.rp <= 32) {
+            dec_consume_mfma<32>(p, v, b, t, n0, n1, lds);
+        } else {
+            dec_consume_mfma<64>(p, v, b, t, n0, n1, lds);
+        }
+    } else if (v.rp <= 32)
         dec_consume<T, 32>(p, v, b, t, n0, n1, lds);
     else
         dec_consume<T, 64>(p, v, b, t, n0, n1, lds);
