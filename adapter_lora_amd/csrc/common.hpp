@@ -129,6 +129,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// 64-bit value of lane `l` (wave-uniform l), as two 32-bit readlanes.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Sum over each row of 16 lanes, left in every lane of the row, with DPP
 // lane swaps (VALU only: swap neighbours, swap pairs, mirror half rows, mirror
 // rows).  Fixed order, so the result is deterministic.

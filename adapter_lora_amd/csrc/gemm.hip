@@ -25,11 +25,14 @@
 // addresses), so the number of loads in flight is the same everywhere and the
 // compiler's waits keep the newer stage in flight.
 //
-// Epilogue: for each segment that meets the unit's rows (and has a nonzero
-// rank), the unit's S rows of that segment are staged in LDS as a bf16
-// hi / lo pair (zero elsewhere) and multiplied with the adapter's B rows on
-// the same MFMA blocks; then one bf16 rounding, staged through LDS so that
-// each output row is written in 16-byte pieces by token index.
+// Epilogue: the unit's S values and the B operands of its first two
+// segments are loaded during the last two stages, which need no global loads
+// or LDS writes of their own.  The S values go to LDS once as a bf16 hi / lo
+// pair; each segment that meets the unit's rows (and has a nonzero rank)
+// then multiplies its rows of them, selected by a mask on the operand, with
+// the adapter's B rows on the same MFMA blocks.  One bf16 rounding, staged
+// through LDS so that each output row is written in 16-byte pieces by token
+// index.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -92,6 +95,15 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
     const int srch1 = a.seg_indptr[min(lane * p.seg_stride, L)];
     const int m_valid = a.seg_indptr[L];
     const int nseg = a.num_segments[0];
+    // with fewer than 64 adapter slots the stride is 1 and lane j holds
+    // segment start j; with it, lane j also loads segment j's adapter and
+    // slot j's rank and B offset, so the unit's segments need no further
+    // round of loads
+    const bool quick = L < kWave;
+    const int lq = min(lane, max(L - 1, 0));
+    const int q_id = a.req_to_lora[lq];
+    const int q_rk = a.rank[lq];
+    const int64_t q_bo = a.b_off[lq];
 
     if (tid < kGM) s_tok[tid] = tid < rows ? a.sorted_idx[p0 + tid] : -1;
 
@@ -194,6 +206,27 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
     __syncthreads();
     Ops o0 = oread(0, 0);
 
+    // the unit's first two segments (start, end, rank, B offset; rank 0:
+    // none), for the B operands loaded during the last two stages
+    int sfirst = 0;
+    int pk_beg[2] = {0, 0}, pk_end[2] = {0, 0}, pk_rp[2] = {0, 0};
+    int64_t pk_bo[2] = {0, 0};
+    if (quick && p0 < m_valid) {
+        sfirst = 63 - __clzll((long long)__ballot(lane <= L && srch1 <= p0));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int sj = sfirst + j;
+            if (sj >= nseg) break;
+            pk_beg[j] = __builtin_amdgcn_readlane(srch1, sj);
+            pk_end[j] = __builtin_amdgcn_readlane(srch1, sj + 1);
+            const int id = __builtin_amdgcn_readlane(q_id, sj);
+            if (pk_beg[j] < p0 + rows && id >= 0 && id < L) {
+                pk_rp[j] = __builtin_amdgcn_readlane(q_rk, id);
+                pk_bo[j] = readlane64(q_bo, id);
+            }
+        }
+    }
+
     // stage ks; `slot` (ks & 1) is a literal at every call.  The ring slot of
     // stage ks + 2 was last read (stage ks - 1) before the previous barrier;
     // stage ks + 1 was written a stage ago, before that barrier.  With one
@@ -203,105 +236,171 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
     // fixed order: the writes of stage ks + 2 during the first two K steps,
     // the loads of stage ks + 4 (into the registers just written out) during
     // the last two.
-    auto step = [&](int ks, int slot) {
+    //
+    // `mode` (a literal at every call): 0 = as above; 1 = no global loads
+    // (stages ks + 4 do not exist); 2 = MFMAs and operand reads only (the
+    // last two stages: nothing left to write, no barrier); 3 = the same
+    // without the reads for a next stage.
+    auto step = [&](int ks, int slot, int mode) {
         Ops o1, o2, o3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             mfma1(o0, i);
             if (i < 6) oread1(o1, ks, 1, i);
-            if (i < 6) lstore1(ks + 2, slot, i);
+            if (i < 6 && mode < 2) lstore1(ks + 2, slot, i);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             mfma1(o1, i);
             if (i < 6) oread1(o2, ks, 2, i);
-            if (i < 6) lstore1(ks + 2, slot, 6 + i);
+            if (i < 6 && mode < 2) lstore1(ks + 2, slot, 6 + i);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             mfma1(o2, i);
             if (i < 6) oread1(o3, ks, 3, i);
-            if (i < 6) gload1(ks + 4, slot, i);
+            if (i < 6 && mode == 0) gload1(ks + 4, slot, i);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             mfma1(o3, i);
-            if (i < 6) oread1(o0, ks + 1, 0, i);
-            if (i < 6) gload1(ks + 4, slot, 6 + i);
+            if (i < 6 && mode < 3) oread1(o0, ks + 1, 0, i);
+            if (i < 6 && mode == 0) gload1(ks + 4, slot, 6 + i);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
+        if (mode < 2) __syncthreads();
     };
-    for (int ks = 0; ks < p.nk2; ks += 2) {
-        step(ks, 0);
-        step(ks + 1, 1);
+    int ks = 0;
+    for (; ks + 4 < p.nk2; ks += 2) {
+        step(ks, 0, 0);
+        step(ks + 1, 1, 0);
+    }
+    if (p.nk2 >= 4) {
+        step(ks, 0, 1);
+        step(ks + 1, 1, 1);
+        ks += 2;
     }
 
-    // ---- LoRA epilogue, one pass per segment that meets the unit's rows
-    if (p0 < m_valid) {
-        uint16_t* sHi = reinterpret_cast<uint16_t*>(smem);   // the ring is free now
-        uint16_t* sLo = sHi + kGM * kSLD;
-        // segment of sorted position p0: the last s with seg_indptr[s] <= p0
-        const uint64_t b1 = __ballot(lane * p.seg_stride <= L && srch1 <= p0);
-        const int lo = (63 - __clzll((long long)b1)) * p.seg_stride;
-        const int v2 = a.seg_indptr[min(lo + lane, L)];
-        const uint64_t b2 = __ballot(lane < p.seg_stride && lo + lane <= L && v2 <= p0);
-        int s = lo + 63 - __clzll((long long)b2);
-        for (; s < nseg; ++s) {
-            const int beg = a.seg_indptr[s];
-            if (beg >= p0 + rows) break;
-            const int end = a.seg_indptr[s + 1];
-            const int id = a.req_to_lora[s];
-            const int rp = a.rank[id];
-            if (rp == 0) continue;
-            const int r0 = max(beg - p0, 0), r1 = min(end - p0, rows);
-            const uint16_t* Bt = reinterpret_cast<const uint16_t*>(a.B) + a.b_off[id];
-            // B operands of the 16-wide rank steps t < rp / 16
-            uint4 bop[kGCB][4];
+    // ---- LoRA operands, loaded during the last two stages: the unit's S
+    // values for this slice, the same for every segment (thread t: row t / 2,
+    // rank positions 32 (t % 2) + 4 e, clamped into the row; positions past a
+    // segment's rank are never multiplied), and the B operands of the first
+    // two segments (rank steps t < rp / 16, as below)
+    const bool lora = p0 < m_valid && a.r_max > 0;
+    float4 sv[8];
+    uint4 pb[2][kGCB][4];
+    if (lora) {
+        const int srow = min(p0 + tid / 2, a.M - 1);
+        const float* sp = p.S + (int64_t)srow * a.cols + sl * a.r_max;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sv[e] = *reinterpret_cast<const float4*>(sp + min((tid % 2) * 32 + 4 * e, a.r_max - 4));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (pk_rp[j] == 0) continue;
+            const int rp = pk_rp[j];
+            const uint16_t* Bt = reinterpret_cast<const uint16_t*>(a.B) + pk_bo[j];
 #pragma unroll
             for (int cb = 0; cb < kGCB; ++cb) {
                 const int n = min(n0 + wave * 64 + cb * 32 + lr, n1 - 1);
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    bop[cb][t] = ld16(Bt + (int64_t)n * rp + min(t * 16, rp - 16) + lh * 8);
+                    pb[j][cb][t] = ld16(Bt + (int64_t)n * rp + min(t * 16, rp - 16) + lh * 8);
             }
-            // stage S rows [r0, r1) of the unit, zero elsewhere and past rp:
-            // thread t covers row t / 2, rank values 32 (t % 2) .. + 32
-            {
-                const int row = tid / 2, j0 = (tid % 2) * 32;
-                const bool in = row >= r0 && row < r1;
-                const float* sp = p.S + (int64_t)(p0 + row) * a.cols + sl * a.r_max;
+        }
+    }
+    step(ks, 0, 2);
+    step(ks + 1, 1, 3);
+    __syncthreads();     // every wave is done with the ring
+
+    // ---- LoRA epilogue: the unit's S values as a bf16 hi / lo pair in LDS,
+    // then one pass per segment that meets the unit's rows, its S rows picked
+    // by a row mask on the operand
+    if (lora) {
+        uint16_t* sHi = reinterpret_cast<uint16_t*>(smem);   // the ring is free now
+        uint16_t* sLo = sHi + kGM * kSLD;
+        {
+            const int row = tid / 2, j0 = (tid % 2) * 32;
 #pragma unroll
-                for (int e = 0; e < 32; e += 4) {
-                    const int j = j0 + e;
-                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (in && j < rp) v = *reinterpret_cast<const float4*>(sp + j);
-                    const float f[4] = {v.x, v.y, v.z, v.w};
-                    uint32_t h[4], l[4];
+            for (int e = 0; e < 8; ++e) {
+                const float f[4] = {sv[e].x, sv[e].y, sv[e].z, sv[e].w};
+                uint32_t h[4], l[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        h[q] = f32_to_bf16(f[q]);
-                        l[q] = f32_to_bf16(f[q] - bf16_to_f32(h[q]));
-                    }
-                    *reinterpret_cast<uint2*>(sHi + row * kSLD + j) =
-                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                    *reinterpret_cast<uint2*>(sLo + row * kSLD + j) =
-                        make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+                for (int q = 0; q < 4; ++q) {
+                    h[q] = f32_to_bf16(f[q]);
+                    l[q] = f32_to_bf16(f[q] - bf16_to_f32(h[q]));
+                }
+                *reinterpret_cast<uint2*>(sHi + row * kSLD + j0 + 4 * e) =
+                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                *reinterpret_cast<uint2*>(sLo + row * kSLD + j0 + 4 * e) =
+                    make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+            }
+        }
+        __syncthreads();
+        // segment of sorted position p0: the last s with seg_indptr[s] <= p0
+        int s0 = sfirst;
+        if (!quick) {
+            const uint64_t b1 = __ballot(lane * p.seg_stride <= L && srch1 <= p0);
+            const int lo = (63 - __clzll((long long)b1)) * p.seg_stride;
+            const int v2 = a.seg_indptr[min(lo + lane, L)];
+            const uint64_t b2 = __ballot(lane < p.seg_stride && lo + lane <= L && v2 <= p0);
+            s0 = lo + 63 - __clzll((long long)b2);
+        }
+        for (int s = s0; s < nseg; ++s) {
+            const int k = quick ? s - s0 : 2;       // 0, 1: the prefetched segments
+            int beg, end, rp;
+            int64_t bo = 0;
+            uint4 bop[kGCB][4];
+            if (k == 0) {
+                beg = pk_beg[0]; end = pk_end[0]; rp = pk_rp[0];
+            } else if (k == 1) {
+                beg = pk_beg[1]; end = pk_end[1]; rp = pk_rp[1];
+            } else {
+                beg = a.seg_indptr[s];
+                end = a.seg_indptr[s + 1];
+                const int id = a.req_to_lora[s];
+                rp = beg < p0 + rows ? a.rank[id] : 0;
+                bo = a.b_off[id];
+            }
+            if (beg >= p0 + rows) break;
+            if (rp == 0) continue;
+            if (k == 0) {
+#pragma unroll
+                for (int cb = 0; cb < kGCB; ++cb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) bop[cb][t] = pb[0][cb][t];
+            } else if (k == 1) {
+#pragma unroll
+                for (int cb = 0; cb < kGCB; ++cb)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) bop[cb][t] = pb[1][cb][t];
+            } else {
+                const uint16_t* Bt = reinterpret_cast<const uint16_t*>(a.B) + bo;
+#pragma unroll
+                for (int cb = 0; cb < kGCB; ++cb) {
+                    const int n = min(n0 + wave * 64 + cb * 32 + lr, n1 - 1);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        bop[cb][t] = ld16(Bt + (int64_t)n * rp + min(t * 16, rp - 16) + lh * 8);
                 }
             }
-            __syncthreads();
+            const int r0 = max(beg - p0, 0), r1 = min(end - p0, rows);
 #pragma unroll
             for (int rb = 0; rb < kGRB; ++rb) {
                 if (rb * 32 + 32 <= r0 || rb * 32 >= r1) continue;
+                const int row = rb * 32 + lr;
+                const uint32_t m = opaque_mask(row >= r0 && row < r1);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     if (t * 16 >= rp) continue;
-                    const int o = (rb * 32 + lr) * kSLD + t * 16 + lh * 8;
-                    const uint4 h = *reinterpret_cast<const uint4*>(sHi + o);
-                    const uint4 l = *reinterpret_cast<const uint4*>(sLo + o);
+                    const int o = row * kSLD + t * 16 + lh * 8;
+                    const uint4 h0 = *reinterpret_cast<const uint4*>(sHi + o);
+                    const uint4 l0 = *reinterpret_cast<const uint4*>(sLo + o);
+                    const uint4 h = make_uint4(h0.x & m, h0.y & m, h0.z & m, h0.w & m);
+                    const uint4 l = make_uint4(l0.x & m, l0.y & m, l0.z & m, l0.w & m);
 #pragma unroll
                     for (int cb = 0; cb < kGCB; ++cb) {
                         acc[rb][cb] = mfma32_bf16(h, bop[cb][t], acc[rb][cb]);
@@ -309,8 +408,8 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
                     }
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();     // the output staging below reuses the S rows' LDS
     }
 
     // ---- store through LDS (the ring is free: every wave has passed the last
