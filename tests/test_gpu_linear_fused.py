@@ -95,6 +95,10 @@ CASES = [
     ("one_token", lambda: W.random_linear(44, 1, 512, [264], [64], W.BF16, p_none=0.0)),
     ("contiguous_segments", lambda: W.random_linear(45, 520, 768, [1024], [16, 16, 32, 64],
                                                     W.BF16, contiguous=True)),
+    # 70 adapter slots (past one wavefront of slots: the segment search takes
+    # two rounds of loads) and about 30 segments in each 128-row unit
+    ("many_adapters", lambda: W.random_linear(48, 300, 256, [136], [16, 32, 0, 64, 16] * 14,
+                                              W.BF16)),
 ]
 
 
