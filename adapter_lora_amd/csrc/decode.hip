@@ -38,12 +38,15 @@ struct DecodeParams {
     void* y;
     int64_t ldy;
     int* err;
-    slot_t* slots;     // [C][n_tiles][64][r_max]: one copy per consumer tile
+    slot_t* slots;     // [C][n_groups][64][r_max]: one copy per consumer
     int C;
     int jb_max;        // n_sl * r_max / 16
     int grid1;
     int n_tiles;
     int tile_start[LORA_MAX_SLICES + 1];
+    int G;             // 256-column tiles per consumer (consecutive, one slice)
+    int n_groups;      // consumers per segment, all slices
+    int group_start[LORA_MAX_SLICES + 1];
     const int32_t* ids;      // non-null: segments grouped on chip from the ids
     const int32_t* enabled;  // adapter mask for that grouping (may be null)
     SegOut out;              // segment table written by the last workgroup (ids mode)
@@ -68,10 +71,10 @@ struct SegView {
     int64_t off2;              // the adapter's A offset as well (embedding lookup)
 };
 
-// Exchange slot of K chunk c, consumer tile t (its own copy), sorted
-// position pos and slice-local S column j.
+// Exchange slot of K chunk c, consumer t (its own copy), sorted position
+// pos and slice-local S column j.
 __device__ __forceinline__ slot_t* slot_at(const DecodeParams& p, int c, int t, int pos, int j) {
-    return p.slots + (((int64_t)c * p.n_tiles + t) * LORA_DECODE_MAX_M + pos) * p.a.r_max + j;
+    return p.slots + (((int64_t)c * p.n_groups + t) * LORA_DECODE_MAX_M + pos) * p.a.r_max + j;
 }
 
 // The arguments the segment view reads first, passed ahead of the parameter
@@ -295,7 +298,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
     }
     if (p.by_slot) slot_group(b, va.M, va.L, v);
     const T* X = reinterpret_cast<const T*>(p.x);
-    const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
+    const int t_beg = p.group_start[sl], t_end = p.group_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += kTokGroup) {
         float acc[kTokGroup][4];
 #pragma unroll
@@ -372,7 +375,7 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < a.K, A);
     if (p.by_slot) slot_group(b, va.M, va.L, v);
-    const int t_beg = p.tile_start[sl], t_end = p.tile_start[sl + 1];
+    const int t_beg = p.group_start[sl], t_end = p.group_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += 16) {
         const int nt = min(16, v.ms - t0);
         const int m = __shfl(v.my_idx, v.p0 + t0 + min(lr, nt - 1), kWave);
@@ -417,7 +420,7 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds);
     uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
     float* sS = reinterpret_cast<float*>(lds);
-    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * p.a.r_max;
+    const int64_t cstride = (int64_t)p.n_groups * LORA_DECODE_MAX_M * p.a.r_max;
     bool ok = true;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
@@ -465,16 +468,18 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
 // their only reader.
 __device__ __forceinline__ void clear_slots(const DecodeParams& p, const SegView& v, int tile) {
     const int rp = v.rp;
-    const int64_t cstride = (int64_t)p.n_tiles * LORA_DECODE_MAX_M * p.a.r_max;
+    const int64_t cstride = (int64_t)p.n_groups * LORA_DECODE_MAX_M * p.a.r_max;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
         for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
     }
 }
 
+// `first`: the consumer's first tile (group the tokens, collect S, which then
+// stays in LDS for its later tiles); `last`: its last (empty its slot copy).
 template <typename T, int RCAP>
-__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, int b, int tile,
-                                            int n0, int n1, uint4* lds) {
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, int b, int tile,
+                                            int n0, int n1, uint4* lds, bool first, bool last) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
     constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
@@ -493,7 +498,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
     uint4 brow[CPR];
 #pragma unroll
     for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
-    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
+    if (first && p.by_slot) slot_group(b, a.M, a.L, v);   // b: this lane's token bucket
     float yv[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
@@ -506,7 +511,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
     uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
     float* sS = reinterpret_cast<float*>(lds);
     bool ok = true;
-    if (p.tokens) {
+    if (first && p.tokens) {
         // embedding lookup: the S row of sorted position p0 + t is row `tok`
         // of the adapter's transposed A table; wave w takes tokens w, w + 4, ...
         // (the token is wave-uniform, so it is read with readlane)
@@ -526,9 +531,11 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
             }
         }
     }
-    if (!p.tokens) ok = collect_S<T>(p, v, tile, lds);
-    if (!ok) atomicOr(p.err, kErrSpin);
-    __syncthreads();
+    if (first) {
+        if (!p.tokens) ok = collect_S<T>(p, v, tile, lds);
+        if (!ok) atomicOr(p.err, kErrSpin);
+        __syncthreads();
+    }
     // 3. delta of column n for each token: B row . S row (read by every lane
     //    at the same LDS address, a broadcast)
     auto delta = [&](int t) {
@@ -586,7 +593,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
     // 4. this workgroup is its slot copy's only reader: empty it for the next
     //    call.  Issued after the y stores, so that no wait for a prefetched y
     //    value has to count these stores as well.
-    if (!p.tokens) clear_slots(p, v, tile);
+    if (last && !p.tokens) clear_slots(p, v, tile);
 }
 
 // bf16 consumers for ranks above 16: the deltas of 16 tokens x 64 columns
@@ -597,8 +604,9 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView v, in
 // column n0 + 64 w + 16 cb + l % 16.  For a segment with several tokens this
 // replaces 2 rp dot products per token and column by a few MFMAs per wave.
 template <int RCAP>
-__device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView v, int b, int tile,
-                                                 int n0, int n1, uint4* lds) {
+__device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView& v, int b, int tile,
+                                                 int n0, int n1, uint4* lds, bool first,
+                                                 bool last) {
     constexpr int NT = RCAP / 32;              // 32-wide rank steps
     constexpr int SLD = LORA_MAX_RANK;
     const LinearArgs& a = p.a;
@@ -618,7 +626,7 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView 
 #pragma unroll
         for (int t = 0; t < NT; ++t) bop[cb][t] = ld16(B + (int64_t)n * rp + min(t * 32 + lq * 8, rp - 8));
     }
-    if (p.by_slot) slot_group(b, a.M, a.L, v);      // b: this lane's token bucket
+    if (first && p.by_slot) slot_group(b, a.M, a.L, v);   // b: this lane's token bucket
     auto token_row = [&](int u) {                  // token index at sorted position p0 + u
         return __shfl(v.my_idx, v.p0 + min(u, v.ms - 1), kWave);
     };
@@ -632,10 +640,12 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView 
             yv[cb][q] = bf16_to_f32(Y[(int64_t)m * p.ldy + n]);
         }
     }
-    // 2. S of the segment's tokens
-    const bool ok = collect_S<uint16_t>(p, v, tile, lds);
-    if (!ok) atomicOr(p.err, kErrSpin);
-    __syncthreads();
+    // 2. S of the segment's tokens (first tile only; it stays in LDS)
+    if (first) {
+        const bool ok = collect_S<uint16_t>(p, v, tile, lds);
+        if (!ok) atomicOr(p.err, kErrSpin);
+        __syncthreads();
+    }
     // 3. deltas, 16 tokens at a time, and the y update
     const uint16_t* sHi = reinterpret_cast<const uint16_t*>(lds);
     const uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
@@ -674,7 +684,7 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView 
         }
     }
     // 4. empty the slot copies (after the y stores, as in dec_consume)
-    clear_slots(p, v, tile);
+    if (last) clear_slots(p, v, tile);
 }
 
 template <typename T>
@@ -706,8 +716,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
     }
     const LinearArgs& a = p.a;
     const int u = blockIdx.x - p.grid1;
-    const int s = u / p.n_tiles;
-    const int t = u % p.n_tiles;
+    const int s = u / p.n_groups;
+    const int g = u % p.n_groups;
     const ViewArgs va{ids, rank, b_off, M, L, p.tokens, p.tokens ? a_off : nullptr};
     SegView v;
     int b = 0;
@@ -720,25 +730,31 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
         v = seg_view(p, va, s);
         if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
     }
+    // consumer g: tiles tb .. te - 1 of one slice, S collected once
     int sl = 0;
-    while (sl + 1 < a.n_sl && t >= p.tile_start[sl + 1]) ++sl;
-    const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
-    const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
-    if (v.rp <= 16)
-        dec_consume<T, 16>(p, v, b, t, n0, n1, lds);
-    else if constexpr (sizeof(T) == 2) {
-        if (p.tokens) {
-            if (v.rp <= 32) dec_consume<T, 32>(p, v, b, t, n0, n1, lds);
-            else dec_consume<T, 64>(p, v, b, t, n0, n1, lds);
-        } else if (v.rp <= 32) {
-            dec_consume_mfma<32>(p, v, b, t, n0, n1, lds);
-        } else {
-            dec_consume_mfma<64>(p, v, b, t, n0, n1, lds);
-        }
-    } else if (v.rp <= 32)
-        dec_consume<T, 32>(p, v, b, t, n0, n1, lds);
-    else
-        dec_consume<T, 64>(p, v, b, t, n0, n1, lds);
+    while (sl + 1 < a.n_sl && g >= p.group_start[sl + 1]) ++sl;
+    const int tb = p.tile_start[sl] + (g - p.group_start[sl]) * p.G;
+    const int te = min(tb + p.G, p.tile_start[sl + 1]);
+    for (int t = tb; t < te; ++t) {
+        const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
+        const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
+        const bool first = t == tb, last = t + 1 == te;
+        if (v.rp <= 16)
+            dec_consume<T, 16>(p, v, b, g, n0, n1, lds, first, last);
+        else if constexpr (sizeof(T) == 2) {
+            if (p.tokens) {
+                if (v.rp <= 32) dec_consume<T, 32>(p, v, b, g, n0, n1, lds, first, last);
+                else dec_consume<T, 64>(p, v, b, g, n0, n1, lds, first, last);
+            } else if (v.rp <= 32) {
+                dec_consume_mfma<32>(p, v, b, g, n0, n1, lds, first, last);
+            } else {
+                dec_consume_mfma<64>(p, v, b, g, n0, n1, lds, first, last);
+            }
+        } else if (v.rp <= 32)
+            dec_consume<T, 32>(p, v, b, g, n0, n1, lds, first, last);
+        else
+            dec_consume<T, 64>(p, v, b, g, n0, n1, lds, first, last);
+    }
 }
 
 static hipError_t launch_decode(DecodeParams& p, unsigned grid, hipStream_t st) {
@@ -753,15 +769,23 @@ static hipError_t launch_decode(DecodeParams& p, unsigned grid, hipStream_t st) 
     return hipGetLastError();
 }
 
-static void set_tiles(DecodeParams& p) {
+// Tiles of 256 columns per slice, and consumers of G consecutive tiles of
+// one slice each.
+static void set_tiles(DecodeParams& p, int G) {
     const LinearArgs& a = p.a;
-    int t = 0;
+    int t = 0, g = 0;
     for (int s = 0; s < a.n_sl; ++s) {
         p.tile_start[s] = t;
-        t += (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+        p.group_start[s] = g;
+        const int nt = (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+        t += nt;
+        g += (nt + G - 1) / G;
     }
     p.tile_start[a.n_sl] = t;
+    p.group_start[a.n_sl] = g;
     p.n_tiles = t;
+    p.G = G;
+    p.n_groups = g;
 }
 
 hipError_t launch_embedding_decode(const LinearArgs& a, const int32_t* ids,
@@ -779,9 +803,11 @@ hipError_t launch_embedding_decode(const LinearArgs& a, const int32_t* ids,
     p.C = 0;
     p.jb_max = a.cols / 16;
     p.grid1 = 0;                        // consumers only: S comes from the lookup
-    set_tiles(p);
-    return launch_decode(p, (unsigned)(a.s_max * p.n_tiles + p.writer), st);
+    set_tiles(p, 1);
+    return launch_decode(p, (unsigned)(a.s_max * p.n_groups + p.writer), st);
 }
+
+constexpr int kResident = 1536;
 
 hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
                                const SegOut& out, const void* x, int64_t ldx, void* y,
@@ -806,8 +832,16 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     p.C = (a.K + kDecKChunk - 1) / kDecKChunk;
     p.jb_max = a.cols / 16;
     p.grid1 = a.s_max * p.jb_max * p.C;
-    set_tiles(p);
-    return launch_decode(p, (unsigned)(p.grid1 + a.s_max * p.n_tiles + p.writer), st);
+    // Consumers wait for their producers, so a consumer that is not resident
+    // yet starts only when an earlier one has finished.  Wide outputs (a
+    // vocabulary-sized LM head) therefore give each consumer G tiles, enough
+    // to keep the launch within about six workgroups per CU (this kernel keeps
+    // seven resident); S is collected once per consumer.
+    set_tiles(p, 1);
+    const int room = kResident - p.grid1 - p.writer;
+    const int cons = a.s_max * p.n_tiles;
+    if (cons > room) set_tiles(p, room > 0 ? (cons + room - 1) / room : p.n_tiles);
+    return launch_decode(p, (unsigned)(p.grid1 + a.s_max * p.n_groups + p.writer), st);
 }
 
 }  // namespace mlora
