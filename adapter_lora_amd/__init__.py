@@ -31,9 +31,19 @@ __all__ = [
 ]
 
 
-def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
+def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:
+    """hipStream_t of `stream`, else of the current stream (read without
+    building a Stream object: a decode call is short enough for the host side
+    of a launch to matter)."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _dtype_code(t: torch.dtype) -> int:
@@ -44,8 +54,10 @@ def _dtype_code(t: torch.dtype) -> int:
     raise LoraError(f"unsupported dtype {t}")
 
 
-def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
-    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    """Device address of a tensor (0 for None), passed as a plain int: the
+    argument types declared for the library convert it."""
+    return 0 if t is None else t.data_ptr()
 
 
 def _rows(t: torch.Tensor, name: str) -> int:
@@ -141,6 +153,7 @@ class LoraTable:
                                 ctypes.cast(_ptr(self.a_off), ctypes.POINTER(ctypes.c_int64)),
                                 ctypes.cast(_ptr(self.b_off), ctypes.POINTER(ctypes.c_int64)),
                                 ctypes.cast(_ptr(self.rank_dev), ctypes.POINTER(ctypes.c_int32)))
+        self.ref = ctypes.pointer(self.c)
 
     @property
     def cols(self) -> int:
@@ -167,6 +180,14 @@ class Segments:
         self.c = lora_segments_t(p32(self.sorted_idx), p32(self.seg_indptr), p32(self.req_to_lora),
                                  p32(self.num_segments), p32(self.tile_info), p32(self.tile_rows),
                                  p32(self.num_tiles), self.L, self.max_tiles)
+        # the output pointers of a call that writes the table, in ABI order
+        self.outs = tuple(_ptr(t) for t in (self.sorted_idx, self.seg_indptr, self.req_to_lora,
+                                            self.num_segments, self.tile_info, self.tile_rows,
+                                            self.num_tiles))
+        self.ref = ctypes.pointer(self.c)
+
+
+_NO_OUTS = (0,) * 7
 
 
 def _ids_arg(ids: torch.Tensor) -> int:
@@ -189,11 +210,9 @@ def lora_build_segments(ids: torch.Tensor, seg: Segments, stream=None,
     M = _ids_arg(ids)
     if M > seg.sorted_idx.shape[0]:
         raise LoraError("segment buffers too small")
-    check(lib.lora_build_segments(_ptr(ids), _mask_arg(adapter_enabled, seg.L), M, seg.L,
-                                  _ptr(seg.sorted_idx), _ptr(seg.seg_indptr),
-                                  _ptr(seg.req_to_lora), _ptr(seg.num_segments),
-                                  _ptr(seg.tile_info), _ptr(seg.tile_rows), _ptr(seg.num_tiles),
-                                  seg.max_tiles, stream_handle(stream)), "lora_build_segments")
+    check(lib.lora_build_segments(ids.data_ptr(), _mask_arg(adapter_enabled, seg.L), M, seg.L,
+                                  *seg.outs, seg.max_tiles, stream_handle(stream)),
+          "lora_build_segments")
 
 
 def lora_tile_capacity(M: int, L: int) -> int:
@@ -222,6 +241,7 @@ class Workspace:
 
     def __init__(self, nbytes: int, device="cuda", stream=None):
         self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        self.ptr, self.nbytes = _ptr(self.buf), self.buf.numel()
         lora_workspace_init(self.buf, stream)
 
     @classmethod
@@ -290,9 +310,8 @@ def lora_shrink_expand_add(table: LoraTable, x: torch.Tensor, seg: Segments, y: 
     ldx, ldy = _rows(x, "x"), _rows(y, "y")
     if x.shape[0] != y.shape[0]:
         raise LoraError("x and y must have the same number of rows")
-    check(lib.lora_shrink_expand_add(ctypes.byref(table.c), _ptr(x), ldx, x.shape[0],
-                                     ctypes.byref(seg.c), _ptr(y), ldy, _ptr(ws.buf),
-                                     ws.buf.numel(), stream_handle(stream)),
+    check(lib.lora_shrink_expand_add(table.ref, x.data_ptr(), ldx, x.shape[0], seg.ref,
+                                     y.data_ptr(), ldy, ws.ptr, ws.nbytes, stream_handle(stream)),
           "lora_shrink_expand_add")
 
 
@@ -324,17 +343,12 @@ def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: t
     if seg is not None:
         if seg.L != table.L or M > seg.sorted_idx.shape[0]:
             raise LoraError("segment buffers do not match the table or the batch")
-        outs = [_ptr(seg.sorted_idx), _ptr(seg.seg_indptr), _ptr(seg.req_to_lora),
-                _ptr(seg.num_segments), _ptr(seg.tile_info), _ptr(seg.tile_rows),
-                _ptr(seg.num_tiles)]
-        cap = seg.max_tiles
+        outs, cap = seg.outs, seg.max_tiles
     else:
-        outs = [_ptr(None)] * 7
-        cap = 0
-    check(lib.lora_fused_decode(ctypes.byref(table.c), _ptr(ids),
-                                _mask_arg(adapter_enabled, table.L), _ptr(x), ldx, M, _ptr(y),
-                                ldy, *outs, cap, _ptr(ws.buf), ws.buf.numel(),
-                                stream_handle(stream)), "lora_fused_decode")
+        outs, cap = _NO_OUTS, 0
+    check(lib.lora_fused_decode(table.ref, ids.data_ptr(), _mask_arg(adapter_enabled, table.L),
+                                x.data_ptr(), ldx, M, y.data_ptr(), ldy, *outs, cap, ws.ptr,
+                                ws.nbytes, stream_handle(stream)), "lora_fused_decode")
 
 
 # ------------------------------------------------------------------------- MoE
