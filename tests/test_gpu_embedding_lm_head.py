@@ -155,6 +155,29 @@ def test_lm_head_vocab_shard_with_output_offset(ml):
     assert_close(full[:, shard:], oracle_y(case), case.dtype, case.y_base.values, "shard")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lm_head_consumers_over_tile_groups(ml, dtype):
+    """Outputs wide enough that each decode consumer takes several column
+    tiles (two stacked slices of 20000 and 10136 columns, 20 adapters: two
+    tiles per consumer, a one-tile group at the end of the first slice and a
+    ragged last tile)."""
+    ranks = [16] * 20 if dtype == "f32" else [16, 32, 64, 0, 48] * 4
+    case = W.random_linear(27, 8, 256, [20000, 10136], ranks, W.F32 if dtype == "f32" else W.BF16)
+    log(f"lm_head tile groups {dtype} M={case.M} K={case.K} N={case.N}")
+    table = table_for(case)
+    ids = torch.from_numpy(case.ids).cuda()
+    y = to_dev(case.y_base)
+    seg = ml.Segments(case.M, case.L)
+    ws = ml.Workspace.for_table(table, case.M)
+    ml.lora_fused_decode(table, ids, to_dev(case.x), y, ws, seg=seg)
+    torch.cuda.synchronize()
+    assert ml.lora_read_device_error(ws.buf) == 0
+    got = to_f64(y)
+    keep = ~O.delta_rows(case.ids, case.ranks)
+    assert np.array_equal(got[keep], case.y_base.values[keep])
+    assert_close(got, oracle_y(case), case.dtype, case.y_base.values, case.name)
+
+
 def test_lm_head_larger_batch(ml):
     """More than 64 rows (the segmented shrink + expand) at vocabulary width."""
     case = W.random_linear(26, 160, 1024, [32000], [16, 64, 32, 0, 48], W.BF16)
