@@ -99,6 +99,9 @@ CASES = [
     # two rounds of loads) and about 30 segments in each 128-row unit
     ("many_adapters", lambda: W.random_linear(48, 300, 256, [136], [16, 32, 0, 64, 16] * 14,
                                               W.BF16)),
+    # K of one stage and of four stages (no steady-state loop iterations)
+    ("K_one_stage", lambda: W.random_linear(49, 150, 64, [264], [16, 32], W.BF16)),
+    ("K_four_stages", lambda: W.random_linear(50, 130, 200, [512], [64, 16, 32], W.BF16)),
 ]
 
 
@@ -107,6 +110,35 @@ def test_linear_fused_matches_oracle(ml, name, mk):
     case = mk()
     Wt = W.base_weight(100 + [c[0] for c in CASES].index(name), case.N, case.K)
     check(ml, case, Wt)
+
+
+def test_linear_fused_strided_operands(ml):
+    """x, W and y as column slices of wider buffers (leading dimensions past
+    K and N): the padding must be neither read into the result nor written."""
+    case = W.random_linear(51, 190, 320, [384], [16, 64, 32], W.BF16)
+    Wt = W.base_weight(51, case.N, case.K)
+    log(f"linear_fused strided M={case.M} K={case.K}")
+    table = table_for(case)
+    ids = torch.from_numpy(case.ids).cuda()
+    seg = ml.Segments(case.M, case.L)
+    ml.lora_build_segments(ids, seg)
+    xw = torch.full((case.M, case.K + 40), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xw[:, :case.K] = to_dev(case.x)
+    Ww = torch.full((case.N, case.K + 24), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Ww[:, :case.K] = to_dev(Wt)
+    yw = torch.full((case.M, case.N + 56), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = ml.Workspace.for_table(table, case.M)
+    ml.lora_linear_fused(table, Ww[:, :case.K], xw[:, :case.K], seg, yw[:, :case.N], ws)
+    torch.cuda.synchronize()
+    full = to_f64(yw)
+    assert np.all(full[:, case.N:] == 7.0), "padding columns of y were written"
+    got = full[:, :case.N]
+    ref = O.linear_with_base(case.x.values, Wt.values, case.ids, [a.values for a in case.A],
+                             [b.values for b in case.B], case.ranks, case.slice_sizes)
+    assert not np.isnan(got).any()
+    assert float(np.max(np.abs(got - ref))) <= TOL_BF16 * float(np.max(np.abs(ref)))
+    gamma = 2.0 * (case.K + 64) * 2.0 ** -24
+    assert not (np.abs(got - ref) > 2.0 ** -8 * np.abs(ref) + gamma * abs_bound(case, Wt)).any()
 
 
 def test_linear_fused_integer_exact(ml):
