@@ -395,7 +395,7 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
             if (tok < nt) {
                 const float sum = (red[(0 * 16 + tok) * 16 + row] + red[(1 * 16 + tok) * 16 + row]) +
                                   (red[(2 * 16 + tok) * 16 + row] + red[(3 * 16 + tok) * 16 + row]);
-                // one copy for every consumer tile of the slice
+                // one copy for every consumer of the slice
                 for (int t = t_beg; t < t_end; ++t)
                     slot_put(slot_at(p, c, t, v.p0 + t0 + tok, jj * 16 + row), sum);
             }
