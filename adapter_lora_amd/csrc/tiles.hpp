@@ -71,6 +71,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // issued together with the A loads, so a unit costs one memory round trip.
 // ---------------------------------------------------------------------------
 constexpr int kShrinkK = 512;
+// the A chunk is staged one row per direct-load instruction (64 lanes x 16 B)
+static_assert(kShrinkK * 2 == kWave * 16, "an A row of the K chunk is one wave's direct load");
 constexpr int kGroupCols = 64;
 constexpr int kShrinkLds = kGroupCols * kShrinkK * 2;   // bytes: the A chunk
 
