@@ -14,18 +14,20 @@ from typing import List, Optional, Sequence
 import torch
 
 from ._abi import (LORA_BF16, LORA_F32, LORA_MAX_ADAPTERS, LORA_MAX_RANK,
-                   LORA_MAX_SLICES, LORA_DECODE_MAX_M, LORA_TILE_ROWS, LoraError, lib, lora_weights_t,
+                   LORA_MAX_SLICES, LORA_DECODE_MAX_M, LORA_TILE_ROWS, LORA_DEVERR_WAIT,
+                   LORA_DEVERR_BAD_ID, LoraError, lib, lora_weights_t,
                    lora_segments_t, lora_moe_weights_t, lora_moe_align_t, check)
 
 __all__ = [
-    "LORA_BF16", "LORA_F32", "LoraError", "LoraTable", "Segments", "Workspace",
+    "LORA_BF16", "LORA_F32", "LORA_DEVERR_WAIT", "LORA_DEVERR_BAD_ID", "LoraError", "LoraTable",
+    "Segments", "Workspace",
     "MoeWeights", "MoeAlign",
     "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",
     "lora_shrink_expand_add", "lora_fused_decode",
     "lora_pack_embedding_adapter", "lora_embedding_shrink", "lora_embedding_decode",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
-    "lora_moe_align_capacity", "lora_moe_align_run", "lora_moe_workspace_size",
+    "lora_moe_align_capacity", "lora_moe_align", "lora_moe_workspace_size",
     "lora_moe_gate_up_add", "lora_moe_silu_and_mul", "lora_moe_down_add",
     "lora_moe_topk_reduce", "stream_handle",
 ]
@@ -58,6 +60,24 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
     """Device address of a tensor (0 for None), passed as a plain int: the
     argument types declared for the library convert it."""
     return 0 if t is None else t.data_ptr()
+
+
+def _check_io(dtype: torch.dtype, **named) -> None:
+    """Every operand shares the table's dtype (the kernels read and write
+    elements of that size): checked before any launch, on the tensors'
+    metadata only."""
+    for name, t in named.items():
+        if t is not None and t.dtype != dtype:
+            raise LoraError(f"{name} is {t.dtype} but the weights are {dtype}")
+
+
+def _cols(t: torch.Tensor, name: str, want: int, exact: bool = True) -> None:
+    """A 2-D operand has `want` columns (exact) or at least `want`."""
+    if t.dim() != 2:
+        raise LoraError(f"{name} must be a 2-D tensor")
+    w = t.shape[1]
+    if (w != want) if exact else (w < want):
+        raise LoraError(f"{name} has {w} columns, {'' if exact else 'at least '}{want} needed")
 
 
 def _rows(t: torch.Tensor, name: str) -> int:
@@ -252,6 +272,8 @@ class Workspace:
 # ------------------------------------------------------------------------- dense calls
 def lora_shrink(table: LoraTable, x: torch.Tensor, seg: Segments, S: torch.Tensor,
                 ws: Workspace, stream=None) -> None:
+    _check_io(table.dtype, x=x)
+    _cols(x, "x", table.K)
     ldx = _rows(x, "x")
     if S.dtype != torch.float32 or not S.is_contiguous() or S.numel() < x.shape[0] * table.cols:
         raise LoraError("S must be a contiguous fp32 [M, n_slices, r_max] tensor")
@@ -276,6 +298,8 @@ def lora_embedding_decode(table: LoraTable, ids: torch.Tensor, tokens: torch.Ten
     """One launch: y += B_i A_i[:, token] for up to 64 tokens (embedding
     LoRA), grouped by adapter on chip; writes the segment table into `seg`
     when given."""
+    _check_io(table.dtype, y=y)
+    _cols(y, "y", table.N, exact=False)
     M = _ids_arg(ids)
     if _ids_arg(tokens) != M or y.shape[0] != M:
         raise LoraError("ids, tokens and y must have the same number of rows")
@@ -298,15 +322,22 @@ def lora_embedding_decode(table: LoraTable, ids: torch.Tensor, tokens: torch.Ten
 
 def lora_expand_add(table: LoraTable, S: torch.Tensor, seg: Segments, y: torch.Tensor,
                     stream=None) -> None:
-    ldy = _rows(y, "y")
+    _check_io(table.dtype, y=y)
+    _cols(y, "y", table.N, exact=False)
     if S.dtype != torch.float32 or not S.is_contiguous():
         raise LoraError("S must be a contiguous fp32 tensor")
+    if S.numel() < y.shape[0] * table.cols:
+        raise LoraError("S must hold [M, n_slices, r_max] values")
+    ldy = _rows(y, "y")
     check(lib.lora_expand_add(ctypes.byref(table.c), _ptr(S), y.shape[0], ctypes.byref(seg.c),
                               _ptr(y), ldy, stream_handle(stream)), "lora_expand_add")
 
 
 def lora_shrink_expand_add(table: LoraTable, x: torch.Tensor, seg: Segments, y: torch.Tensor,
                            ws: Workspace, stream=None) -> None:
+    _check_io(table.dtype, x=x, y=y)
+    _cols(x, "x", table.K)
+    _cols(y, "y", table.N, exact=False)
     ldx, ldy = _rows(x, "x"), _rows(y, "y")
     if x.shape[0] != y.shape[0]:
         raise LoraError("x and y must have the same number of rows")
@@ -319,11 +350,15 @@ def lora_linear_fused(table: LoraTable, W: torch.Tensor, x: torch.Tensor, seg: S
                       y: torch.Tensor, ws: Workspace, stream=None) -> None:
     """y = x W^T + (x A_i^T) B_i^T per token (bf16), y overwritten; W is the
     base weight [N, K] with the table's slices stacked in order."""
-    ldw, ldx, ldy = _rows(W, "W"), _rows(x, "x"), _rows(y, "y")
+    _check_io(table.dtype, W=W, x=x, y=y)
+    _cols(W, "W", table.K)
+    _cols(x, "x", table.K)
+    _cols(y, "y", table.N, exact=False)
     if x.shape[0] != y.shape[0]:
         raise LoraError("x and y must have the same number of rows")
     if W.shape[0] != table.N:
         raise LoraError("W must have one row per output column of the table")
+    ldw, ldx, ldy = _rows(W, "W"), _rows(x, "x"), _rows(y, "y")
     check(lib.lora_linear_fused(ctypes.byref(table.c), _ptr(W), ldw, _ptr(x), ldx, x.shape[0],
                                 ctypes.byref(seg.c), _ptr(y), ldy, _ptr(ws.buf), ws.buf.numel(),
                                 stream_handle(stream)),
@@ -336,6 +371,9 @@ def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: t
     """One launch: y += (x A_id^T) B_id^T for up to 64 tokens, grouped by
     adapter on chip; when `seg` is given the launch also writes the batch's
     segment table there."""
+    _check_io(table.dtype, x=x, y=y)
+    _cols(x, "x", table.K)
+    _cols(y, "y", table.N, exact=False)
     M = _ids_arg(ids)
     ldx, ldy = _rows(x, "x"), _rows(y, "y")
     if x.shape[0] != M or y.shape[0] != M:
@@ -397,15 +435,18 @@ class MoeAlign:
             max_tokens_padded, block_size_m)
 
 
-def lora_moe_align_run(topk_ids: torch.Tensor, ids: torch.Tensor, adapter_enabled: torch.Tensor,
-                       E: int, out: MoeAlign, stream=None) -> None:
+def lora_moe_align(topk_ids: torch.Tensor, ids: torch.Tensor, adapter_enabled: torch.Tensor,
+                   E: int, out: MoeAlign, stream=None) -> None:
     M, topk = topk_ids.shape
     for t, n in ((topk_ids, "topk_ids"), (ids, "ids"), (adapter_enabled, "adapter_enabled")):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise LoraError(f"{n} must be a contiguous int32 device tensor")
-    check(lib.lora_moe_align_run(_ptr(topk_ids), _ptr(ids), _ptr(adapter_enabled), M, topk, E,
-                                 out.L, ctypes.byref(out.c), stream_handle(stream)),
-          "lora_moe_align_run")
+    if ids.numel() != M or adapter_enabled.numel() < out.L:
+        raise LoraError("ids must have M entries and adapter_enabled L")
+    check(lib.lora_moe_align(_ptr(topk_ids), _ptr(ids), _ptr(adapter_enabled), M, topk, E,
+                             out.L, out.block_size_m, out.max_tokens_padded,
+                             _ptr(out.sorted_token_ids), _ptr(out.expert_ids), _ptr(out.ntpp),
+                             stream_handle(stream)), "lora_moe_align")
 
 
 def lora_moe_workspace_size(w: MoeWeights, max_tokens_padded: int) -> int:
@@ -414,6 +455,11 @@ def lora_moe_workspace_size(w: MoeWeights, max_tokens_padded: int) -> int:
 
 def lora_moe_gate_up_add(w: MoeWeights, x: torch.Tensor, topk: int, align: MoeAlign,
                          cache1: torch.Tensor, ws: Workspace, stream=None) -> None:
+    _check_io(w.dtype, x=x, cache1=cache1)
+    _cols(x, "x", w.H)
+    _cols(cache1, "cache1", 2 * w.I, exact=False)
+    if cache1.shape[0] < x.shape[0] * topk:
+        raise LoraError("cache1 needs one row per (token, expert) pair")
     check(lib.lora_moe_gate_up_add(ctypes.byref(w.c), _ptr(x), _rows(x, "x"), x.shape[0], topk,
                                    ctypes.byref(align.c), _ptr(cache1), _rows(cache1, "cache1"),
                                    _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
@@ -421,7 +467,11 @@ def lora_moe_gate_up_add(w: MoeWeights, x: torch.Tensor, topk: int, align: MoeAl
 
 
 def lora_moe_silu_and_mul(cache1: torch.Tensor, cache2: torch.Tensor, stream=None) -> None:
+    _check_io(cache1.dtype, cache2=cache2)
     P, I = cache2.shape
+    _cols(cache1, "cache1", 2 * I, exact=False)
+    if cache1.shape[0] < P:
+        raise LoraError("cache1 has fewer rows than cache2")
     check(lib.lora_moe_silu_and_mul(_dtype_code(cache1.dtype), _ptr(cache1), _rows(cache1, "cache1"),
                                     _ptr(cache2), _rows(cache2, "cache2"), P, I,
                                     stream_handle(stream)), "lora_moe_silu_and_mul")
@@ -429,6 +479,11 @@ def lora_moe_silu_and_mul(cache1: torch.Tensor, cache2: torch.Tensor, stream=Non
 
 def lora_moe_down_add(w: MoeWeights, cache2: torch.Tensor, M: int, topk: int, align: MoeAlign,
                       cache3: torch.Tensor, ws: Workspace, stream=None) -> None:
+    _check_io(w.dtype, cache2=cache2, cache3=cache3)
+    _cols(cache2, "cache2", w.I)
+    _cols(cache3, "cache3", w.H, exact=False)
+    if cache2.shape[0] < M * topk or cache3.shape[0] < M * topk:
+        raise LoraError("cache2 and cache3 need one row per (token, expert) pair")
     check(lib.lora_moe_down_add(ctypes.byref(w.c), _ptr(cache2), _rows(cache2, "cache2"), M, topk,
                                 ctypes.byref(align.c), _ptr(cache3), _rows(cache3, "cache3"),
                                 _ptr(ws.buf), ws.buf.numel(), stream_handle(stream)),
@@ -440,6 +495,10 @@ def lora_moe_topk_reduce(cache3: torch.Tensor, topk_weights: torch.Tensor, out: 
     M, topk = topk_weights.shape
     if topk_weights.dtype != torch.float32 or not topk_weights.is_contiguous():
         raise LoraError("topk_weights must be contiguous fp32")
+    _check_io(cache3.dtype, out=out)
+    _cols(cache3, "cache3", out.shape[1], exact=False)
+    if out.shape[0] < M or cache3.shape[0] < M * topk:
+        raise LoraError("out needs M rows and cache3 M * topk")
     check(lib.lora_moe_topk_reduce(_dtype_code(cache3.dtype), _ptr(cache3), _rows(cache3, "cache3"),
                                    _ptr(topk_weights), _ptr(out), _rows(out, "out"), M, topk,
                                    out.shape[1], stream_handle(stream)), "lora_moe_topk_reduce")

@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MLORA_LIB", os.path.join(HERE, "libmlora.so"))
 
 LORA_OK, LORA_INVALID_ARG, LORA_UNSUPPORTED, LORA_HIP_ERROR = 0, 1, 2, 3
+LORA_DEVERR_WAIT, LORA_DEVERR_BAD_ID = 1, 2
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_SLICES = 4
 LORA_RANK_ALIGN = 16
@@ -17,7 +18,7 @@ LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
 LORA_TILE_ROWS = 64
-MLORA_ABI_VERSION = 4
+MLORA_ABI_VERSION = 5
 
 
 class LoraError(RuntimeError):
@@ -88,7 +89,7 @@ SIGNATURES = {
     "lora_embedding_shrink": (I32, [PW, P, I32, PS, P, P]),
     "lora_embedding_decode": (I32, [PW, P, P, P, I32, P, I64, P, P, P, P, P, P, P, I32, P]),
     "lora_moe_align_capacity": (I32, [I32, I32, I32, I32]),
-    "lora_moe_align_run": (I32, [P, P, P, I32, I32, I32, I32, PMA, P]),
+    "lora_moe_align": (I32, [P, P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
     "lora_moe_workspace_size": (SZ, [PMW, I32]),
     "lora_moe_gate_up_add": (I32, [PMW, P, I64, I32, I32, PMA, P, I64, P, SZ, P]),
     "lora_moe_silu_and_mul": (I32, [I32, P, I64, P, I64, I32, I32, P]),

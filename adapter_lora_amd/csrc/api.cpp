@@ -87,21 +87,18 @@ LinearArgs make_args(const lora_weights_t* w, const lora_segments_t* seg, int M)
 }
 
 LinearWs layout_for(const lora_weights_t* w, int M) {
-    int tiles = 0;
-    for (int s = 0; s < w->n_slices; ++s)
-        tiles += (int)((w->slice_offsets[s + 1] - w->slice_offsets[s] + kNTile - 1) / kNTile);
-    return linear_ws_layout(M, w->K, w->n_slices * w->r_max, w->r_max, tiles);
+    return linear_ws_layout(M, w->K, w->n_slices * w->r_max);
 }
 
 }  // namespace
 
 namespace mlora {
 
-// header | decode slots [Cd][n_tiles][64][r_max] | shrink partials
-// [C][M][cols] | S [M][cols], with Cd = ceil(K / kDecKChunk) and
-// C = ceil(K / kKChunk).  The decode region does not depend on M, so calls
-// of any M may share one workspace.
-LinearWs linear_ws_layout(int M, int K, int cols, int r_max, int n_tiles) {
+// header | decode slots [Cd][64][cols] | shrink partials [C][M][cols] |
+// S [M][cols], with Cd = ceil(K / kDecKChunk) and C = ceil(K / kKChunk).
+// The header and decode region do not depend on M, so calls of any M may
+// share one workspace.
+LinearWs linear_ws_layout(int M, int K, int cols) {
     LinearWs ws{};
     const size_t C = (size_t)kchunks(K);
     const size_t Cd = (size_t)((K + kDecKChunk - 1) / kDecKChunk);
@@ -109,7 +106,7 @@ LinearWs linear_ws_layout(int M, int K, int cols, int r_max, int n_tiles) {
     ws.header = off;
     off += up(sizeof(WsHeader));
     ws.slots = off;
-    off += up(Cd * n_tiles * LORA_DECODE_MAX_M * r_max * sizeof(slot_t));
+    off += up(Cd * LORA_DECODE_MAX_M * (size_t)cols * sizeof(slot_t));
     ws.partial = off;
     off += up(C * (size_t)M * cols * sizeof(float));
     ws.S = off;
@@ -287,7 +284,7 @@ lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64
     const LinearArgs a = make_args(w, seg, M);
     if (M <= LORA_DECODE_MAX_M)
         return from_hip(launch_decode_fused(a, nullptr, nullptr, SegOut{}, x, ldx, y, ldy,
-                                            workspace, stream));
+                                            workspace, nullptr, stream));
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.S);
     hipError_t e = launch_shrink(a, x, ldx, S, workspace, stream);
     if (e != hipSuccess) return LORA_HIP_ERROR;
@@ -353,7 +350,7 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
     const SegOut out{sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
                      num_tiles};
     return from_hip(launch_decode_fused(a, ids, adapter_enabled, out, x, ldx, y, ldy, workspace,
-                                        stream));
+                                        nullptr, stream));
 }
 
 lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t emb, int32_t rank,
@@ -444,19 +441,23 @@ static lora_status check_moe_weights(const lora_moe_weights_t* w) {
     return LORA_OK;
 }
 
-lora_status lora_moe_align_run(const int32_t* topk_ids, const int32_t* ids,
-                               const int32_t* adapter_enabled, int32_t M, int32_t topk, int32_t E,
-                               int32_t L, const lora_moe_align_t* out, hipStream_t stream) {
+lora_status lora_moe_align(const int32_t* topk_ids, const int32_t* ids,
+                           const int32_t* adapter_enabled, int32_t M, int32_t topk, int32_t E,
+                           int32_t L, int32_t block_size_m, int32_t max_tokens_padded,
+                           int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
+                           hipStream_t stream) {
     if (M < 0 || topk < 1 || topk > 16 || E < 1 || E > 256 || L < 1 || L > LORA_MAX_ADAPTERS)
         return LORA_INVALID_ARG;
     if ((int64_t)M * topk > (1 << 24)) return LORA_INVALID_ARG;
     if (!adapter_enabled) return LORA_INVALID_ARG;
     if (M > 0 && (!topk_ids || !ids)) return LORA_INVALID_ARG;
-    lora_status st = check_align(out, M, topk, E);
+    const lora_moe_align_t out{sorted_token_ids, expert_ids, ntpp, max_tokens_padded,
+                               block_size_m};
+    lora_status st = check_align(&out, M, topk, E);
     if (st != LORA_OK) return st;
     return from_hip(launch_moe_align(topk_ids, ids, adapter_enabled, M, topk, E, L,
-                                     out->sorted_token_ids, out->expert_ids, out->ntpp,
-                                     out->max_tokens_padded, out->block_size_m, stream));
+                                     sorted_token_ids, expert_ids, ntpp, max_tokens_padded,
+                                     block_size_m, stream));
 }
 
 size_t lora_moe_workspace_size(const lora_moe_weights_t* w, int32_t max_tokens_padded) {

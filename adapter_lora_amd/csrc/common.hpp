@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mlora.h"
+
 namespace mlora {
 
 constexpr int kWave = 64;
@@ -169,33 +171,39 @@ __device__ __forceinline__ float wave_total(float v) {
 // A slot is one 64-bit word {fp32 value (low), tag (high)} written and read
 // with single 64-bit relaxed atomics at agent scope, so the value and its tag
 // always travel together: no fence is needed to order data before a flag.
-// Tag 1 = full, 0 = empty.  The consumer that reads a group of slots last
-// (decided by a per-group counter) empties them again, so a workspace stays
-// ready for the next launch.
+// The tag identifies the launch (launch_tag below): a slot counts as full
+// for a launch only when it carries that launch's tag, so slots are never
+// emptied after use, and values left by earlier launches (or by a launch
+// that gave up waiting) are simply ignored.  Tag 0 never matches, so a
+// zeroed workspace holds no full slot.
 // ----------------------------------------------------------------------------
 typedef unsigned long long slot_t;
 
-__device__ __forceinline__ void slot_put(slot_t* s, float v) {
-    const slot_t w = (1ull << 32) | (slot_t)__float_as_uint(v);
+__device__ __forceinline__ void slot_put(slot_t* s, float v, uint32_t tag) {
+    const slot_t w = ((slot_t)tag << 32) | (slot_t)__float_as_uint(v);
     __hip_atomic_store(s, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void slot_clear(slot_t* s) {
-    __hip_atomic_store(s, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ slot_t slot_load(const slot_t* s) {
+    return __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until the slot is full.  Gives up after `max_spin` polls (then
-// returns false and the caller reports a device error): every wave exits.
-__device__ __forceinline__ bool slot_get(const slot_t* s, float* out, int max_spin) {
-    for (int i = 0;; ++i) {
-        const slot_t w = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(w >> 32) == 1u) {
-            *out = __uint_as_float((uint32_t)w);
-            return true;
-        }
-        if (i >= max_spin) return false;
-        __builtin_amdgcn_s_sleep(2);
-    }
+__device__ __forceinline__ bool slot_full(slot_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+// The dispatch's packet index on its hardware queue (a user SGPR set by the
+// command processor for every dispatch, graph replays included).
+extern "C" __device__ uint64_t mlora_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// Tag of this launch: the dispatch index mixed with the queue's address,
+// reduced to [1, 2^32 - 1].  Consecutive dispatches on one queue get
+// different tags (for 2^32 - 1 dispatches), and equal dispatch indices on two
+// queues get different tags unless the two queue addresses happen to
+// collide in 32 bits.  Wave-uniform; scalar arithmetic only.
+__device__ __forceinline__ uint32_t launch_tag() {
+    const uint64_t id = mlora_dispatch_id();
+    const uint64_t q = (uint64_t)(uintptr_t)__builtin_amdgcn_queue_ptr() >> 6;
+    const uint64_t h = id + q * 0x9E3779B97F4A7C15ull;
+    return (uint32_t)(h % 0xffffffffull) + 1u;
 }
 
 __device__ __forceinline__ int atomic_add_agent(int* p, int v) {
@@ -206,13 +214,15 @@ __device__ __forceinline__ void atomic_store_agent(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workspace header shared by every kernel that uses a workspace.
+// Workspace header shared by every kernel that uses a workspace (256 bytes).
 struct WsHeader {
-    int error;        // sticky error bits (bit 0: gave up waiting)
-    int pad[63];      // keeps counters that follow on their own 256-byte line
+    int error;        // sticky error bits (LORA_DEVERR_*), first word: read by the host
+    int pad[63];
 };
+static_assert(sizeof(WsHeader) == 256, "workspace header size");
 
-constexpr int kErrSpin = 1;
+constexpr int kErrSpin = LORA_DEVERR_WAIT;
+constexpr int kErrBadId = LORA_DEVERR_BAD_ID;
 constexpr int kMaxSpin = 1 << 20;
 
 }  // namespace mlora

@@ -14,7 +14,9 @@
 //   consumers  (blockIdx >= grid1): unit = (segment, 256 output columns of a
 //              slice), thread t owning column n0 + t.  A thread first loads its
 //              column's B row (rp contiguous values) and the y values it will
-//              update, and only then waits for the segment's slots; the K-chunk
+//              update, and only then waits for the segment's slots (one set
+//              per launch, shared by every consumer of the segment and
+//              tagged with the launch's own tag); the K-chunk
 //              partials are summed in a fixed order into LDS (S stays on chip,
 //              as a bf16 hi / lo pair for bf16 data) and each thread dots its B
 //              row with every token's S row, read from LDS as a broadcast.  No
@@ -38,7 +40,7 @@ struct DecodeParams {
     void* y;
     int64_t ldy;
     int* err;
-    slot_t* slots;     // [C][n_groups][64][r_max]: one copy per consumer
+    slot_t* slots;     // [C][64][a.cols]: K chunk, sorted position, S column
     int C;
     int jb_max;        // n_sl * r_max / 16
     int grid1;
@@ -65,16 +67,17 @@ struct DecodeParams {
 // of up to 256 slots, every slot's rank and weight offset (picked by lane
 // shuffle once the id is known).
 struct SegView {
-    int nseg, id, rp, p0, ms, my_idx;
+    int nseg, id, rp, p0, ms;
+    int tl;                    // lane t < ms: the segment's t-th token (sorted order)
     int64_t off;
-    int tok;                   // lane p: token id at sorted position p (embedding lookup)
+    int tok;                   // lane t < ms: token id of the segment's t-th token (embedding lookup)
     int64_t off2;              // the adapter's A offset as well (embedding lookup)
 };
 
-// Exchange slot of K chunk c, consumer t (its own copy), sorted position
-// pos and slice-local S column j.
-__device__ __forceinline__ slot_t* slot_at(const DecodeParams& p, int c, int t, int pos, int j) {
-    return p.slots + (((int64_t)c * p.n_groups + t) * LORA_DECODE_MAX_M + pos) * p.a.r_max + j;
+// Exchange slot of K chunk c, sorted position pos and S column col
+// (slice sl, rank index j: col = sl * r_max + j).
+__device__ __forceinline__ slot_t* slot_at(const DecodeParams& p, int c, int pos, int col) {
+    return p.slots + ((int64_t)c * LORA_DECODE_MAX_M + pos) * p.a.cols + col;
 }
 
 // The arguments the segment view reads first, passed ahead of the parameter
@@ -108,7 +111,7 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
         p1 = a.seg_indptr[s + 1];
         // indices are clamped rather than tested, so every load is
         // unconditional and all of them are in flight together
-        v.my_idx = a.sorted_idx[min(lane, M - 1)];
+        v.tl = a.sorted_idx[min(lane, M - 1)];
     }
     int rk[4];
     int64_t of[4], of2[4];
@@ -133,9 +136,11 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
         int n;
         wave_segment(g, s, &v.p0, &n, &v.id);
         v.nseg = g.nseg;
-        v.my_idx = g.key & 63;
+        v.tl = g.key & 63;
         p1 = v.p0 + n;
     }
+    // lane t: token at sorted position p0 + t
+    v.tl = __shfl(v.tl, (v.p0 + lane) & (kWave - 1), kWave);
     const int id = v.id < 0 ? 0 : v.id;
     if (small) {
         // id is the same in every lane: the entry is read with readlane
@@ -155,8 +160,8 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
         v.off = offs[id];
         v.off2 = va.offs2 ? va.offs2[id] : 0;
     }
-    // token id at each sorted position (lane p reads token my_idx of lane p)
-    v.tok = va.tokens ? __shfl(tk, v.my_idx & (kWave - 1), kWave) : 0;
+    // token id of the segment's t-th token (lane t reads token tl of lane t)
+    v.tok = va.tokens ? __shfl(tk, v.tl & (kWave - 1), kWave) : 0;
     v.ms = p1 - v.p0;
     return v;
 }
@@ -165,8 +170,8 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
 // unit s serves adapter slot s rather than the s-th segment.  Its rank and
 // weight offset are then two scalar loads issued together with the ids, and
 // once both are in, one ballot over the token buckets tells whether any
-// token uses the slot; the weight loads are issued before the grouping is
-// computed, which afterwards gives the slot's token rows.
+// token uses the slot; the weight loads are issued before the slot's token
+// list (slot_tokens) is formed.
 __device__ __forceinline__ SegView slot_head(const ViewArgs& va, int s) {
     SegView v{};
     v.id = s;
@@ -180,16 +185,21 @@ __device__ __forceinline__ bool slot_used(int b, int M, int s) {
     return __ballot(lane_id() < M && b == s) != 0ull;
 }
 
-// The grouping part of slot s's view: sorted token order (my_idx), and the
-// first sorted position and count of the slot's tokens.
-__device__ __forceinline__ void slot_group(int b, int M, int L, SegView& v) {
+// The token list of slot s (b: this lane's token bucket) without grouping
+// the whole batch: one ballot marks the slot's tokens, and one lane permute
+// puts the t-th of them (ascending token index: the stable order) in lane t.
+// The first sorted position is the number of tokens with a smaller bucket.
+__device__ __forceinline__ void slot_tokens(int b, int M, SegView& v) {
     const int lane = lane_id();
-    const WaveGroups g = wave_group(b, M, L);
     const bool valid = lane < M;
-    v.my_idx = g.key & 63;
+    const unsigned long long mine = __ballot(valid && b == v.id);
     v.p0 = __popcll(__ballot(valid && b < v.id));
-    v.ms = __popcll(__ballot(valid && b == v.id));
-    v.nseg = g.nseg;
+    v.ms = __popcll(mine);
+    const int below = __popcll(mine & ((1ull << lane) - 1ull));
+    const bool in = (mine >> lane) & 1ull;
+    // members go to lanes 0 .. ms-1 in order, the others to ms .. 63
+    const int dst = in ? below : v.ms + (lane - below);
+    v.tl = __builtin_amdgcn_ds_permute(dst * 4, lane);
 }
 
 // ---------------------------------------------------------------- producers
@@ -260,7 +270,8 @@ __device__ __forceinline__ float dot8(const Raw8<T>& a, const Raw8<T>& b, float 
 template <typename T> constexpr int dec_steps() { return 2; }
 
 template <typename T>
-__device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArgs& va, int unit) {
+__device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArgs& va, int unit,
+                                            uint32_t tag) {
     constexpr int ST = dec_steps<T>();
     const LinearArgs& a = p.a;
     const int per_s = p.jb_max * p.C;
@@ -296,9 +307,8 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
             ar[st][i] = ld_raw8_if(A + (int64_t)i * a.K + k, k < a.K, A);
         }
     }
-    if (p.by_slot) slot_group(b, va.M, va.L, v);
+    if (p.by_slot) slot_tokens(b, va.M, v);
     const T* X = reinterpret_cast<const T*>(p.x);
-    const int t_beg = p.group_start[sl], t_end = p.group_start[sl + 1];
     for (int t0 = 0; t0 < v.ms; t0 += kTokGroup) {
         float acc[kTokGroup][4];
 #pragma unroll
@@ -307,7 +317,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
             for (int i = 0; i < 4; ++i) acc[u][i] = 0.f;
         int mrow[kTokGroup];
 #pragma unroll
-        for (int u = 0; u < kTokGroup; ++u) mrow[u] = __shfl(v.my_idx, v.p0 + t0 + u, kWave);
+        for (int u = 0; u < kTokGroup; ++u) mrow[u] = __shfl(v.tl, (t0 + u) & (kWave - 1), kWave);
 #pragma unroll
         for (int st = 0; st < ST; ++st) {
             const int k = kbase + st * 512;
@@ -331,8 +341,8 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
             const float r2 = wave_total(acc[u][2]), r3 = wave_total(acc[u][3]);
             const float tot = lane == 0 ? r0 : lane == 1 ? r1 : lane == 2 ? r2 : r3;
             if (lane < 4)
-                for (int t = t_beg; t < t_end; ++t)
-                    slot_put(slot_at(p, c, t, v.p0 + t0 + u, jj * 16 + wave * 4 + lane), tot);
+                slot_put(slot_at(p, c, v.p0 + t0 + u, sl * a.r_max + jj * 16 + wave * 4 + lane), tot,
+                         tag);
         }
     }
 }
@@ -344,7 +354,7 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
 // over K happens inside the matrix core.  The four waves' 16 x 16 partials
 // are added in LDS in a fixed order and written to the exchange slots.
 __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const ViewArgs& va, int unit,
-                                                 float* red) {
+                                                 float* red, uint32_t tag) {
     const LinearArgs& a = p.a;
     const int per_s = p.jb_max * p.C;
     const int s = unit / per_s;
@@ -374,11 +384,10 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
     uint4 av[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < a.K, A);
-    if (p.by_slot) slot_group(b, va.M, va.L, v);
-    const int t_beg = p.group_start[sl], t_end = p.group_start[sl + 1];
+    if (p.by_slot) slot_tokens(b, va.M, v);
     for (int t0 = 0; t0 < v.ms; t0 += 16) {
         const int nt = min(16, v.ms - t0);
-        const int m = __shfl(v.my_idx, v.p0 + t0 + min(lr, nt - 1), kWave);
+        const int m = __shfl(v.tl, t0 + min(lr, nt - 1), kWave);
         const uint16_t* xp = X + (int64_t)m * p.ldx;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         uint4 xv[8];
@@ -395,9 +404,8 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
             if (tok < nt) {
                 const float sum = (red[(0 * 16 + tok) * 16 + row] + red[(1 * 16 + tok) * 16 + row]) +
                                   (red[(2 * 16 + tok) * 16 + row] + red[(3 * 16 + tok) * 16 + row]);
-                // one copy for every consumer of the slice
-                for (int t = t_beg; t < t_end; ++t)
-                    slot_put(slot_at(p, c, t, v.p0 + t0 + tok, jj * 16 + row), sum);
+                // one slot, read by every consumer of the slice
+                slot_put(slot_at(p, c, v.p0 + t0 + tok, sl * a.r_max + jj * 16 + row), sum, tag);
             }
         }
         __syncthreads();     // red is rewritten by the next token group
@@ -407,40 +415,34 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
 // ---------------------------------------------------------------- consumers
 constexpr int kPollBatch = 8;    // exchange slots polled together
 
-// S of a segment's tokens for one consumer tile: each element is the sum of
-// its K-chunk partials in chunk order, polled kPollBatch exchange slots at a
-// time; written to LDS (bf16 tables: as a hi / lo pair, rows of
-// LORA_MAX_RANK values).  False when a wait ran out (the error word is set by
-// the caller).
+// S of a segment's tokens for slice sl: each element is the sum of its
+// K-chunk partials in chunk order, polled kPollBatch exchange slots at a
+// time until each carries the launch's tag; written to LDS (bf16 tables: as
+// a hi / lo pair, rows of LORA_MAX_RANK values).  False when a wait ran out
+// (the error word is set by the caller).
 template <typename T>
-__device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& v, int tile,
-                                          uint4* lds) {
+__device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& v, int sl,
+                                          uint32_t tag, uint4* lds) {
     constexpr int SLD = LORA_MAX_RANK;
     const int rp = v.rp;
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds);
     uint16_t* sLo = sHi + LORA_DECODE_MAX_M * SLD;
     float* sS = reinterpret_cast<float*>(lds);
-    const int64_t cstride = (int64_t)p.n_groups * LORA_DECODE_MAX_M * p.a.r_max;
+    const int64_t cstride = (int64_t)LORA_DECODE_MAX_M * p.a.cols;
     bool ok = true;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
-        slot_t* sp = slot_at(p, 0, tile, v.p0 + t, j);
+        const slot_t* sp = slot_at(p, 0, v.p0 + t, sl * p.a.r_max + j);
         float acc = 0.f;
         for (int c0 = 0; c0 < p.C; c0 += kPollBatch) {
             slot_t w[kPollBatch];
             for (int spin = 0;; ++spin) {
                 bool all = true;
 #pragma unroll
-                for (int q = 0; q < kPollBatch; ++q) {
-                    if (c0 + q < p.C) {
-                        w[q] = __hip_atomic_load(sp + (c0 + q) * cstride, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                    } else {
-                        w[q] = 1ull << 32;
-                    }
-                }
+                for (int q = 0; q < kPollBatch; ++q)
+                    w[q] = c0 + q < p.C ? slot_load(sp + (c0 + q) * cstride) : ((slot_t)tag << 32);
 #pragma unroll
-                for (int q = 0; q < kPollBatch; ++q) all = all && (uint32_t)(w[q] >> 32) == 1u;
+                for (int q = 0; q < kPollBatch; ++q) all = all && slot_full(w[q], tag);
                 if (all) break;
                 if (!ok || spin >= kMaxSpin) {
                     ok = false;
@@ -450,8 +452,7 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
             }
 #pragma unroll
             for (int q = 0; q < kPollBatch; ++q)
-                if (c0 + q < p.C && (uint32_t)(w[q] >> 32) == 1u)
-                    acc += __uint_as_float((uint32_t)w[q]);
+                if (c0 + q < p.C && slot_full(w[q], tag)) acc += __uint_as_float((uint32_t)w[q]);
         }
         if constexpr (sizeof(T) == 2) {
             const uint32_t h = f32_to_bf16(acc);
@@ -464,22 +465,12 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
     return ok;
 }
 
-// Empty this consumer tile's slot copies for the next call: the workgroup is
-// their only reader.
-__device__ __forceinline__ void clear_slots(const DecodeParams& p, const SegView& v, int tile) {
-    const int rp = v.rp;
-    const int64_t cstride = (int64_t)p.n_groups * LORA_DECODE_MAX_M * p.a.r_max;
-    for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
-        slot_t* sp = slot_at(p, 0, tile, v.p0 + e / rp, e % rp);
-        for (int c = 0; c < p.C; ++c) slot_clear(sp + c * cstride);
-    }
-}
-
-// `first`: the consumer's first tile (group the tokens, collect S, which then
-// stays in LDS for its later tiles); `last`: its last (empty its slot copy).
+// `first`: the consumer's first tile (find the tokens, collect S, which then
+// stays in LDS for its later tiles).
 template <typename T, int RCAP>
-__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, int b, int tile,
-                                            int n0, int n1, uint4* lds, bool first, bool last) {
+__device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, int b, int sl,
+                                            int n0, int n1, uint4* lds, bool first,
+                                            uint32_t tag) {
     constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
     constexpr int CPR = RCAP / EPC;            // 16-byte chunks of a B row
     constexpr int SLD = LORA_MAX_RANK;         // row stride of S in LDS (elements)
@@ -498,11 +489,11 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
     uint4 brow[CPR];
 #pragma unroll
     for (int q = 0; q < CPR; ++q) brow[q] = ld16(B + (int64_t)n_ld * rp + min(q * EPC, rp - EPC));
-    if (first && p.by_slot) slot_group(b, a.M, a.L, v);   // b: this lane's token bucket
+    if (first && p.by_slot) slot_tokens(b, a.M, v);   // b: this lane's token bucket
     float yv[kTokGroup];
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
-        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + min(u, v.ms - 1));
+        const int m = __builtin_amdgcn_readlane(v.tl, min(u, v.ms - 1));
         yv[u] = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
     }
     // 2. S of the segment's tokens for this slice: sum of the K-chunk partials,
@@ -518,7 +509,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
         const T* At = reinterpret_cast<const T*>(a.A) + v.off2;
         const int lane = lane_id();
         for (int t = tid / kWave; t < v.ms; t += kDecWaves) {
-            const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
+            const int tok = __builtin_amdgcn_readlane(v.tok, t);
             const bool on = tok >= 0 && tok < a.K;
             if (lane < rp) {
                 const float val = on ? Io<T>::ld(At + (int64_t)tok * rp + lane) : 0.f;
@@ -532,7 +523,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
         }
     }
     if (first) {
-        if (!p.tokens) ok = collect_S<T>(p, v, tile, lds);
+        if (!p.tokens) ok = collect_S<T>(p, v, sl, tag, lds);
         if (!ok) atomicOr(p.err, kErrSpin);
         __syncthreads();
     }
@@ -569,7 +560,7 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
     //    not stored at all.
     auto row_on = [&](int t) {
         if (!p.tokens) return true;
-        const int tok = __builtin_amdgcn_readlane(v.tok, v.p0 + t);
+        const int tok = __builtin_amdgcn_readlane(v.tok, t);
         return tok >= 0 && tok < a.K;
     };
     float res[kTokGroup];
@@ -581,19 +572,15 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
 #pragma unroll
     for (int u = 0; u < kTokGroup; ++u) {
         if (u >= v.ms) break;
-        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + u);
+        const int m = __builtin_amdgcn_readlane(v.tl, u);
         if (nin && row_on(u)) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, res[u]);
     }
     for (int t = kTokGroup; t < v.ms; ++t) {
-        const int m = __builtin_amdgcn_readlane(v.my_idx, v.p0 + t);
+        const int m = __builtin_amdgcn_readlane(v.tl, t);
         const float old = Io<T>::ld(Y + (int64_t)m * p.ldy + n_ld);
         const float r = old + delta(t);
         if (nin && row_on(t)) Io<T>::st(Y + (int64_t)m * p.ldy + n_out, r);
     }
-    // 4. this workgroup is its slot copy's only reader: empty it for the next
-    //    call.  Issued after the y stores, so that no wait for a prefetched y
-    //    value has to count these stores as well.
-    if (last && !p.tokens) clear_slots(p, v, tile);
 }
 
 // bf16 consumers for ranks above 16: the deltas of 16 tokens x 64 columns
@@ -604,9 +591,9 @@ __device__ __forceinline__ void dec_consume(const DecodeParams& p, SegView& v, i
 // column n0 + 64 w + 16 cb + l % 16.  For a segment with several tokens this
 // replaces 2 rp dot products per token and column by a few MFMAs per wave.
 template <int RCAP>
-__device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView& v, int b, int tile,
+__device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView& v, int b, int sl,
                                                  int n0, int n1, uint4* lds, bool first,
-                                                 bool last) {
+                                                 uint32_t tag) {
     constexpr int NT = RCAP / 32;              // 32-wide rank steps
     constexpr int SLD = LORA_MAX_RANK;
     const LinearArgs& a = p.a;
@@ -626,9 +613,9 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView&
 #pragma unroll
         for (int t = 0; t < NT; ++t) bop[cb][t] = ld16(B + (int64_t)n * rp + min(t * 32 + lq * 8, rp - 8));
     }
-    if (first && p.by_slot) slot_group(b, a.M, a.L, v);   // b: this lane's token bucket
-    auto token_row = [&](int u) {                  // token index at sorted position p0 + u
-        return __shfl(v.my_idx, v.p0 + min(u, v.ms - 1), kWave);
+    if (first && p.by_slot) slot_tokens(b, a.M, v);   // b: this lane's token bucket
+    auto token_row = [&](int u) {                  // the segment's u-th token
+        return __shfl(v.tl, min(u, v.ms - 1), kWave);
     };
     float yv[4][4];
 #pragma unroll
@@ -642,7 +629,7 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView&
     }
     // 2. S of the segment's tokens (first tile only; it stays in LDS)
     if (first) {
-        const bool ok = collect_S<uint16_t>(p, v, tile, lds);
+        const bool ok = collect_S<uint16_t>(p, v, sl, tag, lds);
         if (!ok) atomicOr(p.err, kErrSpin);
         __syncthreads();
     }
@@ -683,8 +670,61 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView&
             }
         }
     }
-    // 4. empty the slot copies (after the y stores, as in dec_consume)
-    if (last) clear_slots(p, v, tile);
+}
+
+// Ids mode: an id outside [-1, L) is treated as "no adapter" and reported in
+// the error word (one wavefront).
+__device__ __forceinline__ void report_bad_ids(const DecodeParams& p, const int32_t* ids, int M,
+                                               int L) {
+    if (!ids || !p.err) return;
+    const int lane = lane_id();
+    const int id = ids[min(lane, M - 1)];
+    if (__ballot(lane < M && (id < -1 || id >= L)) != 0ull && lane == 0) atomicOr(p.err, kErrBadId);
+}
+
+// Consumer unit u: segment (or slot) u / n_groups, and G consecutive
+// 256-column tiles of one slice; S is collected once, on the first tile.
+template <typename T>
+__device__ __forceinline__ void dec_consumer(const DecodeParams& p, const ViewArgs& va, int u,
+                                             uint4* lds, uint32_t tag) {
+    const LinearArgs& a = p.a;
+    const int s = u / p.n_groups;
+    const int g = u % p.n_groups;
+    SegView v;
+    int b = 0;
+    if (p.by_slot) {
+        const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
+        v = slot_head(va, s);
+        b = token_bucket(tl, p.enabled, va.L);
+        if (v.rp == 0 || !slot_used(b, va.M, s)) return;
+    } else {
+        v = seg_view(p, va, s);
+        if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
+    }
+    int sl = 0;
+    while (sl + 1 < a.n_sl && g >= p.group_start[sl + 1]) ++sl;
+    const int tb = p.tile_start[sl] + (g - p.group_start[sl]) * p.G;
+    const int te = min(tb + p.G, p.tile_start[sl + 1]);
+    for (int t = tb; t < te; ++t) {
+        const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
+        const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
+        const bool first = t == tb;
+        if (v.rp <= 16)
+            dec_consume<T, 16>(p, v, b, sl, n0, n1, lds, first, tag);
+        else if constexpr (sizeof(T) == 2) {
+            if (p.tokens) {
+                if (v.rp <= 32) dec_consume<T, 32>(p, v, b, sl, n0, n1, lds, first, tag);
+                else dec_consume<T, 64>(p, v, b, sl, n0, n1, lds, first, tag);
+            } else if (v.rp <= 32) {
+                dec_consume_mfma<32>(p, v, b, sl, n0, n1, lds, first, tag);
+            } else {
+                dec_consume_mfma<64>(p, v, b, sl, n0, n1, lds, first, tag);
+            }
+        } else if (v.rp <= 32)
+            dec_consume<T, 32>(p, v, b, sl, n0, n1, lds, first, tag);
+        else
+            dec_consume<T, 64>(p, v, b, sl, n0, n1, lds, first, tag);
+    }
 }
 
 template <typename T>
@@ -703,58 +743,24 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __r
             write_wave_segments(g, a.M, a.L, p.out.sorted_idx, p.out.seg_indptr,
                                 p.out.req_to_lora, p.out.num_segments, p.out.tile_info,
                                 p.out.tile_rows, p.out.num_tiles);
+            report_bad_ids(p, ids, M, L);
         }
         return;
     }
+    const uint32_t tag = launch_tag();
     if ((int)blockIdx.x < p.grid1) {
         const ViewArgs va{ids, rank, a_off, M, L, nullptr, nullptr};
         if constexpr (sizeof(T) == 2)
-            dec_produce_mfma(p, va, blockIdx.x, reinterpret_cast<float*>(lds));
+            dec_produce_mfma(p, va, blockIdx.x, reinterpret_cast<float*>(lds), tag);
         else
-            dec_produce<T>(p, va, blockIdx.x);
-        return;
-    }
-    const LinearArgs& a = p.a;
-    const int u = blockIdx.x - p.grid1;
-    const int s = u / p.n_groups;
-    const int g = u % p.n_groups;
-    const ViewArgs va{ids, rank, b_off, M, L, p.tokens, p.tokens ? a_off : nullptr};
-    SegView v;
-    int b = 0;
-    if (p.by_slot) {
-        const TokenLoad tl = load_token(ids, p.enabled, M, L);
-        v = slot_head(va, s);
-        b = token_bucket(tl, p.enabled, L);
-        if (v.rp == 0 || !slot_used(b, M, s)) return;
+            dec_produce<T>(p, va, blockIdx.x, tag);
     } else {
-        v = seg_view(p, va, s);
-        if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
+        const ViewArgs va{ids, rank, b_off, M, L, p.tokens, p.tokens ? a_off : nullptr};
+        dec_consumer<T>(p, va, blockIdx.x - p.grid1, lds, tag);
     }
-    // consumer g: tiles tb .. te - 1 of one slice, S collected once
-    int sl = 0;
-    while (sl + 1 < a.n_sl && g >= p.group_start[sl + 1]) ++sl;
-    const int tb = p.tile_start[sl] + (g - p.group_start[sl]) * p.G;
-    const int te = min(tb + p.G, p.tile_start[sl + 1]);
-    for (int t = tb; t < te; ++t) {
-        const int n0 = (int)(a.slice_off[sl] + (int64_t)(t - p.tile_start[sl]) * kNTile);
-        const int n1 = (int)min((int64_t)n0 + kNTile, a.slice_off[sl + 1]);
-        const bool first = t == tb, last = t + 1 == te;
-        if (v.rp <= 16)
-            dec_consume<T, 16>(p, v, b, g, n0, n1, lds, first, last);
-        else if constexpr (sizeof(T) == 2) {
-            if (p.tokens) {
-                if (v.rp <= 32) dec_consume<T, 32>(p, v, b, g, n0, n1, lds, first, last);
-                else dec_consume<T, 64>(p, v, b, g, n0, n1, lds, first, last);
-            } else if (v.rp <= 32) {
-                dec_consume_mfma<32>(p, v, b, g, n0, n1, lds, first, last);
-            } else {
-                dec_consume_mfma<64>(p, v, b, g, n0, n1, lds, first, last);
-            }
-        } else if (v.rp <= 32)
-            dec_consume<T, 32>(p, v, b, g, n0, n1, lds, first, last);
-        else
-            dec_consume<T, 64>(p, v, b, g, n0, n1, lds, first, last);
-    }
+    // without a table writer, the first workgroup checks the ids once its
+    // own work is done (off the path of its weight loads)
+    if (!p.writer && blockIdx.x == 0 && threadIdx.x < kWave) report_bad_ids(p, ids, M, L);
 }
 
 static hipError_t launch_decode(DecodeParams& p, unsigned grid, hipStream_t st) {
@@ -816,7 +822,7 @@ constexpr int kResident = 1536;
 
 hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
                                const SegOut& out, const void* x, int64_t ldx, void* y,
-                               int64_t ldy, void* ws, hipStream_t st) {
+                               int64_t ldy, void* ws, int32_t* err, hipStream_t st) {
     DecodeParams p{};
     p.a = a;
     p.ids = ids;
@@ -828,9 +834,9 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     p.y = y;
     p.ldy = ldy;
     p.by_slot = (ids && a.L <= a.s_max) ? 1 : 0;
-    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.r_max, ntiles_total(a));
+    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols);
     char* base = reinterpret_cast<char*>(ws);
-    p.err = reinterpret_cast<int*>(base + L.header);
+    p.err = err ? err : &reinterpret_cast<WsHeader*>(base + L.header)->error;
     p.slots = reinterpret_cast<slot_t*>(base + L.slots);
     static_assert(512 * dec_steps<uint16_t>() == kDecKChunk && 512 * dec_steps<float>() == kDecKChunk,
                   "producer K chunk");

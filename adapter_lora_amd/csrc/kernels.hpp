@@ -58,14 +58,13 @@ constexpr int kDecKChunk = 1024;
 // Workspace layout (bytes from the start), see api.cpp.
 struct LinearWs {
     size_t header;      // WsHeader
-    size_t slots;       // slot_t[Cd][n_tiles][64][r_max] (decode exchange, one copy per consumer tile)
+    size_t slots;       // slot_t[Cd][64][cols] (decode exchange: K chunk, sorted position, S column)
     size_t partial;     // float[C][M][cols]   (MFMA shrink partial sums)
     size_t S;           // float[M][cols]      (S between shrink and expand)
     size_t total;
 };
 
-// n_tiles: 256-column output tiles over all slices (ntiles_total)
-LinearWs linear_ws_layout(int M, int K, int cols, int r_max, int n_tiles);
+LinearWs linear_ws_layout(int M, int K, int cols);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
@@ -103,9 +102,10 @@ struct SegOut {
 // from the table in `a`; otherwise every workgroup groups the batch from
 // `ids` (and `enabled`, may be null) on chip and one extra workgroup writes
 // the segment table into `out` when out.sorted_idx is not null.
+// `err`: where errors are reported (null: the workspace's own error word).
 hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const int32_t* enabled,
                                const SegOut& out, const void* x, int64_t ldx, void* y,
-                               int64_t ldy, void* ws, hipStream_t st);
+                               int64_t ldy, void* ws, int32_t* err, hipStream_t st);
 
 // Single-launch embedding decode (M <= LORA_DECODE_MAX_M): the fused decode
 // kernel's consumers only, with S rows looked up from the transposed A table

@@ -174,7 +174,7 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
     const int C = bf16 ? (a.K + kShrinkK - 1) / kShrinkK : kchunks(a.K);
     const int G = bf16 ? (a.cols + kGroupCols - 1) / kGroupCols : 1;
     const int units = a.max_tiles * C * G;
-    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols, a.r_max, ntiles_total(a));
+    const LinearWs L = linear_ws_layout(a.M, a.K, a.cols);
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + L.partial);
     if (bf16)
         hipLaunchKernelGGL(k_shrink_dense<uint16_t>, dim3(grid_of(units)), dim3(kTileThreads), 0, st,

@@ -20,15 +20,18 @@ Protocol:
     rotation, bracketed by one HIP event pair on its stream; elapsed / K is
     its mean duration, and algorithmic bytes per launch / that duration gives
     the roofline figure against 8 TB/s;
-  * a plain streaming copy (bf16 negation, read + write) of the same byte
-    count and of 256 MB is timed the same way as the practical ceiling and as
-    the calibration kernel for the FETCH_SIZE / WRITE_SIZE counter runs;
+  * a hand-written streaming kernel (adapter_lora_amd/csrc/stream_copy.hip)
+    moving the decode step's byte mix (its reads, then its y writes) is timed
+    the same way, at the decode launch's own grid and at the best grid of a
+    sweep, as the practical ceiling; the same kernel copying 128 MB is the
+    calibration kernel for the FETCH_SIZE / WRITE_SIZE counter runs;
   * HBM traffic per launch comes from those counter runs, kept as a summary
     under profiles/ with a hash of the kernel's sources; it is reported only
     while the sources still match the hash;
   * the same step is also captured as a HIP graph (one per input copy) and
     replayed, reported under "graph_replay" as context;
-  * the oracle (fp64 CPU) is timed on the host on a bounded sample.
+  * the oracle (fp64 CPU, one BLAS thread) is timed on the host on a bounded
+    sample of each workload, median of three runs.
 Other configurations (prefill, stacked QKV / gate-up, MoE, and the
 LM-head and embedding LoRA decode cases: 32 tokens, 32000-token vocabulary,
 4096 hidden) are measured the same way and reported under "extra" as
@@ -125,19 +128,92 @@ def back_to_back(launch, n):
     return t0.elapsed_time(t1) / n
 
 
-def copy_ceiling(nbytes, n=50):
-    """A plain streaming copy (out = -in, bf16) moving `nbytes` in total
-    (nbytes/2 read, nbytes/2 written), rotated over enough buffers to miss the
-    Infinity Cache.  Returns GB/s over the back-to-back launches."""
+_STREAM = None
+
+
+def stream_lib():
+    """The streaming reference kernel's library (built beside libmlora.so)."""
+    global _STREAM
+    if _STREAM is None:
+        import ctypes
+        path = os.path.join(ROOT, "adapter_lora_amd", "libmlora_stream.so")
+        if not os.path.exists(path):
+            raise SystemExit(f"{path} not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.mlora_stream.restype = ctypes.c_int
+        lib.mlora_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        _STREAM = lib
+    return _STREAM
+
+
+def stream_time(rd_bytes, wr_bytes, n, grid=0, unroll=4, rotation=None):
+    """Mean duration (ms) of the streaming kernel reading rd_bytes and writing
+    wr_bytes, over n back-to-back launches on buffers rotated so that the
+    reads miss the Infinity Cache."""
     import torch
-    elems = max(1, nbytes // 4)
-    R = max(2, int(np.ceil(2 * MALL_BYTES / (2 * elems * 2))))
-    R = min(R, 64)
-    src = [torch.randn(elems, device="cuda").to(torch.bfloat16) for _ in range(R)]
-    dst = [torch.empty_like(t) for t in src]
-    ms = back_to_back(lambda i: torch.neg(src[i % R], out=dst[i % R]), n)
-    return {"bytes": 4 * elems, "ms": ms, "gbs": 4 * elems / (ms * 1e-3) / 1e9, "rotation": R,
-            "kernel": "torch neg (bf16), read + write"}
+    import adapter_lora_amd as ml
+    lib = stream_lib()
+    rd = (rd_bytes + 15) // 16 * 16
+    wr = min((wr_bytes + 15) // 16 * 16, rd)
+    R = rotation or max(2, min(64, int(np.ceil(2 * MALL_BYTES / rd))))
+    src = [torch.randint(0, 255, (rd,), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dst = [torch.empty(max(wr, 16), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sh = ml.stream_handle()
+
+    def launch(i):
+        rc = lib.mlora_stream(src[i % R].data_ptr(), rd, dst[i % R].data_ptr(), wr, grid, unroll, sh)
+        if rc != 0:
+            raise RuntimeError(f"mlora_stream failed ({rc})")
+    ms = back_to_back(launch, n)
+    del src, dst
+    return ms, R
+
+
+def stream_ceiling(rd_bytes, wr_bytes, n, launch_grid):
+    """The streaming kernel on the given byte mix: at `launch_grid` workgroups
+    of 256 threads (unroll chosen so that one pass covers the reads), and the
+    best of a sweep over loads in flight per thread (one pass each) and
+    grid-stride launches of 256..2048 workgroups."""
+    words = (rd_bytes + 15) // 16
+    u_at = 1
+    while u_at < 16 and launch_grid * 256 * u_at < words:
+        u_at *= 2
+    ms_at, R = stream_time(rd_bytes, wr_bytes, n, launch_grid, u_at)
+    sweep = []
+    for u in (1, 2, 4, 8, 16):
+        sweep.append((stream_time(rd_bytes, wr_bytes, n, 0, u, R)[0], 0, u))
+    for g in (256, 512, 1024, 2048):
+        sweep.append((stream_time(rd_bytes, wr_bytes, n, g, 4, R)[0], g, 4))
+    best = min(sweep)
+    tot = rd_bytes + wr_bytes
+    res = {"kernel": "k_stream (hand-written, stream_copy.hip)", "read_bytes": rd_bytes,
+           "write_bytes": wr_bytes, "rotation": R,
+           "at_launch_grid": {"workgroups": launch_grid, "unroll": u_at, "ms": ms_at,
+                              "gbs": tot / (ms_at * 1e-3) / 1e9},
+           "best": {"workgroups": best[1] or int(-(-words // (256 * best[2]))),
+                    "unroll": best[2], "ms": best[0], "gbs": tot / (best[0] * 1e-3) / 1e9},
+           "sweep_ms": {f"{'auto' if g == 0 else g}x{u}": round(m, 5) for m, g, u in sweep}}
+    return res
+
+
+def copy_calibration(n=20):
+    """The streaming kernel copying 128 MB (read) into 128 MB (write): the
+    kernel whose FETCH_SIZE / WRITE_SIZE readings calibrate the counter runs."""
+    ms, R = stream_time(128 << 20, 128 << 20, n, 0, 4, rotation=2)
+    return {"bytes": 256 << 20, "ms": ms, "gbs": (256 << 20) / (ms * 1e-3) / 1e9,
+            "kernel": "k_stream copy, 128 MB read + 128 MB written"}
+
+
+def decode_launch_grid(case):
+    """Workgroups of the single-launch decode for this case: producers
+    (slots x 16-row A blocks x 1024-wide K chunks), consumers (slots x
+    256-column tiles), and the workgroup that writes the segment table."""
+    s_max = min(case.L, case.M)
+    r_max = max(16, max(-(-r // 16) * 16 for r in case.ranks))
+    C = -(-case.K // 1024)
+    tiles = sum(-(-n // 256) for n in case.slice_sizes)
+    return s_max * (case.n_slices * r_max // 16) * C + s_max * tiles + 1
 
 
 def source_hash(files):
@@ -406,7 +482,7 @@ def bench_moe(case, steps, warmup):
 
     def step(i):
         w, x, c1, c3 = copies[i % R]
-        ml.lora_moe_align_run(tid, ids, en, case.E, al)
+        ml.lora_moe_align(tid, ids, en, case.E, al)
         ml.lora_moe_gate_up_add(w, x, case.topk, al, c1, ws)
         ml.lora_moe_silu_and_mul(c1, c2)
         ml.lora_moe_down_add(w, c2, case.M, case.topk, al, c3, ws)
@@ -435,28 +511,76 @@ def bench_moe(case, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- oracle
-def cpu_baseline(case, seconds):
-    """The oracle as it stands, on the host: whole decode batches repeated
-    until about `seconds` of CPU time have been spent."""
-    from threadpoolctl import threadpool_info
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(fn, units, seconds):
+    """Median over three runs of units / second for `fn` repeated until each
+    run has taken about seconds / 3, with the BLAS pool held to one thread
+    (so that `cores` is what the oracle actually used)."""
+    from threadpoolctl import threadpool_limits
+    rates = []
+    reps_tot, el_tot = 0, 0.0
+    with threadpool_limits(limits=1):
+        for _ in range(3):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds / 3:
+                    break
+            rates.append(units * reps / el)
+            reps_tot, el_tot = reps_tot + reps, el_tot + el
+    return float(np.median(rates)), reps_tot, el_tot
+
+
+def cpu_baseline_linear(case, seconds, tokens=None):
+    """The dense oracle (fp64 per-token loop) on the first `tokens` tokens of
+    the batch (all when None), as tokens with an adapter per second."""
     from oracle import lora as O
+    M = case.M if tokens is None else min(tokens, case.M)
     A = [a.values for a in case.A]
     B = [b.values for b in case.B]
-    m_valid = int(sum(1 for i in case.ids if i >= 0))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.lora_linear(case.x.values, case.ids, A, B, case.ranks, case.slice_sizes,
-                      case.y_base.values)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": m_valid * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full decode batches (M=32, {m_valid} tokens with an adapter) "
-                      f"in {el:.1f} s, fp64 numpy per-token loop",
-            "host_cpus": len(os.sched_getaffinity(0))}
+    x, ids, yb = case.x.values[:M], case.ids[:M], case.y_base.values[:M]
+    m_valid = int(sum(1 for i in ids if 0 <= i < case.L and case.ranks[i] > 0))
+    rate, reps, el = _oracle_rate(
+        lambda: O.lora_linear(x, ids, A, B, case.ranks, case.slice_sizes, yb), m_valid, seconds)
+    return {"value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} passes over {M} of the {case.M} tokens ({m_valid} with an "
+                      f"adapter) in {el:.1f} s, median of 3 runs; fp64 numpy per-token loop, "
+                      f"one BLAS thread",
+            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_moe(case, seconds, tokens=32):
+    """The MoE oracle's four stages (gate/up delta, silu-and-mul, down delta,
+    top-k reduce) on the first `tokens` tokens, as tokens per second."""
+    from oracle import moe as OM
+    M, k = min(tokens, case.M), case.topk
+    sl = slice(0, M * k)
+    args = (case.topk_ids[:M], case.ids[:M], case.adapter_enabled)
+    x, c1, c3 = case.x.values[:M], case.cache1.values[sl], case.cache3.values[sl]
+    A_gu, B_gu, A_d, B_d = (t.values for t in (case.A_gu, case.B_gu, case.A_d, case.B_d))
+    w = case.topk_weights[:M]
+
+    def run():
+        g = OM.moe_gate_up_add(x, c1, *args, A_gu, B_gu, case.shared_outer)
+        c2 = OM.silu_and_mul(g)
+        c3o = OM.moe_down_add(c2, c3, *args, A_d, B_d, case.shared_outer)
+        OM.topk_reduce(c3o, w)
+    rate, reps, el = _oracle_rate(run, M, seconds)
+    return {"value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} passes over {M} of the {case.M} tokens (all four stages) in "
+                      f"{el:.1f} s, median of 3 runs; fp64 numpy per-pair loop, one BLAS thread",
+            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 # ----------------------------------------------------------------------------- main
@@ -474,20 +598,26 @@ def main():
 
     results = {}
     dec_case = W.decode_bf16(0)
+    cases = {}                      # workloads that also get an oracle timing
     if want("decode"):
         results["decode_bf16"] = bench_linear(dec_case, args.steps, args.warmup,
                                               "k_decode_fused<uint16_t>", single_launch=True)
     if want("prefill"):
-        results["prefill_bf16"] = bench_linear(W.prefill_bf16(0), args.steps, args.warmup,
+        cases["prefill_bf16"] = (W.prefill_bf16(0), 64)
+        results["prefill_bf16"] = bench_linear(cases["prefill_bf16"][0], args.steps, args.warmup,
                                                "k_shrink_dense + k_reduce_partials + k_expand_dense")
     if want("qkv"):
-        results["stacked_qkv_bf16"] = bench_linear(W.stacked_bf16("qkv", 0), args.steps,
+        cases["stacked_qkv_bf16"] = (W.stacked_bf16("qkv", 0), 64)
+        results["stacked_qkv_bf16"] = bench_linear(cases["stacked_qkv_bf16"][0], args.steps,
                                                    args.warmup, "shrink + reduce + expand")
     if want("gate_up"):
-        results["stacked_gate_up_bf16"] = bench_linear(W.stacked_bf16("gate_up", 0), args.steps,
-                                                       args.warmup, "shrink + reduce + expand")
+        cases["stacked_gate_up_bf16"] = (W.stacked_bf16("gate_up", 0), 32)
+        results["stacked_gate_up_bf16"] = bench_linear(cases["stacked_gate_up_bf16"][0],
+                                                       args.steps, args.warmup,
+                                                       "shrink + reduce + expand")
     if want("moe"):
-        results["moe_bf16"] = bench_moe(W.moe_case(0), args.steps, args.warmup)
+        cases["moe_bf16"] = (W.moe_case(0), 16)
+        results["moe_bf16"] = bench_moe(cases["moe_bf16"][0], args.steps, args.warmup)
     if want("moe_shared"):
         results["moe_shared_outer_bf16"] = bench_moe(W.moe_case(0, shared_outer=True),
                                                      args.steps, args.warmup)
@@ -503,11 +633,23 @@ def main():
                                                            args.warmup)
 
     head = results.get("decode_bf16")
-    ceiling = {}
+    ceiling = None
     if head is not None:
-        ceiling["same_bytes_as_decode"] = copy_ceiling(head["alg_bytes"], args.steps)
-    ceiling["256MB"] = copy_ceiling(256 << 20, 20)
-    cpu = None if args.no_cpu or head is None else cpu_baseline(dec_case, args.cpu_seconds)
+        # the decode step's mix: everything it reads, then the y rows it writes
+        wr = head["m_valid"] * dec_case.N * 2
+        ceiling = stream_ceiling(head["alg_bytes"] - wr, wr, args.steps,
+                                 decode_launch_grid(dec_case))
+        ceiling["decode_kernel_over_ceiling_at_launch_grid"] = (
+            head["ms_kernel_b2b"] / ceiling["at_launch_grid"]["ms"])
+        ceiling["decode_kernel_over_best_ceiling"] = head["ms_kernel_b2b"] / ceiling["best"]["ms"]
+    calib = copy_calibration()
+    cpu = None
+    if not args.no_cpu:
+        if head is not None:
+            cpu = cpu_baseline_linear(dec_case, args.cpu_seconds)
+        for key, (case, tokens) in cases.items():
+            f = cpu_baseline_moe if key.startswith("moe") else cpu_baseline_linear
+            results[key]["cpu_baseline"] = f(case, args.cpu_seconds / 4, tokens)
     traffic = measured_traffic()
     line = {
         "metric": METRIC,
@@ -532,9 +674,15 @@ def main():
             "traffic": None if traffic is None else traffic["total_bytes"],
             "kernel": head["kernel"], "kernel_ms": head["ms_kernel_b2b"],
             "alg_bytes_per_launch": head["alg_bytes"],
+            "vs_stream_ceiling": None if ceiling is None else {
+                "at_launch_grid": ceiling["decode_kernel_over_ceiling_at_launch_grid"],
+                "best": ceiling["decode_kernel_over_best_ceiling"],
+                "note": "decode kernel time / time of the hand-written streaming kernel "
+                        "moving the same bytes"},
             "traffic_detail": traffic},
         "cpu_baseline": cpu,
-        "copy_ceiling": ceiling,
+        "ceiling": ceiling,
+        "counter_calibration_copy": calib,
         "graph_replay": None if head is None else {
             "ms_per_step": head["ms_per_step_graph"],
             "tokens_per_s": head["m_valid"] / (head["ms_per_step_graph"] * 1e-3),

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLORA_ABI_VERSION 4
+#define MLORA_ABI_VERSION 5
 
 typedef enum lora_status {
     LORA_OK = 0,
@@ -145,10 +145,20 @@ lora_status lora_workspace_init(void* workspace, size_t bytes, hipStream_t strea
 
 /*
  * Read (and clear) the sticky device error word of a workspace.  Synchronises
- * `stream`.  *out receives 0 when no kernel reported an error; bit 0 means a
- * kernel gave up waiting on data from another workgroup (results of that call
- * are not valid and the workspace must be re-initialised).
+ * `stream`.  *out receives 0 when no kernel reported an error, else an OR of
+ *   LORA_DEVERR_WAIT    a kernel gave up waiting on data from another
+ *                       workgroup; the results of that call are not valid
+ *                       (the workspace itself stays usable);
+ *   LORA_DEVERR_BAD_ID  lora_fused_decode met a token id outside [-1, L); the
+ *                       token was treated as one without an adapter.  An id
+ *                       past the table would index a slot that does not
+ *                       exist, the mixed-up-rows failure of the Ascend
+ *                       walkthrough's s4.1 troubleshooting table, so it is
+ *                       reported and never followed.
  */
+#define LORA_DEVERR_WAIT 1
+#define LORA_DEVERR_BAD_ID 2
+
 lora_status lora_read_device_error(void* workspace, int32_t* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- weight table (load time) */
@@ -391,7 +401,7 @@ typedef struct lora_moe_weights {
  * caller; max_tokens_padded is a multiple of block_size_m and at least
  * lora_moe_align_capacity(M, topk, E, block_size_m).
  */
-typedef struct lora_moe_align {
+typedef struct lora_moe_align_buffers {
     int32_t* sorted_token_ids;   /* [L, max_tokens_padded]: flat pairs m*topk+k, sentinel M*topk */
     int32_t* expert_ids;         /* [L, max_tokens_padded / block_size_m]: -1 for unused blocks */
     int32_t* ntpp;               /* [L]: padded list length per adapter */
@@ -407,15 +417,25 @@ int32_t lora_moe_align_capacity(int32_t M, int32_t topk, int32_t E, int32_t bloc
  * the pairs f = m*topk + k with ids[m] == l and topk_ids[m, k] == e in
  * increasing f, each (l, e) bucket padded with the sentinel M*topk to a
  * multiple of block_size_m; expert_ids records e per block.  Disabled or
- * idle adapters get ntpp = 0 and a row of sentinels.
+ * idle adapters get ntpp = 0 and a row of sentinels.  Ids outside [0, L)
+ * belong to no list.
  *   topk_ids device [M, topk] int32 in [0, E); ids device [M] (-1 = none);
- *   adapter_enabled device [L].
+ *   adapter_enabled device [L];
+ *   sorted_token_ids device [L, max_tokens_padded] (out);
+ *   expert_ids device [L, max_tokens_padded / block_size_m] (out, -1 for
+ *       unused blocks);
+ *   ntpp device [L] (out): padded list length per adapter.
  * One workgroup per adapter.  M*topk <= 2^24, E <= 256, topk <= 16,
- * block_size_m a multiple of 16 in [16, 256].
+ * block_size_m a multiple of 16 in [16, 256], max_tokens_padded a multiple
+ * of block_size_m and at least lora_moe_align_capacity(M, topk, E,
+ * block_size_m).  The outputs are the fields of a lora_moe_align_t that the
+ * two delta calls read.
  */
-lora_status lora_moe_align_run(const int32_t* topk_ids, const int32_t* ids,
-                               const int32_t* adapter_enabled, int32_t M, int32_t topk, int32_t E,
-                               int32_t L, const lora_moe_align_t* out, hipStream_t stream);
+lora_status lora_moe_align(const int32_t* topk_ids, const int32_t* ids,
+                           const int32_t* adapter_enabled, int32_t M, int32_t topk, int32_t E,
+                           int32_t L, int32_t block_size_m, int32_t max_tokens_padded,
+                           int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
+                           hipStream_t stream);
 
 /* Bytes of device workspace needed by the two MoE delta calls. */
 size_t lora_moe_workspace_size(const lora_moe_weights_t* w, int32_t max_tokens_padded);

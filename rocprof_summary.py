@@ -11,7 +11,7 @@
       WORKGROUPS workgroups when given: the single-launch form) from two counter runs
       (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by what
       the same counter reads for the 256 MB streaming copy that bench.py runs
-      (the torch bf16 negation: half of its bytes read, half written).
+      (the hand-written k_stream kernel: 128 MB read, 128 MB written).
 
 The traffic summary carries a hash of the decode kernel's sources; bench.py
 reports the figure only while that hash still matches.
@@ -25,8 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DECODE_KERNEL = "k_decode_fused"
-CALIB_KERNEL = "neg_kernel"
-CALIB_BYTES = 256 << 20          # bench.copy_ceiling(256 MB): 128 MB read + 128 MB written
+CALIB_KERNEL = "k_stream"
+CALIB_BYTES = 256 << 20          # bench.copy_calibration(): 128 MB read + 128 MB written
 
 
 def _rows(directory, suffix):
@@ -42,8 +42,6 @@ def _rows(directory, suffix):
 
 def short(name):
     name = name.replace("void ", "")
-    if "neg_kernel" in name:
-        return "torch neg (bf16 copy)"
     if "(" in name:
         name = name[:name.index("(")]
     return name[:70]
@@ -81,10 +79,10 @@ def traffic(fetch_dir, write_dir, fetch_cmd, write_cmd, workgroups=None):
     wr = _rows(write_dir, "counter_collection.csv")
     kf, nkf, kf_med = _per_dispatch_kib(fr, "FETCH_SIZE", DECODE_KERNEL, wg)
     kw, nkw, kw_med = _per_dispatch_kib(wr, "WRITE_SIZE", DECODE_KERNEL, wg)
-    # the calibration copies of bench.copy_ceiling have two sizes; take the 256 MB ones
+    # the streaming kernel also runs at the decode byte count; take the 128 MB copies
     half = CALIB_BYTES / 2
-    cal = [v for v in _all(fr, "FETCH_SIZE", CALIB_KERNEL) if v * 1024 > 0.5 * half]
-    calw = [v for v in _all(wr, "WRITE_SIZE", CALIB_KERNEL) if v * 1024 > 0.5 * half]
+    cal = [v for v in _all(fr, "FETCH_SIZE", CALIB_KERNEL) if v * 1024 > 0.25 * half]
+    calw = [v for v in _all(wr, "WRITE_SIZE", CALIB_KERNEL) if v * 1024 > 0.25 * half]
     f_fac = (sum(cal) / len(cal)) * 1024 / half
     w_fac = (sum(calw) / len(calw)) * 1024 / half
     fetch = kf * 1024 / f_fac

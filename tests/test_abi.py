@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["lora_build_segments", "lora_shrink", "lora_expand_add", "lora_shrink_expand_add",
               "lora_fused_decode", "lora_linear_fused",
-              "lora_moe_align_run", "lora_moe_gate_up_add", "lora_moe_silu_and_mul",
+              "lora_moe_align", "lora_moe_gate_up_add", "lora_moe_silu_and_mul",
               "lora_moe_down_add", "lora_moe_topk_reduce", "lora_workspace_size",
               "lora_status_string", "lora_read_device_error", "lora_table_plan",
               "lora_pack_adapter"]:
@@ -115,12 +115,74 @@ def test_argument_checks_fail_before_any_launch():
                                  some, 128, some, 1 << 20, null) == INV      # ldw < K
     assert lib.lora_linear_fused(ctypes.byref(w2), some, 128, some, 128, 8, ctypes.byref(seg),
                                  some, 128, some, 16, null) == INV           # workspace short
-    ma = _abi.lora_moe_align_t()
-    ma.max_tokens_padded, ma.block_size_m = 100, 64               # not a multiple of the block
-    assert lib.lora_moe_align_run(null, null, null, 4, 2, 8, 2, ctypes.byref(ma), null) == INV
+    # MoE align: capacity not a multiple of the block; then outputs missing
+    assert lib.lora_moe_align(some, some, some, 4, 2, 8, 2, 64, 100, some, some, some,
+                              null) == INV
+    assert lib.lora_moe_align(some, some, some, 4, 2, 8, 2, 64, 128, null, some, some,
+                              null) == INV
+    assert lib.lora_moe_align(some, some, null, 4, 2, 8, 2, 64, 128, some, some, some,
+                              null) == INV                                  # mask null
     assert lib.lora_moe_silu_and_mul(1, null, 0, null, 0, 4, 12, null) == INV   # I % 8
     assert lib.lora_moe_topk_reduce(1, null, 0, null, null, 0, 4, 0, 64, null) == INV
     assert lib.lora_table_plan(2, (ctypes.c_int32 * 2)(8, 65), 1, 64, 64,
                                (ctypes.c_int32 * 2)(), (ctypes.c_int64 * 2)(),
                                (ctypes.c_int64 * 2)(), ctypes.byref(ctypes.c_int64()),
                                ctypes.byref(ctypes.c_int64())) == INV           # rank > 64
+
+
+# ------------------------------------------------------------------ binding checks
+class _FakeTable:
+    """Metadata of a table, enough for the binding's checks (which run before
+    anything touches the device or the library)."""
+
+    def __init__(self, dtype, K=64, N=32, L=4, cols=16):
+        import torch
+        self.dtype, self.K, self.N, self.L, self.cols = dtype, K, N, L, cols
+
+
+def test_binding_rejects_mismatched_operands_before_any_launch():
+    """An operand whose dtype differs from the table's (the kernels would
+    store elements of the table's size into it), an x whose width is not K,
+    a y narrower than N and a short S are refused by the binding itself."""
+    import torch
+    import adapter_lora_amd as ml
+    bf, f32 = torch.bfloat16, torch.float32
+    tb = _FakeTable(bf)
+    ids = torch.zeros(4, dtype=torch.int32)
+    x, y = torch.zeros(4, 64, dtype=bf), torch.zeros(4, 32, dtype=bf)
+    for bad in [dict(x=x.float()), dict(y=y.float()), dict(x=torch.zeros(4, 72, dtype=bf)),
+                dict(y=torch.zeros(4, 24, dtype=bf))]:
+        args = dict(x=x, y=y)
+        args.update(bad)
+        with pytest.raises(ml.LoraError, match="weights are|columns"):
+            ml.lora_fused_decode(tb, ids, args["x"], args["y"], None)
+        with pytest.raises(ml.LoraError, match="weights are|columns"):
+            ml.lora_shrink_expand_add(tb, args["x"], None, args["y"], None)
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_shrink(tb, x.float(), None, None, None)
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_linear_fused(tb, torch.zeros(32, 64, dtype=f32), x, None, y, None)
+    with pytest.raises(ml.LoraError, match="S must hold"):
+        ml.lora_expand_add(tb, torch.zeros(4 * 16 - 1, dtype=f32), None, y)
+    with pytest.raises(ml.LoraError, match="weights are|columns"):
+        ml.lora_embedding_decode(tb, ids, ids, y.float())
+    # the same calls with matching operands get past these checks and stop
+    # at the device check (CPU tensors), not at a dtype or shape complaint
+    with pytest.raises(ml.LoraError, match="GPU|device"):
+        ml.lora_fused_decode(tb, ids, x, y, None)
+    with pytest.raises(ml.LoraError, match="GPU|device"):
+        ml.lora_shrink_expand_add(tb, x, None, y, None)
+    # MoE: caches of another dtype or width
+    mw = type("W", (), dict(dtype=bf, H=64, I=32))()
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_moe_gate_up_add(mw, x, 2, None, torch.zeros(8, 64, dtype=f32), None)
+    with pytest.raises(ml.LoraError, match="columns"):
+        ml.lora_moe_gate_up_add(mw, x, 2, None, torch.zeros(8, 60, dtype=bf), None)
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_moe_down_add(mw, torch.zeros(8, 32, dtype=f32), 4, 2, None,
+                             torch.zeros(8, 64, dtype=bf), None)
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_moe_silu_and_mul(torch.zeros(8, 64, dtype=bf), torch.zeros(8, 32, dtype=f32))
+    with pytest.raises(ml.LoraError, match="weights are"):
+        ml.lora_moe_topk_reduce(torch.zeros(8, 64, dtype=bf), torch.zeros(4, 2, dtype=f32),
+                                torch.zeros(4, 64, dtype=f32))

@@ -34,7 +34,7 @@ def mask_for(L, seed, p_on=0.7):
     return m
 
 
-def run_decode(ml, case, enabled=None, reps=1, with_table=True):
+def run_decode(ml, case, enabled=None, reps=1, with_table=True, expect_err=0):
     table = table_for(case)
     ids = torch.from_numpy(case.ids).cuda()
     seg = ml.Segments(case.M, case.L) if with_table else None
@@ -45,7 +45,7 @@ def run_decode(ml, case, enabled=None, reps=1, with_table=True):
     for _ in range(reps):
         ml.lora_fused_decode(table, ids, x, y, ws, seg=seg, adapter_enabled=en)
     torch.cuda.synchronize()
-    assert ml.lora_read_device_error(ws.buf) == 0
+    assert ml.lora_read_device_error(ws.buf) == expect_err
     return to_f64(y), seg
 
 
@@ -63,10 +63,10 @@ def check_table(seg, case, enabled):
     assert np.array_equal(seg.tile_rows.cpu().numpy().reshape(-1, 64)[:nt], rows)
 
 
-def check(ml, case, enabled=None, reps=1):
+def check(ml, case, enabled=None, reps=1, expect_err=0):
     log(f"fused_decode {case.name} M={case.M} K={case.K} slices={case.slice_sizes} L={case.L} "
         f"mask={'none' if enabled is None else int(enabled.sum())}")
-    got, seg = run_decode(ml, case, enabled, reps)
+    got, seg = run_decode(ml, case, enabled, reps, expect_err=expect_err)
     check_table(seg, case, enabled)
     ref = O.lora_linear(case.x.values, case.ids, [a.values for a in case.A],
                         [b.values for b in case.B], case.ranks, case.slice_sizes,
@@ -118,8 +118,9 @@ def test_fused_decode_large_table(ml):
 
 
 def test_fused_decode_repeated_calls(ml):
-    """The exchange slots are emptied by their last reader, so repeated calls
-    on one workspace each add a fresh delta."""
+    """The exchange slots carry the launch's epoch, so repeated calls on one
+    workspace each add a fresh delta and never read an earlier call's
+    partial sums."""
     check(ml, W.decode_bf16(7, M=20, K=1536, N=512, L=6), reps=3)
 
 
@@ -133,7 +134,8 @@ def test_fused_decode_edge_cases(ml):
     case = W.random_linear(25, 20, 128, [64], [16, 16, 16, 16], W.F32)
     case.ids[:] = np.array([5, -1, 2, 9, -7, 2, 0, 4, 3, 3, 1, 100, -2, 0, 1, 2, 3, 4, 4, 0],
                            np.int32)
-    check(ml, case)
+    # ids outside [-1, L) are treated as "no adapter" and reported
+    check(ml, case, expect_err=ml.LORA_DEVERR_BAD_ID)
     # M = 0 writes the empty table and touches nothing else
     case0 = W.random_linear(19, 0, 128, [64], [16], W.BF16)
     got, seg = run_decode(ml, case0)
@@ -191,3 +193,46 @@ def test_build_segments_with_mask_bit_exact(ml, name, M, L, seed):
     nt = int(seg.num_tiles.cpu()[0])
     assert np.array_equal(seg.tile_info.cpu().numpy().reshape(-1, 4)[:nt], info)
     assert np.array_equal(seg.tile_rows.cpu().numpy().reshape(-1, 64)[:nt], rows)
+
+
+def test_error_word_only_for_ids_outside_the_table(ml):
+    """-1 is the ordinary "no adapter" id and reports nothing; one id past
+    the table (or below -1) sets LORA_DEVERR_BAD_ID, its row is left as it
+    was, and every other row still gets its delta."""
+    case = W.decode_bf16(9, M=24, K=1024, N=512, L=6)
+    case.ids[:] = np.where(case.ids >= 0, case.ids, -1)
+    check(ml, case, expect_err=0)
+    for bad in (6, 1000, -2):
+        c2 = W.decode_bf16(9, M=24, K=1024, N=512, L=6)
+        c2.ids[5] = bad
+        check(ml, c2, expect_err=ml.LORA_DEVERR_BAD_ID)
+
+
+def test_each_launch_tags_its_slots_afresh(ml):
+    """The exchange slots are never emptied: each launch tags the slots it
+    writes with a value of its own (from its dispatch), and consumers take
+    only slots with their launch's tag.  Consecutive launches on one
+    workspace leave different tags in the slot of sorted position 0,
+    S column 0 (workspace: 256-byte header, then 64-bit {value, tag} slots
+    [K chunk][position][column]); and a launch with new x after one with
+    other x on the same workspace still matches the oracle for the new x
+    (a stale partial sum would be taken before its producer rewrote it)."""
+    case = W.decode_bf16(8, M=16, K=1024, N=512, L=5)
+    case.ids[0] = 2                     # sorted position 0 has an adapter
+    other = W.decode_bf16(11, M=16, K=1024, N=512, L=5)
+    table = table_for(case)
+    ws = ml.Workspace.for_table(table, case.M)
+    slot0 = ws.buf[256:264].view(torch.int64)
+    ids = torch.from_numpy(case.ids).cuda()
+    tags = []
+    for c in (other, case, other, case):
+        x, y = to_dev(c.x), to_dev(case.y_base)
+        ml.lora_fused_decode(table, ids, x, y, ws)
+        torch.cuda.synchronize()
+        tags.append(int(slot0.cpu()[0]) >> 32 & 0xffffffff)
+    assert ml.lora_read_device_error(ws.buf) == 0
+    assert all(t != 0 for t in tags) and len(set(tags)) == len(tags), tags
+    ref = O.lora_linear(case.x.values, case.ids, [a.values for a in case.A],
+                        [b.values for b in case.B], case.ranks, case.slice_sizes,
+                        case.y_base.values)
+    assert_close(to_f64(y), ref, case.dtype, case.y_base.values, "after other x")

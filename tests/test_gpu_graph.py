@@ -1,8 +1,9 @@
 """HIP graph capture of the dense path (segment table + fused call, and the
 single-launch decode with an adapter enable mask).
 
-The kernels allocate nothing and clear their own exchange state (slots,
-counters), so a captured step replays correctly.  Each replay is preceded by
+The kernels allocate nothing and keep their exchange state ready on the
+device (slots tagged with an epoch that the last workgroup of each launch
+advances), so a captured step replays correctly.  Each replay is preceded by
 eager work on the captured buffers (new ids and x, y reset to its base) and
 followed by a synchronisation, and every replay must equal the eager result
 bit for bit (the kernels sum in a fixed order).

@@ -37,7 +37,7 @@ def setup(ml, case):
                       torch.from_numpy(case.adapter_enabled).cuda())
     cap = ml.lora_moe_align_capacity(case.M, case.topk, case.E, case.block_size_m)
     al = ml.MoeAlign(case.L, cap, case.block_size_m)
-    ml.lora_moe_align_run(torch.from_numpy(case.topk_ids).cuda(), torch.from_numpy(case.ids).cuda(),
+    ml.lora_moe_align(torch.from_numpy(case.topk_ids).cuda(), torch.from_numpy(case.ids).cuda(),
                           torch.from_numpy(case.adapter_enabled).cuda(), case.E, al)
     ws = ml.Workspace(ml.lora_moe_workspace_size(w, cap))
     return w, al, ws, cap
@@ -59,7 +59,7 @@ def test_align_bit_exact(ml, name, mk):
     log(f"align {name}")
     cap = ml.lora_moe_align_capacity(case.M, case.topk, case.E, case.block_size_m)
     al = ml.MoeAlign(case.L, cap, case.block_size_m)
-    ml.lora_moe_align_run(torch.from_numpy(case.topk_ids).cuda(), torch.from_numpy(case.ids).cuda(),
+    ml.lora_moe_align(torch.from_numpy(case.topk_ids).cuda(), torch.from_numpy(case.ids).cuda(),
                           torch.from_numpy(case.adapter_enabled).cuda(), case.E, al)
     torch.cuda.synchronize()
     s, e, n = O.moe_align(case.topk_ids, case.ids, case.adapter_enabled, case.L, case.E,
