@@ -23,7 +23,7 @@ __all__ = [
     "Segments", "Workspace",
     "MoeWeights", "MoeAlign",
     "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",
-    "lora_shrink_expand_add", "lora_fused_decode",
+    "lora_shrink_expand_add", "lora_fused_decode", "lora_fused_decode_noalloc",
     "lora_pack_embedding_adapter", "lora_embedding_shrink", "lora_embedding_decode",
     "lora_workspace_size", "lora_workspace_init", "lora_read_device_error",
     "lora_table_plan", "lora_pack_adapter",
@@ -387,6 +387,36 @@ def lora_fused_decode(table: LoraTable, ids: torch.Tensor, x: torch.Tensor, y: t
     check(lib.lora_fused_decode(table.ref, ids.data_ptr(), _mask_arg(adapter_enabled, table.L),
                                 x.data_ptr(), ldx, M, y.data_ptr(), ldy, *outs, cap, ws.ptr,
                                 ws.nbytes, stream_handle(stream)), "lora_fused_decode")
+
+
+def lora_fused_decode_noalloc(table: LoraTable, ids: torch.Tensor, x: torch.Tensor,
+                              y: torch.Tensor, seg: Optional[Segments] = None,
+                              adapter_enabled: Optional[torch.Tensor] = None,
+                              error_word: Optional[torch.Tensor] = None, stream=None) -> None:
+    """lora_fused_decode without a workspace, for callers that cannot
+    allocate: the library's fixed per-GPU array holds the exchange slots.
+    Allocates nothing here either; error bits are OR-ed into `error_word`
+    (a one-element int32 device tensor) when given."""
+    _check_io(table.dtype, x=x, y=y)
+    _cols(x, "x", table.K)
+    _cols(y, "y", table.N, exact=False)
+    M = _ids_arg(ids)
+    ldx, ldy = _rows(x, "x"), _rows(y, "y")
+    if x.shape[0] != M or y.shape[0] != M:
+        raise LoraError("ids, x and y must have the same number of rows")
+    if error_word is not None and (error_word.dtype != torch.int32 or not error_word.is_cuda
+                                   or error_word.numel() < 1):
+        raise LoraError("error_word must be an int32 device tensor")
+    if seg is not None:
+        if seg.L != table.L or M > seg.sorted_idx.shape[0]:
+            raise LoraError("segment buffers do not match the table or the batch")
+        outs, cap = seg.outs, seg.max_tiles
+    else:
+        outs, cap = _NO_OUTS, 0
+    check(lib.lora_fused_decode_noalloc(table.ref, ids.data_ptr(),
+                                        _mask_arg(adapter_enabled, table.L), x.data_ptr(), ldx,
+                                        M, y.data_ptr(), ldy, *outs, cap, _ptr(error_word),
+                                        stream_handle(stream)), "lora_fused_decode_noalloc")
 
 
 # ------------------------------------------------------------------------- MoE

@@ -17,6 +17,7 @@ LORA_RANK_ALIGN = 16
 LORA_MAX_RANK = 64
 LORA_MAX_ADAPTERS = 1024
 LORA_DECODE_MAX_M = 64
+LORA_NOALLOC_SCRATCH_BYTES = 1 << 20
 LORA_TILE_ROWS = 64
 MLORA_ABI_VERSION = 5
 
@@ -85,6 +86,8 @@ SIGNATURES = {
     "lora_linear_fused": (I32, [PW, P, I64, P, I64, I32, PS, P, I64, P, SZ, P]),
     "lora_fused_decode": (I32, [PW, P, P, P, I64, I32, P, I64, P, P, P, P, P, P, P, I32, P, SZ,
                                 P]),
+    "lora_fused_decode_noalloc": (I32, [PW, P, P, P, I64, I32, P, I64, P, P, P, P, P, P, P, I32,
+                                        P, P]),
     "lora_pack_embedding_adapter": (I32, [I32, I32, I64, I32, I32, P, P, P, P, P]),
     "lora_embedding_shrink": (I32, [PW, P, I32, PS, P, P]),
     "lora_embedding_decode": (I32, [PW, P, P, P, I32, P, I64, P, P, P, P, P, P, P, I32, P]),

@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "segments.hip", "pack.hip", "decode.hip", "linear.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["api.cpp", "segments.hip", "pack.hip", "decode.hip", "linear.hip", "gemm.hip", "moe.hip",
+           "noalloc.hip"]
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

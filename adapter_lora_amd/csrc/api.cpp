@@ -130,6 +130,51 @@ MoeWs moe_ws_layout(int L, int mtp, int r, int Kmax) {
     return ws;
 }
 
+// Host-side checks of the single-launch decode's arguments other than the
+// workspace (w already checked, 0 <= M <= LORA_DECODE_MAX_M).
+lora_status fused_decode_check(const lora_weights_t* w, const int32_t* ids, const void* x,
+                               int64_t ldx, int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                               int32_t* seg_indptr, int32_t* req_to_lora, int32_t* num_segments,
+                               int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
+                               int32_t max_tiles) {
+    lora_status st;
+    if (sorted_idx) {
+        if (!seg_indptr || !req_to_lora || !num_segments || !tile_info || !tile_rows || !num_tiles)
+            return LORA_INVALID_ARG;
+        if (max_tiles < lora_tile_capacity(M, w->L)) return LORA_INVALID_ARG;
+    }
+    if (M == 0) return LORA_OK;
+    if (!ids) return LORA_INVALID_ARG;
+    if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
+    return check_rows(y, ldy, n_total(w));
+}
+
+// Launch of the single-launch decode (arguments checked by
+// fused_decode_check), shared by lora_fused_decode and its allocation-free
+// form; `ws` is an exchange workspace already known to be large enough and
+// errors go to `err` (null: the workspace's own error word).
+lora_status fused_decode(const lora_weights_t* w, const int32_t* ids,
+                         const int32_t* adapter_enabled, const void* x, int64_t ldx, int32_t M,
+                         void* y, int64_t ldy, int32_t* sorted_idx, int32_t* seg_indptr,
+                         int32_t* req_to_lora, int32_t* num_segments, int32_t* tile_info,
+                         int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles, void* ws,
+                         int32_t* err, hipStream_t stream) {
+    const bool table = sorted_idx != nullptr;
+    if (M == 0) {
+        if (!table) return LORA_OK;
+        return from_hip(launch_build_segments(nullptr, nullptr, 0, w->L, sorted_idx, seg_indptr,
+                                              req_to_lora, num_segments, tile_info, tile_rows,
+                                              num_tiles, max_tiles, stream));
+    }
+    // segment-table fields of the args are unused in ids mode
+    lora_segments_t none{};
+    LinearArgs a = make_args(w, &none, M);
+    const SegOut out{sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
+                     num_tiles};
+    return from_hip(launch_decode_fused(a, ids, adapter_enabled, out, x, ldx, y, ldy, ws, err,
+                                        stream));
+}
+
 }  // namespace mlora
 
 extern "C" {
@@ -326,31 +371,40 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
     if (st != LORA_OK) return st;
     if (M < 0) return LORA_INVALID_ARG;
     if (M > LORA_DECODE_MAX_M) return LORA_UNSUPPORTED;
-    const bool table = sorted_idx != nullptr;
-    if (table) {
-        if (!seg_indptr || !req_to_lora || !num_segments || !tile_info || !tile_rows || !num_tiles)
-            return LORA_INVALID_ARG;
-        if (max_tiles < lora_tile_capacity(M, w->L)) return LORA_INVALID_ARG;
-    }
-    if (M == 0) {
-        if (!table) return LORA_OK;
-        return from_hip(launch_build_segments(nullptr, nullptr, 0, w->L, sorted_idx, seg_indptr,
-                                              req_to_lora, num_segments, tile_info, tile_rows,
-                                              num_tiles, max_tiles, stream));
-    }
-    if (!ids) return LORA_INVALID_ARG;
-    if ((st = check_rows(x, ldx, w->K)) != LORA_OK) return st;
-    if ((st = check_rows(y, ldy, n_total(w))) != LORA_OK) return st;
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
+    if ((st = fused_decode_check(w, ids, x, ldx, M, y, ldy, sorted_idx, seg_indptr, req_to_lora,
+                                 num_segments, tile_info, tile_rows, num_tiles, max_tiles)) !=
+        LORA_OK)
+        return st;
+    if (M > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) ||
+                  workspace_bytes < layout_for(w, M).total))
         return LORA_INVALID_ARG;
-    if (workspace_bytes < layout_for(w, M).total) return LORA_INVALID_ARG;
-    // segment-table fields of the args are unused in ids mode
-    lora_segments_t none{};
-    LinearArgs a = make_args(w, &none, M);
-    const SegOut out{sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
-                     num_tiles};
-    return from_hip(launch_decode_fused(a, ids, adapter_enabled, out, x, ldx, y, ldy, workspace,
-                                        nullptr, stream));
+    return fused_decode(w, ids, adapter_enabled, x, ldx, M, y, ldy, sorted_idx, seg_indptr,
+                        req_to_lora, num_segments, tile_info, tile_rows, num_tiles, max_tiles,
+                        workspace, nullptr, stream);
+}
+
+lora_status lora_fused_decode_noalloc(const lora_weights_t* w, const int32_t* ids,
+                                      const int32_t* adapter_enabled, const void* x, int64_t ldx,
+                                      int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                                      int32_t* seg_indptr, int32_t* req_to_lora,
+                                      int32_t* num_segments, int32_t* tile_info,
+                                      int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
+                                      int32_t* error_word, hipStream_t stream) {
+    lora_status st = check_weights(w);
+    if (st != LORA_OK) return st;
+    if (M < 0) return LORA_INVALID_ARG;
+    if (M > LORA_DECODE_MAX_M) return LORA_UNSUPPORTED;
+    // header and exchange slots (M plays no part) must fit the fixed array
+    if (layout_for(w, 0).total > (size_t)LORA_NOALLOC_SCRATCH_BYTES) return LORA_UNSUPPORTED;
+    if ((st = fused_decode_check(w, ids, x, ldx, M, y, ldy, sorted_idx, seg_indptr, req_to_lora,
+                                 num_segments, tile_info, tile_rows, num_tiles, max_tiles)) !=
+        LORA_OK)
+        return st;
+    void* scratch = nullptr;
+    if (M > 0 && noalloc_scratch(&scratch) != hipSuccess) return LORA_HIP_ERROR;
+    return fused_decode(w, ids, adapter_enabled, x, ldx, M, y, ldy, sorted_idx, seg_indptr,
+                        req_to_lora, num_segments, tile_info, tile_rows, num_tiles, max_tiles,
+                        scratch, error_word, stream);
 }
 
 lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t emb, int32_t rank,

@@ -107,6 +107,20 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
                                const SegOut& out, const void* x, int64_t ldx, void* y,
                                int64_t ldy, void* ws, int32_t* err, hipStream_t st);
 
+// Checks and launch of the single-launch decode on an exchange workspace
+// `ws` known to be large enough (api.cpp); errors go to `err` (null: the
+// workspace's own error word).
+lora_status fused_decode(const lora_weights_t* w, const int32_t* ids,
+                         const int32_t* adapter_enabled, const void* x, int64_t ldx, int32_t M,
+                         void* y, int64_t ldy, int32_t* sorted_idx, int32_t* seg_indptr,
+                         int32_t* req_to_lora, int32_t* num_segments, int32_t* tile_info,
+                         int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles, void* ws,
+                         int32_t* err, hipStream_t stream);
+
+// Device address of the current GPU's fixed decode scratch
+// (LORA_NOALLOC_SCRATCH_BYTES, noalloc.hip), looked up once per device.
+hipError_t noalloc_scratch(void** out);
+
 // Single-launch embedding decode (M <= LORA_DECODE_MAX_M): the fused decode
 // kernel's consumers only, with S rows looked up from the transposed A table
 // by token id; segments grouped from `ids` on chip (table written to `out`

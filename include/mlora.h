@@ -312,6 +312,34 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
                               int32_t max_tiles, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/*
+ * lora_fused_decode_noalloc: lora_fused_decode for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and table outputs as lora_fused_decode, without `workspace`: the
+ * exchange slots live in a fixed array of LORA_NOALLOC_SCRATCH_BYTES per GPU
+ * inside the library, held until the process ends and found on the first
+ * call made on each device.  The call allocates and frees nothing.
+ *   error_word  device int32, or NULL: error bits (LORA_DEVERR_*) are OR-ed
+ *               into it (sticky; the caller clears it); NULL drops them.
+ * The array's share of a table is 256 + 8 * 64 * ceil(K / 1024) * n_slices
+ * * r_max bytes (M plays no part); a table that needs more than
+ * LORA_NOALLOC_SCRATCH_BYTES returns LORA_UNSUPPORTED before any launch.
+ * Nothing in the array needs clearing between calls (each launch tags what
+ * it writes), but every call on one GPU uses the same array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must
+ * not be issued.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+lora_status lora_fused_decode_noalloc(const lora_weights_t* w, const int32_t* ids,
+                                      const int32_t* adapter_enabled, const void* x, int64_t ldx,
+                                      int32_t M, void* y, int64_t ldy, int32_t* sorted_idx,
+                                      int32_t* seg_indptr, int32_t* req_to_lora,
+                                      int32_t* num_segments, int32_t* tile_info,
+                                      int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
+                                      int32_t* error_word, hipStream_t stream);
+
 /* ---------------------------------------------------------------- embedding LoRA */
 
 /*

@@ -98,6 +98,22 @@ def test_argument_checks_fail_before_any_launch():
                                  null, null, null, null, null, null, 8, null, 0, null) == INV
     assert lib.lora_fused_decode(ctypes.byref(w2), null, null, null, 128, 8, null, 128, *args, 0,
                                  null, 0, null) == INV                            # ids null
+    # allocation-free form: a table whose exchange slots exceed the fixed
+    # array (256 + 8 * 64 * ceil(K / 1024) * n_slices * r_max bytes) is
+    # refused before anything touches a device; one that fits gets as far as
+    # the argument checks (ids null)
+    w3 = _abi.lora_weights_t()
+    w3.dtype, w3.K, w3.n_slices, w3.L, w3.r_max = 1, 16384, 4, 4, 64
+    for s_ in range(5):
+        w3.slice_offsets[s_] = 128 * s_
+    w3.A, w3.B, w3.a_off, w3.b_off, w3.rank = w2.A, w2.B, w2.a_off, w2.b_off, w2.rank
+    assert 256 + 8 * 64 * 16 * 4 * 64 > _abi.LORA_NOALLOC_SCRATCH_BYTES
+    assert lib.lora_fused_decode_noalloc(ctypes.byref(w3), some, null, some, 16384, 8, some, 512,
+                                         *args, 0, null, null) == _abi.LORA_UNSUPPORTED
+    assert lib.lora_fused_decode_noalloc(ctypes.byref(w2), null, null, null, 128, 65, null, 128,
+                                         *args, 0, null, null) == _abi.LORA_UNSUPPORTED
+    assert lib.lora_fused_decode_noalloc(ctypes.byref(w2), null, null, some, 128, 8, some, 128,
+                                         *args, 0, null, null) == INV               # ids null
     # fused base GEMM: fp32 tables are not on this path; a null base weight
     # or a short workspace is rejected before any launch
     w2.dtype = 0
