@@ -155,6 +155,40 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Integer forms with the DPP controls as template arguments: lanes a control
+// leaves out (row / bank masks) or whose source lies outside the row read 0.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ int dpp_int(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// OR over the whole wavefront (wave-uniform): within rows of 16 lanes by
+// DPP swaps and mirrors, then the four row results by readlane.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+    int x = (int)v;
+    x |= dpp_int<0xB1>(x);     // quad_perm [1,0,3,2]
+    x |= dpp_int<0x4E>(x);     // quad_perm [2,3,0,1]
+    x |= dpp_int<0x141>(x);    // row_half_mirror
+    x |= dpp_int<0x140>(x);    // row_mirror
+    return (uint32_t)(__builtin_amdgcn_readlane(x, 15) | __builtin_amdgcn_readlane(x, 31) |
+                      __builtin_amdgcn_readlane(x, 47) | __builtin_amdgcn_readlane(x, 63));
+}
+
+// Inclusive prefix sum over the wavefront's lanes (lane i: v_0 + ... + v_i),
+// the DPP sequence for GFX9: shifts of 1..3 inside each row, then of 4 and 8
+// into the upper banks, then the last lane of a row broadcast into the rows
+// above it (rows 1 and 3, then rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    int x = v + dpp_int<0x111>(v);                 // row_shr:1
+    x += dpp_int<0x112>(v);                        // row_shr:2
+    x += dpp_int<0x113>(v);                        // row_shr:3
+    x += dpp_int<0x114, 0xF, 0xE>(x);              // row_shr:4, banks 1-3
+    x += dpp_int<0x118, 0xF, 0xC>(x);              // row_shr:8, banks 2-3
+    x += dpp_int<0x142, 0xA>(x);                   // row_bcast:15, rows 1 and 3
+    x += dpp_int<0x143, 0xC>(x);                   // row_bcast:31, rows 2 and 3
+    return x;
+}
+
 // Sum over the whole wavefront, returned as a wave-uniform value.
 __device__ __forceinline__ float wave_total(float v) {
     v = row16_sum(v);

@@ -53,7 +53,7 @@ struct DecodeParams {
     const int32_t* enabled;  // adapter mask for that grouping (may be null)
     SegOut out;              // segment table written by the last workgroup (ids mode)
     int writer;              // 1 when the last workgroup writes `out`
-    int by_slot;             // ids mode with L <= M: unit s is adapter slot s (see slot_head)
+    int by_slot;             // ids mode with L <= M: producers numbered over the used slots
     const int32_t* tokens;   // non-null: embedding lookup, S rows read from the
                              // transposed A table by token id (a.K = vocab); no producers
 };
@@ -166,23 +166,66 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
     return v;
 }
 
-// Slot mode (ids mode with L <= M, so that there is a unit for every slot):
-// unit s serves adapter slot s rather than the s-th segment.  Its rank and
-// weight offset are then two scalar loads issued together with the ids, and
-// once both are in, one ballot over the token buckets tells whether any
-// token uses the slot; the weight loads are issued before the slot's token
+// Slot mode (ids mode with L <= M <= 64, so that the launch has units for
+// every slot): units are numbered compactly over the slots the batch uses.
+// Every workgroup loads the ids and, one slot per lane, every slot's rank and
+// weight offset in one batch of loads; from the token buckets it knows which
+// slots have tokens, and a prefix sum over the slots gives each working unit
+// its slot.  Producer unit u is the u-th of the (16-row A block, K chunk)
+// pairs of the used slots in slot order, so the working producers take the
+// lowest workgroup ids, one per compute unit while there are at most 256 of
+// them: a second producer on a compute unit queues its weight loads behind
+// the first one's (measured: the producers of the last used slots, which had
+// landed on compute units already holding working producers, finished about
+// 1 us after the rest).  Units past the work exit at once.  Consumer units
+// stay numbered slot-major (consumer unit u serves slot u / n_groups): a
+// consumer needs only its own slot's rank and offset, two scalar loads, and
+// the compact numbering's extra reductions delayed the B loads of the
+// wide-output consumers.  The weight loads are issued before the slot's token
 // list (slot_tokens) is formed.
-__device__ __forceinline__ SegView slot_head(const ViewArgs& va, int s) {
-    SegView v{};
-    v.id = s;
-    v.rp = va.rank[s];
-    v.off = va.offs[s];
-    return v;
+struct SlotTable {
+    int rk;             // lane s < L: rank of slot s
+    int64_t off;        // lane s < L: weight offset of slot s
+    uint64_t used;      // bit s: slot s has a token and a non-zero rank
+};
+
+__device__ __forceinline__ SlotTable slot_table_load(const ViewArgs& va) {
+    const int j = min(lane_id(), va.L - 1);
+    return SlotTable{va.rank[j], va.offs[j], 0ull};
 }
 
-// Whether any of the batch's tokens (bucket b of lane m < M) uses slot s.
-__device__ __forceinline__ bool slot_used(int b, int M, int s) {
-    return __ballot(lane_id() < M && b == s) != 0ull;
+// b: this lane's token bucket (L for none).  Slots are at most 64 here.
+__device__ __forceinline__ void slot_table_used(SlotTable& t, int b, int M, int L) {
+    const int lane = lane_id();
+    const bool in = lane < M && b < L;
+    const uint32_t lo = wave_or(in && b < 32 ? 1u << (b & 31) : 0u);
+    const uint32_t hi = wave_or(in && b >= 32 ? 1u << (b & 31) : 0u);
+    const uint64_t has = ((uint64_t)hi << 32) | lo;
+    t.used = __ballot(lane < L && ((has >> lane) & 1ull) && t.rk > 0);
+}
+
+__device__ __forceinline__ void slot_pick(const SlotTable& t, int s, SegView& v) {
+    v.id = s;
+    v.rp = __builtin_amdgcn_readlane(t.rk, s);
+    v.off = readlane64(t.off, s);
+}
+
+// Producer unit u: slot, 16-row block jb and K chunk c; false past the work.
+__device__ __forceinline__ bool slot_producer(const SlotTable& t, int u, int per_block, SegView& v,
+                                              int* jb, int* c, int C) {
+    const int lane = lane_id();
+    const int units = ((t.used >> lane) & 1ull) ? (t.rk / 16) * per_block : 0;
+    const int incl = wave_incl_scan(units);
+    const unsigned long long past = __ballot(incl > u);
+    if (past == 0ull) return false;
+    const int s = __ffsll((long long)past) - 1;
+    const int n = __builtin_amdgcn_readlane(units, s);
+    const int local = u - (__builtin_amdgcn_readlane(incl, s) - n);
+    if (local < 0 || local >= n) return false;    // never taken when the scan is right
+    slot_pick(t, s, v);
+    *jb = local / C;
+    *c = local % C;
+    return true;
 }
 
 // The token list of slot s (b: this lane's token bucket) without grouping
@@ -275,16 +318,18 @@ __device__ __forceinline__ void dec_produce(const DecodeParams& p, const ViewArg
     constexpr int ST = dec_steps<T>();
     const LinearArgs& a = p.a;
     const int per_s = p.jb_max * p.C;
-    const int s = unit / per_s;
-    const int jb = (unit % per_s) / p.C;
-    const int c = unit % p.C;
+    int s = unit / per_s;
+    int jb = (unit % per_s) / p.C;
+    int c = unit % p.C;
     SegView v;
     int b = 0;
     if (p.by_slot) {
         const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
-        v = slot_head(va, s);
+        SlotTable st = slot_table_load(va);
         b = token_bucket(tl, p.enabled, va.L);
-        if (!slot_used(b, va.M, s)) return;
+        slot_table_used(st, b, va.M, va.L);
+        if (!slot_producer(st, unit, a.n_sl * p.C, v, &jb, &c, p.C)) return;
+        s = v.id;
     } else {
         v = seg_view(p, va, s);
         if (s >= v.nseg || v.id < 0) return;
@@ -357,16 +402,18 @@ __device__ __forceinline__ void dec_produce_mfma(const DecodeParams& p, const Vi
                                                  float* red, uint32_t tag) {
     const LinearArgs& a = p.a;
     const int per_s = p.jb_max * p.C;
-    const int s = unit / per_s;
-    const int jb = (unit % per_s) / p.C;
-    const int c = unit % p.C;
+    int s = unit / per_s;
+    int jb = (unit % per_s) / p.C;
+    int c = unit % p.C;
     SegView v;
     int b = 0;
     if (p.by_slot) {
         const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
-        v = slot_head(va, s);
+        SlotTable st = slot_table_load(va);
         b = token_bucket(tl, p.enabled, va.L);
-        if (!slot_used(b, va.M, s)) return;
+        slot_table_used(st, b, va.M, va.L);
+        if (!slot_producer(st, unit, a.n_sl * p.C, v, &jb, &c, p.C)) return;
+        s = v.id;
     } else {
         v = seg_view(p, va, s);
         if (s >= v.nseg || v.id < 0) return;
@@ -693,10 +740,15 @@ __device__ __forceinline__ void dec_consumer(const DecodeParams& p, const ViewAr
     SegView v;
     int b = 0;
     if (p.by_slot) {
+        // consumer units keep the slot-major numbering: slot s's rank and
+        // offset are two scalar loads issued with the ids, and one ballot
+        // tells whether any token uses it
         const TokenLoad tl = load_token(va.ids, p.enabled, va.M, va.L);
-        v = slot_head(va, s);
+        v.id = s;
+        v.rp = va.rank[s];
+        v.off = va.offs[s];
         b = token_bucket(tl, p.enabled, va.L);
-        if (v.rp == 0 || !slot_used(b, va.M, s)) return;
+        if (v.rp == 0 || __ballot(lane_id() < va.M && b == s) == 0ull) return;
     } else {
         v = seg_view(p, va, s);
         if (s >= v.nseg || v.id < 0 || v.rp == 0) return;
@@ -728,7 +780,7 @@ __device__ __forceinline__ void dec_consumer(const DecodeParams& p, const ViewAr
 }
 
 template <typename T>
-__global__ __launch_bounds__(kDecThreads) void k_decode_fused(const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_decode_fused(const int32_t* __restrict__ ids,
                                                              const int32_t* __restrict__ rank,
                                                              const int64_t* __restrict__ a_off,
                                                              const int64_t* __restrict__ b_off,
