@@ -56,21 +56,37 @@ __global__ __launch_bounds__(kTileThreads) void k_shrink_dense(LinearArgs a, con
     }
 }
 
-// S[p][:] = sum_c P[c][p][:] for every sorted position with an adapter
+// S[p][:] = sum_c P[c][p][:] for every sorted position with an adapter, the
+// chunks added in order c = 0, 1, ...  A thread issues the loads of up to
+// kReduceBatch chunks before it adds any of them (a loop that adds as it
+// loads waits out one memory round trip per chunk).  The rows are bounded by
+// M, so no load waits for the number of rows with an adapter; that count
+// only gates the stores.
+constexpr int kReduceBatch = 8;
+
 __global__ void k_reduce_partials(const float* __restrict__ P, int C, int64_t cstride,
-                                  float* __restrict__ S, int cols,
+                                  float* __restrict__ S, int cols, int M,
                                   const int32_t* __restrict__ seg_indptr,
                                   const int32_t* __restrict__ num_segments) {
-    const int m_valid = seg_indptr[num_segments[0]];
-    const int64_t total4 = (int64_t)m_valid * cols / 4;   // cols is a multiple of 16
+    const int64_t total4 = (int64_t)M * cols / 4;          // cols is a multiple of 16
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float4* P4 = reinterpret_cast<const float4*>(P);
+    const int64_t c4 = cstride / 4;
+    const int m_valid = seg_indptr[num_segments[0]];
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += stride) {
-        float4 acc = reinterpret_cast<const float4*>(P)[i];
-        for (int c = 1; c < C; ++c) {
-            const float4 v = reinterpret_cast<const float4*>(P + c * cstride)[i];
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        float4 acc = P4[i];
+        for (int c0 = 1; c0 < C; c0 += kReduceBatch) {
+            float4 v[kReduceBatch];
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q) v[q] = P4[min(c0 + q, C - 1) * c4 + i];
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q) {
+                if (c0 + q < C) {
+                    acc.x += v[q].x; acc.y += v[q].y; acc.z += v[q].z; acc.w += v[q].w;
+                }
+            }
         }
-        reinterpret_cast<float4*>(S)[i] = acc;
+        if (i * 4 / cols < m_valid) reinterpret_cast<float4*>(S)[i] = acc;
     }
 }
 
@@ -189,7 +205,7 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
     if (blocks > 2048) blocks = 2048;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(k_reduce_partials, dim3((unsigned)blocks), dim3(256), 0, st, P, C,
-                       (int64_t)a.M * a.cols, S, a.cols, a.seg_indptr, a.num_segments);
+                       (int64_t)a.M * a.cols, S, a.cols, a.M, a.seg_indptr, a.num_segments);
     return hipGetLastError();
 }
 
