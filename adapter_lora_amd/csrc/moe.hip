@@ -136,6 +136,10 @@ __device__ __forceinline__ int64_t moe_slot(const MoeArgs& a, bool outer, int l,
     return (outer && a.shared_outer) ? (int64_t)l : (int64_t)l * a.E + e;
 }
 
+// Units are numbered block-major (block b of every adapter, then block b + 1):
+// an adapter's used blocks are a prefix of its list, so the units with work
+// take the lowest workgroup ids and the idle ones (blocks past an adapter's
+// padded length) come last instead of holding dispatch slots among them.
 struct MoeUnit {
     bool ok;
     int e;
@@ -186,12 +190,11 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
                                                               int64_t ld_in, float* __restrict__ P,
                                                               int C, int K, int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
-    const int nblk = a.max_tokens_padded / a.block_size_m;
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / C;
     const int c = unit % C;
-    const int l = blk / nblk, b = blk % nblk;
+    const int l = blk % a.L, b = blk / a.L;
     __shared__ int s_wlast[kTileWaves];
     const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
@@ -232,13 +235,12 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, i
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     __shared__ int s_wlast[kTileWaves];
     __shared__ float red[kTileWaves * 16 * 16];
-    const int nblk = a.max_tokens_padded / a.block_size_m;
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / (C * G);
     const int c = (unit / G) % C;
     const int cb = unit % G;
-    const int l = blk / nblk, b = blk % nblk;
+    const int l = blk % a.L, b = blk / a.L;
     const MoeUnit mu = moe_unit(a, which, true, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
     const int lane = lane_id();
@@ -279,22 +281,38 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, i
     }
 }
 
-// S rows of the aligned positions that exist (pos < ntpp[l]).
+// S rows of the aligned positions that exist (pos < ntpp[l]), the K chunks
+// added in order; all of a batch's chunk loads are issued before any is added
+// (one memory round trip per batch, not per chunk).  Padding positions
+// (sentinel pairs) are read along but not stored: their S rows are never used.
+constexpr int kMoeReduceBatch = 8;
+
 __global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride,
                              float* __restrict__ S, int r, int mtp,
-                             const int32_t* __restrict__ ntpp, int L) {
+                             const int32_t* __restrict__ ntpp,
+                             const int32_t* __restrict__ sorted_ids, int npairs) {
     const int l = blockIdx.y;
     const int n = ntpp[l];
     const int64_t row0 = (int64_t)l * mtp;
     const int total4 = n * r / 4;
+    const float4* P4 = reinterpret_cast<const float4*>(P);
+    const int64_t c4 = cstride / 4;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += gridDim.x * blockDim.x) {
         const int64_t idx = row0 * r / 4 + i;
-        float4 acc = reinterpret_cast<const float4*>(P)[idx];
-        for (int c = 1; c < C; ++c) {
-            const float4 v = reinterpret_cast<const float4*>(P + c * cstride)[idx];
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        const int f = sorted_ids[row0 + i * 4 / r];
+        float4 acc = P4[idx];
+        for (int c0 = 1; c0 < C; c0 += kMoeReduceBatch) {
+            float4 v[kMoeReduceBatch];
+#pragma unroll
+            for (int q = 0; q < kMoeReduceBatch; ++q) v[q] = P4[min(c0 + q, C - 1) * c4 + idx];
+#pragma unroll
+            for (int q = 0; q < kMoeReduceBatch; ++q) {
+                if (c0 + q < C) {
+                    acc.x += v[q].x; acc.y += v[q].y; acc.z += v[q].z; acc.w += v[q].w;
+                }
+            }
         }
-        reinterpret_cast<float4*>(S)[idx] = acc;
+        if (f >= 0 && f < npairs) reinterpret_cast<float4*>(S)[idx] = acc;
     }
 }
 
@@ -305,12 +323,11 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
                                                               int N, int n_groups, int tpw,
                                                               int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
-    const int nblk = a.max_tokens_padded / a.block_size_m;
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / n_groups;
     const int g = unit % n_groups;
-    const int l = blk / nblk, b = blk % nblk;
+    const int l = blk % a.L, b = blk / a.L;
     __shared__ int s_wlast[kTileWaves];
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
@@ -338,12 +355,11 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4)
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     __shared__ int s_wlast[kWideThreads / kWave];
     __shared__ uint4 lds[kWideLds / 16];
-    const int nblk = a.max_tokens_padded / a.block_size_m;
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / n_groups;
     const int g = unit % n_groups;
-    const int l = blk / nblk, b = blk % nblk;
+    const int l = blk % a.L, b = blk / a.L;
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
     const int64_t ew = moe_slot(a, which == 1, l, mu.e);
@@ -382,7 +398,8 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     int rb = (a.max_tokens_padded * a.r / 4 + 255) / 256;
     if (rb < 1) rb = 1;
     hipLaunchKernelGGL(k_moe_reduce, dim3((unsigned)rb, (unsigned)a.L), dim3(256), 0, st, P, C,
-                       cstride, S, a.r, a.max_tokens_padded, a.ntpp, a.L);
+                       cstride, S, a.r, a.max_tokens_padded, a.ntpp, a.sorted_token_ids,
+                       a.M * a.topk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_tiles = (N + kNTile - 1) / kNTile;
