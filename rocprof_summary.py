@@ -5,6 +5,14 @@
   python rocprof_summary.py mfma DIR "COMMAND" > profiles/<workload>_mfma.md
       per-kernel MFMA work and utilisation from one counter run of
       SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+  python rocprof_summary.py durations "COMMAND_TEMPLATE" NAME=DIR ... > profiles/<file>.md
+      per workload (one rocprofv3 --kernel-trace run each, COMMAND_TEMPLATE with
+      {name} standing for NAME): launches, median, p10 and p90 of every
+      library kernel's duration, grouped by kernel and grid size
+  python rocprof_summary.py traffic_all "FETCH_TEMPLATE" "WRITE_TEMPLATE" NAME=FDIR,WDIR,BENCHJSON ...
+      per workload: FETCH_SIZE and WRITE_SIZE bytes per step of the library's
+      kernels (calibrated as below) against the workload's algorithmic bytes
+      (alg_bytes of the bench line saved as BENCHJSON)
   python rocprof_summary.py traffic FETCH_DIR WRITE_DIR "FETCH_CMD" "WRITE_CMD" [WORKGROUPS] \\
       > profiles/decode_fused_traffic.md
       HBM bytes per launch of the fused decode kernel (only the dispatches with
@@ -41,7 +49,7 @@ def _rows(directory, suffix):
 
 
 def short(name):
-    name = name.replace("void ", "")
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
     if "(" in name:
         name = name[:name.index("(")]
     return name[:70]
@@ -57,6 +65,122 @@ def stats(directory, command):
         print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
               f"{float(r['Percentage']):.1f} |")
+
+
+def _dur_us(r):
+    return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+
+
+def _pct(v, q):
+    v = sorted(v)
+    if not v:
+        return float("nan")
+    i = q / 100 * (len(v) - 1)
+    lo, hi = int(i), min(int(i) + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def durations(template, pairs):
+    print("# Kernel durations per workload (rocprofv3 kernel trace)\n")
+    print("One `rocprofv3 --kernel-trace` run of the benchmark per workload "
+          "(from /tmp, `TMPDIR=/tmp`); the command, with `{name}` the workload:\n")
+    print(f"```\n{template}\n```\n")
+    print("Durations are the trace's start-to-end times of each dispatch, in µs, "
+          "for the library's kernels and the streaming reference kernel; kernels are "
+          "told apart by grid size (threads).  p10 / p90 are the 10th / 90th "
+          "percentiles over all launches of the run (warm-up and timed steps, "
+          "cold-MALL rotation).\n")
+    print("| workload | kernel | grid | launches | median | p10 | p90 | mean |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|")
+    for pair in pairs:
+        name, d = pair.split("=", 1)
+        rows = _rows(d, "kernel_trace.csv")
+        groups = {}
+        for r in rows:
+            n = r["Kernel_Name"]
+            if ("mlora" not in n and "k_stream" not in n) or "k_pack" in n or "k_fill" in n:
+                continue
+            key = (short(n), int(r.get("Grid_Size_X", r.get("Grid_Size", 0))))
+            groups.setdefault(key, []).append(_dur_us(r))
+        for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if len(v) < 20:
+                continue
+            print(f"| {name} | `{k}` | {g} | {len(v)} | {_pct(v, 50):.2f} | {_pct(v, 10):.2f} | "
+                  f"{_pct(v, 90):.2f} | {sum(v) / len(v):.2f} |")
+
+
+def _per_kernel_kib(rows, counter, keep):
+    """Per (kernel, grid): list of the counter's value per dispatch, KiB."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or not keep(r["Kernel_Name"]):
+            continue
+        key = (short(r["Kernel_Name"]), int(r.get("Grid_Size", r.get("Grid_Size_X", 0))),
+               r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, g, _), v in per.items():
+        out.setdefault((k, g), []).append(v)
+    return out
+
+
+def _calibration(rows, counter):
+    """Bytes the counter reads per byte moved, from the 128 MB streaming copy."""
+    half = CALIB_BYTES / 2
+    cal = [v for v in _all(rows, counter, CALIB_KERNEL) if v * 1024 > 0.25 * half]
+    if not cal:
+        raise SystemExit(f"no calibration copy in the {counter} run")
+    return (sum(cal) / len(cal)) * 1024 / half
+
+
+def traffic_all(fetch_template, write_template, triples):
+    import json
+    print("# HBM traffic per workload (FETCH_SIZE, WRITE_SIZE)\n")
+    print("Two counter runs of the benchmark per workload (from /tmp, `TMPDIR=/tmp`), "
+          "with `{name}` the workload:\n")
+    print(f"```\n{fetch_template}\n{write_template}\n```\n")
+    print("Each counter (KiB per dispatch) is scaled by what it reads for the 128 MB "
+          "streaming copy of the same run (`k_stream`, 128 MB read and 128 MB written).  "
+          "Per kernel: bytes per dispatch, median over the run's dispatches.  Per "
+          "workload: the step's kernels summed against the step's algorithmic bytes "
+          "(the bench line's `alg_bytes`: every touched weight, x row and y row "
+          "once).\n")
+    print("| workload | kernel | grid | dispatches | fetch MB | write MB |")
+    print("|---|---|---:|---:|---:|---:|")
+    summary = []
+    for t in triples:
+        name, rest = t.split("=", 1)
+        fdir, wdir, bj = rest.split(",")
+        fr = _rows(fdir, "counter_collection.csv")
+        wr = _rows(wdir, "counter_collection.csv")
+        ff, wf = _calibration(fr, "FETCH_SIZE"), _calibration(wr, "WRITE_SIZE")
+        keep = lambda n: "mlora::" in n and "k_pack" not in n and "k_fill" not in n
+        fk = _per_kernel_kib(fr, "FETCH_SIZE", keep)
+        wk = _per_kernel_kib(wr, "WRITE_SIZE", keep)
+        step_f = step_w = 0.0
+        for key in sorted(set(fk) | set(wk), key=lambda kk: kk[0]):
+            fv = sorted(fk.get(key, [0.0]))
+            wv = sorted(wk.get(key, [0.0]))
+            fb = fv[len(fv) // 2] * 1024 / ff
+            wb = wv[len(wv) // 2] * 1024 / wf
+            if len(fv) < 10:
+                continue
+            step_f += fb
+            step_w += wb
+            print(f"| {name} | `{key[0]}` | {key[1]} | {len(fv)} | {fb / 1e6:.2f} | "
+                  f"{wb / 1e6:.2f} |")
+        line = json.loads(open(bj).read().strip().splitlines()[-1])
+        res = line.get("extra", {}).get(name) or {}
+        alg = res.get("alg_bytes") or res.get("alg_bytes_deltas")
+        if name == "decode_bf16":
+            alg = line["roofline"]["alg_bytes_per_launch"]
+        summary.append((name, step_f, step_w, alg))
+    print("\n| workload | measured MB per step | algorithmic MB | measured / algorithmic |")
+    print("|---|---:|---:|---:|")
+    for name, f, w, alg in summary:
+        ratio = "—" if not alg else f"{(f + w) / alg:.2f}"
+        print(f"| {name} | {(f + w) / 1e6:.2f} | {'—' if not alg else f'{alg / 1e6:.2f}'} | "
+              f"{ratio} |")
 
 
 def _per_dispatch_kib(rows, counter, match, workgroups=None):
@@ -156,5 +280,9 @@ if __name__ == "__main__":
         mfma(sys.argv[2], sys.argv[3])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:7])
+    elif sys.argv[1] == "durations":
+        durations(sys.argv[2], sys.argv[3:])
+    elif sys.argv[1] == "traffic_all":
+        traffic_all(sys.argv[2], sys.argv[3], sys.argv[4:])
     else:
         raise SystemExit(__doc__)
