@@ -145,12 +145,19 @@ def traffic_all(fetch_template, write_template, triples):
           "workload: the step's kernels summed against the step's algorithmic bytes "
           "(the bench line's `alg_bytes`: every touched weight, x row and y row "
           "once).\n")
-    print("| workload | kernel | grid | dispatches | fetch MB | write MB |")
-    print("|---|---|---:|---:|---:|---:|")
+    print("| workload | kernel | grid | dispatches | fetch MB | write MB | in step |")
+    print("|---|---|---:|---:|---:|---:|---|")
     summary = []
     for t in triples:
         name, rest = t.split("=", 1)
-        fdir, wdir, bj = rest.split(",")
+        fdir, wdir, bj, *sel = rest.split(",")
+        # the step's kernels: "+"-separated name fragments, each optionally
+        # "@grid" (threads); default every library kernel of the run
+        picks = [q.split("@") for q in sel[0].split("+")] if sel else []
+
+        def in_step(key):
+            return not picks or any(q[0] in key[0] and (len(q) == 1 or int(q[1]) == key[1])
+                                    for q in picks)
         fr = _rows(fdir, "counter_collection.csv")
         wr = _rows(wdir, "counter_collection.csv")
         ff, wf = _calibration(fr, "FETCH_SIZE"), _calibration(wr, "WRITE_SIZE")
@@ -165,13 +172,15 @@ def traffic_all(fetch_template, write_template, triples):
             wb = wv[len(wv) // 2] * 1024 / wf
             if len(fv) < 10:
                 continue
-            step_f += fb
-            step_w += wb
+            step = in_step(key)
+            if step:
+                step_f += fb
+                step_w += wb
             print(f"| {name} | `{key[0]}` | {key[1]} | {len(fv)} | {fb / 1e6:.2f} | "
-                  f"{wb / 1e6:.2f} |")
+                  f"{wb / 1e6:.2f} |{' step' if step and picks else ''}")
         line = json.loads(open(bj).read().strip().splitlines()[-1])
         res = line.get("extra", {}).get(name) or {}
-        alg = res.get("alg_bytes") or res.get("alg_bytes_deltas")
+        alg = res.get("alg_bytes") or (res.get("alg_bytes_deltas", 0) + res.get("alg_bytes_silu", 0))
         if name == "decode_bf16":
             alg = line["roofline"]["alg_bytes_per_launch"]
         summary.append((name, step_f, step_w, alg))
