@@ -2,14 +2,23 @@
 // ("vLLM-Ascend dynamic LoRA operator" walkthrough, section 2.3: equal ids
 // made contiguous; a segment is an id plus a contiguous range of tokens).
 //
-// One workgroup runs a stable counting sort:
-//   1. histogram of bucket ids in LDS (bucket L = no adapter);
-//   2. one wavefront scans the histogram into bucket bases and compacts the
-//      non-empty adapter buckets into (req_to_lora, seg_indptr);
-//   3. tokens are scattered tile by tile in token order: inside a wavefront
-//      equal buckets are found with one ballot per id bit, so a token's rank
-//      among its equals is a popcount; earlier wavefronts' counts per bucket
-//      come from a small LDS table.  Order inside a bucket is token order.
+// One workgroup of 16 wavefronts runs a stable counting sort.  Wavefront w
+// owns a contiguous chunk of the tokens (a multiple of 64, in passes of 64):
+//   1. every id load is issued at once (the first kCachedPasses passes stay in
+//      registers), together with the adapter mask, which goes to LDS, so a
+//      token's bucket (its id, or L for none or a disabled adapter) costs no
+//      dependent global load;
+//   2. each wavefront counts its chunk per bucket into its own LDS row: inside
+//      a pass equal buckets are found with one ballot per id bit, and the
+//      first lane of each group adds the group's size;
+//   3. per bucket, the rows are turned into exclusive offsets across the
+//      wavefronts; one wavefront scans the bucket totals into bucket bases and
+//      compacts the non-empty adapter buckets into (req_to_lora, seg_indptr);
+//   4. each wavefront scatters its chunk with no further barrier: a token's
+//      position is its bucket's base, plus its wavefront's offset, plus the
+//      equal tokens of its earlier passes (kept in the same row), plus its
+//      rank inside its pass (a popcount).  Order inside a bucket is token
+//      order.
 // It also writes the tile schedule the shrink / expand kernels run on (the
 // walkthrough's section 2.4: which block, which segment, which rank is worked
 // out before the product kernels start): every segment is cut into tiles of
@@ -24,7 +33,12 @@ namespace mlora {
 
 constexpr int kSegThreads = 1024;
 constexpr int kSegWaves = kSegThreads / kWave;
-constexpr int kCachedTiles = 8;
+constexpr int kCachedPasses = 8;   // tokens per wavefront kept in registers: 8 x 64
+
+// LDS words of the block builder for L adapter slots
+inline size_t build_segments_lds(int L) {
+    return ((size_t)(L + 1) * (kSegWaves + 5) + (size_t)L) * sizeof(int);
+}
 
 __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ enabled, int M, int L,
@@ -34,36 +48,40 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     int32_t* __restrict__ num_tiles, int max_tiles) {
     extern __shared__ int lds[];
     const int NB = L + 1;
-    int* count = lds;                    // [NB]
-    int* base = count + NB;              // [NB]  running output position per bucket
-    int* bstart = base + NB;             // [NB]  first sorted position of bucket b
+    int* row = lds;                      // [kSegWaves][NB] per-wavefront bucket counts, then offsets
+    int* total = row + kSegWaves * NB;   // [NB]  tokens per bucket
+    int* bstart = total + NB;            // [NB]  first sorted position of bucket b
     int* btile = bstart + NB;            // [NB]  first tile of bucket b's segment
     int* stile = btile + NB;             // [NB]  first tile of segment s (stile[nseg] = total)
     int* sbucket = stile + NB;           // [NB]  adapter id of segment s
-    int* wcnt = sbucket + NB;            // [kSegWaves][NB] per-tile, per-wave bucket counts
+    int* en = sbucket + NB;              // [L]   adapter mask
     __shared__ int s_segs, s_tiles;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
 
-    for (int i = tid; i < NB * (6 + kSegWaves); i += kSegThreads) lds[i] = 0;
+    // chunk of this wavefront: [c0, c1), passes of 64 tokens
+    const int per = (M + kSegThreads - 1) / kSegThreads;      // passes per wavefront
+    const int c0 = min(M, wave * per * kWave);
+    const int c1 = min(M, c0 + per * kWave);
+
+    // 1. every load at once: the cached passes' ids (index clamped into the
+    //    batch, so no load is conditional) and the mask
+    int idc[kCachedPasses];
+#pragma unroll
+    for (int i = 0; i < kCachedPasses; ++i) idc[i] = ids[min(c0 + i * kWave + lane, M - 1)];
+    const int e = (enabled && tid < L) ? enabled[tid] : 1;
+    for (int i = tid; i < kSegWaves * NB; i += kSegThreads) row[i] = 0;
+    for (int i = tid; i < L; i += kSegThreads) en[i] = (i == tid) ? e : (enabled ? enabled[i] : 1);
     __syncthreads();
-    // bucket L collects tokens without an (enabled) adapter
+
+    // the mask entry is read at a clamped index, so the lookups of several
+    // passes do not wait for one another
     auto bucket_of = [&](int v) {
         const bool in = v >= 0 && v < L;
-        return (in && (!enabled || enabled[v] != 0)) ? v : L;
+        const int on = en[in ? v : 0];
+        return (in && on != 0) ? v : L;
     };
-
-    // bucket of each of this thread's tokens; the first kCachedTiles tiles stay
-    // in registers for the scatter (their loads are issued together)
-    int bk[kCachedTiles];
-#pragma unroll
-    for (int i = 0; i < kCachedTiles; ++i) {
-        const int m = i * kSegThreads + tid;
-        int b = L;
-        if (m < M) b = bucket_of(ids[m]);
-        bk[i] = b;
-    }
     const int nbits = 32 - __clz(L);          // enough bits for buckets 0..L
     const unsigned long long lt = (1ull << lane) - 1ull;
     // lanes of this wavefront (with a token) whose bucket equals b: one
@@ -77,59 +95,75 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
         }
         return pe;
     };
-    // histogram: one LDS atomic per distinct bucket and wavefront (a batch
-    // of contiguous segments gives most wavefronts a single bucket)
-    auto count_tile = [&](int t0, int b) {
-        const bool act = t0 + tid < M;
+    int* my = row + wave * NB;
+    // bucket of pass i's token (L past the chunk); passes past the cached
+    // ones load their ids again
+    auto pass_bucket = [&](int i) {
+        const int m = c0 + i * kWave + lane;
+        return m < c1 ? bucket_of(ids[m]) : L;
+    };
+    int bk[kCachedPasses];
+#pragma unroll
+    for (int i = 0; i < kCachedPasses; ++i) {
+        const int v = idc[i];
+        const bool in = v >= 0 && v < L;
+        const int on = en[in ? v : 0];            // unconditional: the reads overlap
+        bk[i] = (c0 + i * kWave + lane < c1 && in && on != 0) ? v : L;
+    }
+
+    // 2. counts of this wavefront's chunk per bucket (wave-private row; the
+    //    first lane of each group of equal buckets adds the group's size)
+    auto count_pass = [&](int i, int b) {
+        const bool act = c0 + i * kWave + lane < c1;
         const unsigned long long pe = peers_of(b, act);
-        if (act && __popcll(pe & lt) == 0) atomicAdd(&count[b], __popcll(pe));
+        if (act && __popcll(pe & lt) == 0) my[b] += __popcll(pe);
     };
 #pragma unroll
-    for (int i = 0; i < kCachedTiles; ++i) {
-        if (i * kSegThreads >= M) break;
-        count_tile(i * kSegThreads, bk[i]);
-    }
-    for (int t0 = kCachedTiles * kSegThreads; t0 < M; t0 += kSegThreads)
-        count_tile(t0, t0 + tid < M ? bucket_of(ids[t0 + tid]) : L);
+    for (int i = 0; i < kCachedPasses; ++i)
+        if (c0 + i * kWave < c1) count_pass(i, bk[i]);
+    for (int i = kCachedPasses; c0 + i * kWave < c1; ++i) count_pass(i, pass_bucket(i));
     __syncthreads();
 
+    // 3a. per bucket: the wavefront rows become exclusive offsets
+    for (int b = tid; b < NB; b += kSegThreads) {
+        int run = 0;
+        for (int w = 0; w < kSegWaves; ++w) {
+            const int c = row[w * NB + b];
+            row[w * NB + b] = run;
+            run += c;
+        }
+        total[b] = run;
+    }
+    __syncthreads();
+
+    // 3b. bucket bases, segments and tile numbers (one wavefront)
     if (wave == 0) {
         int run = 0, segs = 0, trun = 0;
         for (int b0 = 0; b0 < NB; b0 += kWave) {
             const int b = b0 + lane;
-            const int c = (b < NB) ? count[b] : 0;
+            const int c = (b < NB) ? total[b] : 0;
             const bool present = (b < L) && (c > 0);
             const int nt = present ? (c + kRowTileRows - 1) / kRowTileRows : 0;
-            int inc = c, tinc = nt;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int t = __shfl_up(inc, o, kWave);
-                const int u = __shfl_up(tinc, o, kWave);
-                if (lane >= o) {
-                    inc += t;
-                    tinc += u;
-                }
-            }
+            const int inc = wave_incl_scan(c), tinc = wave_incl_scan(nt);
             const int excl = run + inc - c;
             const int texcl = trun + tinc - nt;
             if (b < NB) {
-                base[b] = excl;
                 bstart[b] = excl;
                 btile[b] = texcl;
             }
             const unsigned long long bal = __ballot(present);
-            const int s = segs + __popcll(bal & ((1ull << lane) - 1ull));
+            const int s = segs + __popcll(bal & lt);
             if (present) {
                 req_to_lora[s] = b;
                 seg_indptr[s + 1] = excl + c;
                 stile[s] = texcl;
                 sbucket[s] = b;
             }
-            run += __shfl(inc, kWave - 1, kWave);
-            trun += __shfl(tinc, kWave - 1, kWave);
+            run += __builtin_amdgcn_readlane(inc, kWave - 1);
+            trun += __builtin_amdgcn_readlane(tinc, kWave - 1);
             segs += __popcll(bal);
         }
-        const int m_valid = run - count[L];
+        const int m_valid = run - total[L];
         if (lane == 0) {
             seg_indptr[0] = 0;
             num_segments[0] = segs;
@@ -144,42 +178,37 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     __syncthreads();
 
     // tile schedule: per 64-row tile its segment, adapter, first position and
-    // row count; rows past the count are marked -1 in tile_rows
+    // row count; rows past the count are marked -1 in tile_rows.  One
+    // wavefront per tile, lane r for row r: the tile's segment is the last s
+    // with stile[s] <= t, found 64 segments at a time by a ballot.
     {
         const int segs = s_segs;
         const int tiles = min(s_tiles, max_tiles);
-        for (int t = tid; t < tiles; t += kSegThreads) {
-            int lo = 0, hi = segs - 1;                 // last s with stile[s] <= t
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) / 2;
-                if (stile[mid] <= t) lo = mid; else hi = mid - 1;
+        for (int t = wave; t < tiles; t += kSegWaves) {
+            int s = 0;
+            for (int s0 = 0; s0 < segs; s0 += kWave) {
+                const bool le = s0 + lane < segs && stile[s0 + lane] <= t;
+                const unsigned long long bl = __ballot(le);
+                if (bl) s = s0 + 63 - __clzll(bl);
             }
-            const int b = sbucket[lo];
-            const int i = t - stile[lo];
+            const int b = sbucket[s];
+            const int i = t - stile[s];
             const int beg = bstart[b] + i * kRowTileRows;
-            const int n = min(kRowTileRows, count[b] - i * kRowTileRows);
-            tile_info[t * 4 + 0] = lo;
-            tile_info[t * 4 + 1] = b;
-            tile_info[t * 4 + 2] = beg;
-            tile_info[t * 4 + 3] = n;
-            for (int r = n; r < kRowTileRows; ++r) tile_rows[t * kRowTileRows + r] = -1;
+            const int n = min(kRowTileRows, total[b] - i * kRowTileRows);
+            if (lane < 4) tile_info[t * 4 + lane] = lane == 0 ? s : lane == 1 ? b : lane == 2 ? beg : n;
+            if (lane >= n) tile_rows[t * kRowTileRows + lane] = -1;
         }
     }
 
-    // one tile of kSegThreads tokens in token order; b = this thread's bucket
-    auto scatter_tile = [&](int t0, int b) {
-        const int m = t0 + tid;
-        const bool act = m < M;
+    // 4. scatter, pass by pass in token order; the wavefront's row now holds,
+    //    per bucket, the sorted offset of its next token inside the bucket
+    auto scatter_pass = [&](int i, int b) {
+        const int m = c0 + i * kWave + lane;
+        const bool act = m < c1;
         const unsigned long long peers = peers_of(b, act);
         const int rank_w = __popcll(peers & lt);
-        const bool leader = act && rank_w == 0;
-        if (leader) wcnt[wave * NB + b] = __popcll(peers);
-        __syncthreads();
         if (act) {
-            // earlier wavefronts' tokens of the bucket (all reads issued together)
-            int pos = base[b] + rank_w;
-#pragma unroll
-            for (int w = 0; w < kSegWaves; ++w) pos += w < wave ? wcnt[w * NB + b] : 0;
+            const int pos = bstart[b] + my[b] + rank_w;
             sorted_idx[pos] = m;
             if (b < L) {
                 const int rel = pos - bstart[b];
@@ -187,23 +216,15 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
                 if (t < max_tiles) tile_rows[t * kRowTileRows + rel % kRowTileRows] = m;
             }
         }
-        __syncthreads();
-        if (leader) {
-            atomicAdd(&base[b], __popcll(peers));
-            wcnt[wave * NB + b] = 0;
-        }
-        __syncthreads();
+        // every lane has read its offset before the group's first lane moves it
+        __builtin_amdgcn_wave_barrier();
+        if (act && rank_w == 0) my[b] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
     };
 #pragma unroll
-    for (int i = 0; i < kCachedTiles; ++i) {
-        if (i * kSegThreads >= M) break;
-        scatter_tile(i * kSegThreads, bk[i]);
-    }
-    for (int t0 = kCachedTiles * kSegThreads; t0 < M; t0 += kSegThreads) {
-        int b = L;
-        if (t0 + tid < M) b = bucket_of(ids[t0 + tid]);
-        scatter_tile(t0, b);
-    }
+    for (int i = 0; i < kCachedPasses; ++i)
+        if (c0 + i * kWave < c1) scatter_pass(i, bk[i]);
+    for (int i = kCachedPasses; c0 + i * kWave < c1; ++i) scatter_pass(i, pass_bucket(i));
 }
 
 // ---------------------------------------------------------------------------
@@ -235,7 +256,7 @@ hipError_t launch_build_segments(const int32_t* ids, const int32_t* enabled, int
                            tile_rows, num_tiles);
         return hipGetLastError();
     }
-    const size_t lds = (size_t)(L + 1) * (6 + kSegWaves) * sizeof(int);
+    const size_t lds = build_segments_lds(L);
     hipLaunchKernelGGL(k_build_segments, dim3(1), dim3(kSegThreads), lds, st, ids, enabled, M, L,
                        sorted_idx, seg_indptr, req_to_lora, num_segments, tile_info, tile_rows,
                        num_tiles, max_tiles);

@@ -28,10 +28,11 @@ def log(msg):
 
 
 # ---------------------------------------------------------------- segments
-def gpu_segments(ml, ids_np, L):
+def gpu_segments(ml, ids_np, L, enabled=None):
     ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
     seg = ml.Segments(len(ids_np), L)
-    ml.lora_build_segments(ids, seg)
+    en = None if enabled is None else torch.from_numpy(enabled.astype(np.int32)).cuda()
+    ml.lora_build_segments(ids, seg, adapter_enabled=en)
     torch.cuda.synchronize()
     M = len(ids_np)
     nt = int(seg.num_tiles.cpu()[0])
@@ -62,20 +63,32 @@ SEG_CASES = [
     ("wave_M63_one_id", lambda: (np.full(63, 2, np.int32), 3)),
     ("wave_M65_block_path", lambda: (np.random.default_rng(5).integers(-1, 6, 65).astype(np.int32),
                                      6)),
+    # adapter mask: disabled slots' tokens join the no-adapter bucket
+    ("mask_block_M3000_L50", lambda: (np.random.default_rng(6).integers(-1, 50, 3000).astype(np.int32),
+                                      50, (np.arange(50) % 3 != 1).astype(np.int32))),
+    ("mask_block_uncached_M9000_L7",
+     lambda: (np.random.default_rng(7).integers(-1, 7, 9000).astype(np.int32), 7,
+              np.array([1, 0, 1, 1, 0, 1, 1], np.int32))),
+    ("mask_wave_M40_L9", lambda: (np.random.default_rng(8).integers(-1, 9, 40).astype(np.int32),
+                                  9, (np.arange(9) % 2).astype(np.int32))),
+    ("mask_block_L1024_all_off",
+     lambda: (np.random.default_rng(9).integers(-1, 1024, 5000).astype(np.int32), 1024,
+              np.zeros(1024, np.int32))),
 ]
 
 
 @pytest.mark.parametrize("name,mk", SEG_CASES, ids=[c[0] for c in SEG_CASES])
 def test_segments_bit_exact(ml, name, mk):
-    ids, L = mk()
+    ids, L, *rest = mk()
+    enabled = rest[0] if rest else None
     log(f"segments {name} M={len(ids)} L={L}")
-    got = gpu_segments(ml, ids, L)
-    ref = O.build_segments(ids, L)
+    got = gpu_segments(ml, ids, L, enabled)
+    ref = O.build_segments(ids, L, enabled)
     assert np.array_equal(got[0], ref[0])
     assert np.array_equal(got[1], ref[1])
     assert np.array_equal(got[2], ref[2])
     assert got[3] == ref[3]
-    info, rows = O.tile_schedule(ids, L)
+    info, rows = O.tile_schedule(ids, L, enabled=enabled)
     assert np.array_equal(got[4], info)
     assert np.array_equal(got[5], rows)
 
