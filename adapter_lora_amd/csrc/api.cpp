@@ -1,8 +1,10 @@
 // C ABI entry points: argument checks, workspace layout, launches.
 // Nothing here allocates device memory or synchronises (except
 // lora_read_device_error, which is documented to synchronise).
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -22,6 +24,46 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 lora_status from_hip(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_HIP_ERROR; }
+
+// roctx ranges around the entry points that launch work, for profiler
+// timelines (rocprofv3 --marker-trace).  Off unless MLORA_ROCTX=1 when the
+// first call is made; the roctx library is then looked up at run time, so
+// the library has no link dependency on it and a call pays one branch when
+// ranges are off.
+struct Roctx {
+    int (*push)(const char*) = nullptr;
+    int (*pop)() = nullptr;
+    Roctx() {
+        const char* on = getenv("MLORA_ROCTX");
+        if (!on || strcmp(on, "1") != 0) return;
+        void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+        if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+        if (!h) return;
+        push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+        pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+        if (!push || !pop) push = nullptr, pop = nullptr;
+    }
+};
+
+const Roctx& roctx() {
+    static const Roctx r;
+    return r;
+}
+
+class Range {
+  public:
+    explicit Range(const char* name) : on_(roctx().push != nullptr) {
+        if (on_) roctx().push(name);
+    }
+    ~Range() {
+        if (on_) roctx().pop();
+    }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+
+  private:
+    bool on_;
+};
 
 int64_t n_total(const lora_weights_t* w) { return w->slice_offsets[w->n_slices]; }
 
@@ -197,11 +239,13 @@ size_t lora_workspace_size(const lora_weights_t* w, int32_t M) {
 }
 
 lora_status lora_workspace_init(void* workspace, size_t bytes, hipStream_t stream) {
+    const Range range("lora_workspace_init");
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) return LORA_INVALID_ARG;
     return from_hip(launch_fill_zero(workspace, bytes, stream));
 }
 
 lora_status lora_read_device_error(void* workspace, int32_t* out, hipStream_t stream) {
+    const Range range("lora_read_device_error");
     if (!workspace || !out) return LORA_INVALID_ARG;
     int v = 0;
     hipError_t e = hipMemcpyAsync(&v, workspace, sizeof(int), hipMemcpyDeviceToHost, stream);
@@ -251,6 +295,7 @@ lora_status lora_table_plan(int32_t L, const int32_t* ranks, int32_t n_slices, i
 lora_status lora_pack_adapter(int32_t dtype, int32_t K, int64_t N_total, int32_t n_slices,
                               int32_t rank, int32_t rank_pad, const void* A_src,
                               const void* B_src, void* A_dst, void* B_dst, hipStream_t stream) {
+    const Range range("lora_pack_adapter");
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_INVALID_ARG;
     if (K <= 0 || N_total <= 0 || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_INVALID_ARG;
     if (rank < 0 || rank > LORA_MAX_RANK) return LORA_INVALID_ARG;
@@ -272,6 +317,7 @@ lora_status lora_build_segments(const int32_t* ids, const int32_t* adapter_enabl
                                 int32_t* req_to_lora, int32_t* num_segments, int32_t* tile_info,
                                 int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
                                 hipStream_t stream) {
+    const Range range("lora_build_segments");
     if (M < 0 || M > (1 << 24) || L < 1 || L > LORA_MAX_ADAPTERS) return LORA_INVALID_ARG;
     if (!seg_indptr || !req_to_lora || !num_segments || !num_tiles) return LORA_INVALID_ARG;
     if (max_tiles < lora_tile_capacity(M, L)) return LORA_INVALID_ARG;
@@ -284,6 +330,7 @@ lora_status lora_build_segments(const int32_t* ids, const int32_t* adapter_enabl
 lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int32_t M,
                         const lora_segments_t* seg, float* S, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
+    const Range range("lora_shrink");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
@@ -301,6 +348,7 @@ lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int
 lora_status lora_expand_add(const lora_weights_t* w, const float* S, int32_t M,
                             const lora_segments_t* seg, void* y, int64_t ldy,
                             hipStream_t stream) {
+    const Range range("lora_expand_add");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
@@ -315,6 +363,7 @@ lora_status lora_expand_add(const lora_weights_t* w, const float* S, int32_t M,
 lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64_t ldx,
                                    int32_t M, const lora_segments_t* seg, void* y, int64_t ldy,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const Range range("lora_shrink_expand_add");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0 || M > (1 << 24)) return LORA_INVALID_ARG;
@@ -340,6 +389,7 @@ lora_status lora_linear_fused(const lora_weights_t* w, const void* W, int64_t ld
                               const void* x, int64_t ldx, int32_t M, const lora_segments_t* seg,
                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
+    const Range range("lora_linear_fused");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (w->dtype != LORA_BF16) return LORA_UNSUPPORTED;
@@ -367,6 +417,7 @@ lora_status lora_fused_decode(const lora_weights_t* w, const int32_t* ids,
                               int32_t* tile_info, int32_t* tile_rows, int32_t* num_tiles,
                               int32_t max_tiles, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
+    const Range range("lora_fused_decode");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0) return LORA_INVALID_ARG;
@@ -390,6 +441,7 @@ lora_status lora_fused_decode_noalloc(const lora_weights_t* w, const int32_t* id
                                       int32_t* num_segments, int32_t* tile_info,
                                       int32_t* tile_rows, int32_t* num_tiles, int32_t max_tiles,
                                       int32_t* error_word, hipStream_t stream) {
+    const Range range("lora_fused_decode_noalloc");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (M < 0) return LORA_INVALID_ARG;
@@ -410,6 +462,7 @@ lora_status lora_fused_decode_noalloc(const lora_weights_t* w, const int32_t* id
 lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t emb, int32_t rank,
                                         int32_t rank_pad, const void* A_src, const void* B_src,
                                         void* A_dst, void* B_dst, hipStream_t stream) {
+    const Range range("lora_pack_embedding_adapter");
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_INVALID_ARG;
     if (vocab <= 0 || vocab % 8 || emb <= 0 || emb % 8) return LORA_INVALID_ARG;
     if (rank < 0 || rank > LORA_MAX_RANK) return LORA_INVALID_ARG;
@@ -423,6 +476,7 @@ lora_status lora_pack_embedding_adapter(int32_t dtype, int32_t vocab, int64_t em
 
 lora_status lora_embedding_shrink(const lora_weights_t* w, const int32_t* tokens, int32_t M,
                                   const lora_segments_t* seg, float* S, hipStream_t stream) {
+    const Range range("lora_embedding_shrink");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (w->n_slices != 1) return LORA_INVALID_ARG;
@@ -440,6 +494,7 @@ lora_status lora_embedding_decode(const lora_weights_t* w, const int32_t* ids,
                                   int32_t* seg_indptr, int32_t* req_to_lora,
                                   int32_t* num_segments, int32_t* tile_info, int32_t* tile_rows,
                                   int32_t* num_tiles, int32_t max_tiles, hipStream_t stream) {
+    const Range range("lora_embedding_decode");
     lora_status st = check_weights(w);
     if (st != LORA_OK) return st;
     if (w->n_slices != 1) return LORA_INVALID_ARG;
@@ -500,6 +555,7 @@ lora_status lora_moe_align(const int32_t* topk_ids, const int32_t* ids,
                            int32_t L, int32_t block_size_m, int32_t max_tokens_padded,
                            int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
                            hipStream_t stream) {
+    const Range range("lora_moe_align");
     if (M < 0 || topk < 1 || topk > 16 || E < 1 || E > 256 || L < 1 || L > LORA_MAX_ADAPTERS)
         return LORA_INVALID_ARG;
     if ((int64_t)M * topk > (1 << 24)) return LORA_INVALID_ARG;
@@ -557,6 +613,7 @@ lora_status lora_moe_gate_up_add(const lora_moe_weights_t* w, const void* x, int
                                  int32_t M, int32_t topk, const lora_moe_align_t* align,
                                  void* cache1, int64_t ld1, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
+    const Range range("lora_moe_gate_up_add");
     return moe_delta(w, 0, x, ldx, M, topk, align, cache1, ld1, workspace, workspace_bytes, stream);
 }
 
@@ -564,12 +621,14 @@ lora_status lora_moe_down_add(const lora_moe_weights_t* w, const void* cache2, i
                               int32_t M, int32_t topk, const lora_moe_align_t* align,
                               void* cache3, int64_t ld3, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
+    const Range range("lora_moe_down_add");
     return moe_delta(w, 1, cache2, ld2, M, topk, align, cache3, ld3, workspace, workspace_bytes,
                      stream);
 }
 
 lora_status lora_moe_silu_and_mul(int32_t dtype, const void* cache1, int64_t ld1, void* cache2,
                                   int64_t ld2, int32_t P, int32_t I, hipStream_t stream) {
+    const Range range("lora_moe_silu_and_mul");
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_INVALID_ARG;
     if (P < 0 || I <= 0 || I % 8) return LORA_INVALID_ARG;
     if (P == 0) return LORA_OK;
@@ -582,6 +641,7 @@ lora_status lora_moe_silu_and_mul(int32_t dtype, const void* cache1, int64_t ld1
 lora_status lora_moe_topk_reduce(int32_t dtype, const void* cache3, int64_t ld3,
                                  const float* topk_weights, void* out, int64_t ldo, int32_t M,
                                  int32_t topk, int32_t H, hipStream_t stream) {
+    const Range range("lora_moe_topk_reduce");
     if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_INVALID_ARG;
     if (M < 0 || topk < 1 || topk > 16 || H <= 0 || H % 8) return LORA_INVALID_ARG;
     if (M == 0) return LORA_OK;

@@ -216,12 +216,28 @@ def decode_launch_grid(case):
     return s_max * (case.n_slices * r_max // 16) * C + s_max * tiles + 1
 
 
-def source_hash(files):
+def strip_comments(text):
+    """C/C++ source without its comments and blank lines (string literals in
+    these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
+def source_hash(files, read=None):
+    """Hash of the code (comments stripped) of `files`, so that an edit to
+    comments alone keeps a counter summary valid.  `read(path)` returns a
+    file's text (default: the working tree)."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(strip_comments(text).encode())
     return h.hexdigest()[:16]
 
 

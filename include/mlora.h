@@ -36,6 +36,11 @@
  *     the storage dtype once (round to nearest even).
  *   - Device pointers to x / y / A / B / cache buffers must be 16-byte
  *     aligned; leading dimensions and K, N are multiples of 8 elements.
+ *   - Profiling: with the environment variable MLORA_ROCTX=1 set before the
+ *     first call, every entry point that launches work (and
+ *     lora_read_device_error) is bracketed by a roctx range named after it
+ *     (rocprofv3 --marker-trace shows them).  The roctx library is looked up
+ *     at run time; without it, or without the variable, no range is made.
  */
 #ifndef MLORA_H
 #define MLORA_H

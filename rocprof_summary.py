@@ -21,8 +21,9 @@
       the same counter reads for the 256 MB streaming copy that bench.py runs
       (the hand-written k_stream kernel: 128 MB read, 128 MB written).
 
-The traffic summary carries a hash of the decode kernel's sources; bench.py
-reports the figure only while that hash still matches.
+The traffic summary carries a hash of the decode kernel's sources (their
+code, comments removed); bench.py reports the figure only while that hash
+still matches.
 """
 import csv
 import glob

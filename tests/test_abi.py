@@ -202,3 +202,41 @@ def test_binding_rejects_mismatched_operands_before_any_launch():
     with pytest.raises(ml.LoraError, match="weights are"):
         ml.lora_moe_topk_reduce(torch.zeros(8, 64, dtype=bf), torch.zeros(4, 2, dtype=f32),
                                 torch.zeros(4, 64, dtype=f32))
+
+
+ROCTX_PROBE = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+from adapter_lora_amd import _abi
+null = ctypes.c_void_p(0)
+st = _abi.lib.lora_build_segments(null, null, -1, 4, null, null, null, null, null, null, null,
+                                  8, null)
+maps = open("/proc/self/maps").read()
+print(st, int("rocprofiler-sdk-roctx" in maps))
+"""
+
+
+def roctx_library_present():
+    return any(os.path.exists(os.path.join(d, n)) for d in ("/opt/rocm/lib",)
+               for n in ("librocprofiler-sdk-roctx.so.1",))
+
+
+@pytest.mark.skipif(not roctx_library_present(), reason="no roctx library on this host")
+def test_roctx_ranges_are_opt_in():
+    """MLORA_ROCTX=1 makes the first range-carrying call load the roctx
+    library (looked up at run time); without it, nothing is loaded."""
+    from adapter_lora_amd import _abi
+    def run(env_value):
+        env = dict(os.environ)
+        env.pop("MLORA_ROCTX", None)
+        if env_value is not None:
+            env["MLORA_ROCTX"] = env_value
+        out = subprocess.run(["python", "-c", ROCTX_PROBE % ROOT], env=env, capture_output=True,
+                             text=True, timeout=120)
+        assert out.returncode == 0, out.stderr
+        st, loaded = out.stdout.split()
+        assert int(st) == _abi.LORA_INVALID_ARG
+        return int(loaded)
+    assert run("1") == 1
+    assert run(None) == 0
+    assert run("0") == 0
