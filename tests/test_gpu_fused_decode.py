@@ -236,3 +236,33 @@ def test_each_launch_tags_its_slots_afresh(ml):
                         [b.values for b in case.B], case.ranks, case.slice_sizes,
                         case.y_base.values)
     assert_close(to_f64(y), ref, case.dtype, case.y_base.values, "after other x")
+
+
+# Inputs in {-1, 0, 1} (workloads.integer_linear): every S value and every
+# delta is a small integer, exact in fp32 and in the S hi / lo bf16 pair, so
+# the device result equals the oracle's rounded result bit for bit.  The
+# cases cover the slot-mode view (L <= M), the segment view (L > M), the
+# enable mask, the MFMA consumers (ranks above 16) and the VALU ones.
+INT_CASES = [
+    ("slot_mode_bf16", lambda: W.integer_linear(31, 32, 4096, [4096], [16, 64, 32, 0, 48] * 4,
+                                                W.BF16), None),
+    ("segments_L_gt_M_bf16", lambda: W.integer_linear(32, 20, 1032, [520, 264],
+                                                      [16, 32, 64, 3] * 10, W.BF16), None),
+    ("masked_bf16", lambda: W.integer_linear(33, 48, 2048, [1024], [64, 16, 32, 9, 64, 16],
+                                             W.BF16), np.array([1, 0, 1, 1, 0, 1], np.int32)),
+    ("slot_mode_fp32", lambda: W.integer_linear(34, 64, 520, [264, 136], [16, 33, 64], W.F32),
+     None),
+]
+
+
+@pytest.mark.parametrize("name,mk,enabled", INT_CASES, ids=[c[0] for c in INT_CASES])
+def test_fused_decode_integer_bit_exact(ml, name, mk, enabled):
+    case = mk()
+    log(f"fused_decode integer {name} M={case.M} K={case.K} L={case.L}")
+    got, seg = run_decode(ml, case, enabled)
+    check_table(seg, case, enabled)
+    ref = O.lora_linear(case.x.values, case.ids, [a.values for a in case.A],
+                        [b.values for b in case.B], case.ranks, case.slice_sizes,
+                        case.y_base.values, enabled)
+    ref = W.make_tensor(ref.astype(np.float32), case.dtype).values     # one rounding
+    assert np.array_equal(got, ref)

@@ -155,3 +155,50 @@ def test_disabled_adapters_leave_caches(ml):
     torch.cuda.synchronize()
     assert np.array_equal(to_f64(c1), case.cache1.values)
     assert np.array_equal(to_f64(c3), case.cache3.values)
+
+
+# The whole chain on the device with exact arithmetic (workloads.
+# integer_moe_case): gate/up delta, down delta and top-k reduce are bit-exact
+# with the oracle's single rounding; the activation is checked to the
+# tolerance and its device output is what the oracle's down stage reads, so
+# every later stage is compared bit for bit.  Cases: the narrow expand, the
+# wide (16 x 1024) expand with a ragged last tile, shared outer matrices
+# with a disabled adapter.
+INT_MOE_CASES = [
+    ("narrow", lambda: W.integer_moe_case(1, M=90, H=264, I=64)),
+    ("wide_ragged", lambda: W.integer_moe_case(2, M=70, H=136, I=4104, rank=32,
+                                               block_size_m=32)),
+    ("shared_outer_masked", lambda: W.integer_moe_case(3, M=50, H=264, I=136, shared_outer=True,
+                                                       enabled=[1, 0, 1])),
+]
+
+
+@pytest.mark.parametrize("name,mk", INT_MOE_CASES, ids=[c[0] for c in INT_MOE_CASES])
+def test_moe_chain_integer_bit_exact(ml, name, mk):
+    case = mk()
+    log(f"moe integer chain {name} M={case.M} H={case.H} I={case.I} E={case.E} L={case.L}")
+    w, al, ws, cap = setup(ml, case)
+    tid, ids, en = case.topk_ids, case.ids, case.adapter_enabled
+    so = case.shared_outer
+    bf = lambda a: W.make_tensor(a.astype(np.float32), W.BF16).values   # one rounding
+    c1 = to_dev(case.cache1)
+    c3 = to_dev(case.cache3)
+    c2 = torch.empty(case.M * case.topk, case.I, dtype=c1.dtype, device="cuda")
+    out = torch.empty(case.M, case.H, dtype=c1.dtype, device="cuda")
+    wts = torch.from_numpy(case.topk_weights).cuda()
+    ml.lora_moe_gate_up_add(w, to_dev(case.x), case.topk, al, c1, ws)
+    ml.lora_moe_silu_and_mul(c1, c2)
+    ml.lora_moe_down_add(w, c2, case.M, case.topk, al, c3, ws)
+    ml.lora_moe_topk_reduce(c3, wts, out)
+    torch.cuda.synchronize()
+    r1 = O.moe_gate_up_add(case.x.values, case.cache1.values, tid, ids, en, case.A_gu.values,
+                           case.B_gu.values, so)
+    assert np.array_equal(to_f64(c1), bf(r1)), "gate/up"
+    got2 = to_f64(c2)
+    assert_close(got2, O.silu_and_mul(r1), W.BF16, None, "silu_and_mul")
+    r3 = O.moe_down_add(got2, case.cache3.values, tid, ids, en, case.A_d.values, case.B_d.values,
+                        so)
+    got3 = to_f64(c3)
+    assert np.array_equal(got3, bf(r3)), "down"
+    r4 = O.topk_reduce(got3, case.topk_weights.astype(np.float64))
+    assert np.array_equal(to_f64(out), bf(r4)), "top-k reduce"

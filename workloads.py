@@ -394,6 +394,53 @@ def moe_case(seed: int = 0, M: int = 256, H: int = 4096, I: int = 14336, E: int 
                    topk_ids, topk_w, x, A_gu, B_gu, A_d, B_d, c1, c3, shared_outer)
 
 
+def integer_moe_case(seed: int, M: int, H: int, I: int, E: int = 4, topk: int = 2, L: int = 3,
+                     rank: int = 16, block_size_m: int = 16, p_none: float = 0.15,
+                     enabled=None, shared_outer: bool = False, a_d_nnz: int = 32) -> MoECase:
+    """MoE-LoRA inputs whose whole chain is exact in fp32, in the S hi / lo
+    bf16 pair and in one final rounding, so device and oracle agree bit for
+    bit (the activation excepted, whose device output feeds the oracle's
+    next stage):
+      * x in {0, 1}; every gate/up A row one-hot (a single 1); every gate/up
+        B row one-hot with sign +-1: the gate/up delta is in {-1, 0, 1};
+      * cache1 gate half in {1, 2}, up half 0: after the delta the gate is in
+        {0, ..., 3} and the up value in {-1, 0, 1}, so silu(gate) * up is 0
+        or of magnitude in [0.7, 2.9] (bf16 steps of at least 2^-8);
+      * down A rows with at most `a_d_nnz` entries +-1: the down S values are
+        multiples of 2^-8 below 2^8 in magnitude (16 significant bits, exact
+        as a bf16 hi / lo pair); down B and cache3 in {-1, 0, 1};
+      * routing weights in {0.25, 0.5, 0.75, 1}."""
+    rng = np.random.default_rng([seed, 23])
+    topk_ids, _ = _route(rng, M, E, topk)
+    topk_w = rng.choice(np.array([0.25, 0.5, 0.75, 1.0], np.float32), size=(M, topk))
+    ids = rng.integers(0, L, size=M).astype(np.int32)
+    ids[rng.random(M) < p_none] = -1
+    en = np.ones(L, np.int32) if enabled is None else np.asarray(enabled, np.int32)
+    Eo = 1 if shared_outer else E
+    x = rng.integers(0, 2, size=(M, H)).astype(np.float32)
+    A_gu = np.zeros((L, Eo, rank, H), np.float32)
+    hot = rng.integers(0, H, size=(L, Eo, rank))
+    np.put_along_axis(A_gu, hot[..., None], 1.0, axis=3)
+    B_gu = np.zeros((L, E, 2 * I, rank), np.float32)
+    hot = rng.integers(0, rank, size=(L, E, 2 * I))
+    sign = rng.choice(np.array([-1.0, 1.0], np.float32), size=(L, E, 2 * I, 1))
+    np.put_along_axis(B_gu, hot[..., None], sign, axis=3)
+    A_d = np.zeros((L, E, rank, I), np.float32)
+    for l in range(L):
+        for e in range(E):
+            for j in range(rank):
+                pos = rng.choice(I, size=min(a_d_nnz, I), replace=False)
+                A_d[l, e, j, pos] = rng.choice(np.array([-1.0, 1.0], np.float32), size=len(pos))
+    B_d = rng.integers(-1, 2, size=(L, Eo, H, rank)).astype(np.float32)
+    c1 = np.zeros((M * topk, 2 * I), np.float32)
+    c1[:, :I] = rng.integers(1, 3, size=(M * topk, I))
+    c3 = rng.integers(-1, 2, size=(M * topk, H)).astype(np.float32)
+    mk = lambda a: make_tensor(a, BF16)
+    return MoECase(f"moe_integer_{seed}", BF16, M, H, I, E, topk, L, rank, block_size_m, ids, en,
+                   topk_ids, topk_w, mk(x), mk(A_gu), mk(B_gu), mk(A_d), mk(B_d), mk(c1), mk(c3),
+                   shared_outer)
+
+
 # ----------------------------------------------------------------------------
 # named workloads (full sizes) and their small parity counterparts
 # ----------------------------------------------------------------------------
