@@ -15,11 +15,11 @@ import torch
 
 from ._abi import (LORA_BF16, LORA_F32, LORA_MAX_ADAPTERS, LORA_MAX_RANK,
                    LORA_MAX_SLICES, LORA_DECODE_MAX_M, LORA_TILE_ROWS, LORA_DEVERR_WAIT,
-                   LORA_DEVERR_BAD_ID, LoraError, lib, lora_weights_t,
+                   LORA_DEVERR_BAD_ID, LORA_DEVERR_TABLE, LoraError, lib, lora_weights_t,
                    lora_segments_t, lora_moe_weights_t, lora_moe_align_t, check)
 
 __all__ = [
-    "LORA_BF16", "LORA_F32", "LORA_DEVERR_WAIT", "LORA_DEVERR_BAD_ID", "LoraError", "LoraTable",
+    "LORA_BF16", "LORA_F32", "LORA_DEVERR_WAIT", "LORA_DEVERR_BAD_ID", "LORA_DEVERR_TABLE", "LoraError", "LoraTable",
     "Segments", "Workspace",
     "MoeWeights", "MoeAlign",
     "lora_build_segments", "lora_tile_capacity", "lora_shrink", "lora_expand_add",

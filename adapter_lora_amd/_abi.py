@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MLORA_LIB", os.path.join(HERE, "libmlora.so"))
 
 LORA_OK, LORA_INVALID_ARG, LORA_UNSUPPORTED, LORA_HIP_ERROR = 0, 1, 2, 3
-LORA_DEVERR_WAIT, LORA_DEVERR_BAD_ID = 1, 2
+LORA_DEVERR_WAIT, LORA_DEVERR_BAD_ID, LORA_DEVERR_TABLE = 1, 2, 4
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_SLICES = 4
 LORA_RANK_ALIGN = 16

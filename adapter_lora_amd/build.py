@@ -2,9 +2,13 @@
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled, then linked into adapter_lora_amd/libmlora.so next to
-this file.  The benchmark's streaming reference kernel (stream_copy.hip) is
-linked into its own libmlora_stream.so beside it.  Run `python adapter_lora_amd/build.py` (not `-m`: importing the
-package loads the library) or __graft_entry__.build().
+this file.  The same sources compiled with MLORA_DEBUG (device-side checks
+of the segment tables the table-form calls are given, reported as
+LORA_DEVERR_TABLE) go into libmlora_debug.so; select it with
+MLORA_LIB=<path> before importing the package.  The benchmark's streaming
+reference kernel (stream_copy.hip) is linked into its own
+libmlora_stream.so.  Run `python adapter_lora_amd/build.py` (not `-m`:
+importing the package loads the library) or __graft_entry__.build().
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libmlora.so")
+DEBUG_OUT = os.path.join(HERE, "libmlora_debug.so")
 STREAM_OUT = os.path.join(HERE, "libmlora_stream.so")
 STREAM_SOURCES = ["stream_copy.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
@@ -34,9 +39,11 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    sub = os.path.join(BUILD_DIR, "debug") if debug else BUILD_DIR
+    obj = os.path.join(sub, os.path.basename(src) + ".o")
+    extra = ["-DMLORA_DEBUG"] if debug else []
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -57,15 +64,16 @@ def _link(objs, out):
 
 
 def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + STREAM_SOURCES
-    jobs = min(len(srcs), max(1, (os.cpu_count() or 4)))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], OUT)
-    _link(objs[len(SOURCES):], STREAM_OUT)
+    os.makedirs(os.path.join(BUILD_DIR, "debug"), exist_ok=True)
+    jobs = [(s, False) for s in SOURCES + STREAM_SOURCES] + [(s, True) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(len(jobs), os.cpu_count() or 4))) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(SOURCES)
+    _link(objs[:n], OUT)
+    _link(objs[n:n + len(STREAM_SOURCES)], STREAM_OUT)
+    _link(objs[n + len(STREAM_SOURCES):], DEBUG_OUT)
     if verbose:
-        print(f"built {OUT} and {STREAM_OUT}")
+        print(f"built {OUT}, {DEBUG_OUT} and {STREAM_OUT}")
     return OUT
 
 

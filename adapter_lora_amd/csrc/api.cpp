@@ -25,6 +25,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 lora_status from_hip(hipError_t e) { return e == hipSuccess ? LORA_OK : LORA_HIP_ERROR; }
 
+// The sticky error word of a linear workspace (its first word).
+int* ws_error(void* workspace) { return &reinterpret_cast<WsHeader*>(workspace)->error; }
+
 // roctx ranges around the entry points that launch work, for profiler
 // timelines (rocprofv3 --marker-trace).  Off unless MLORA_ROCTX=1 when the
 // first call is made; the roctx library is then looked up at run time, so
@@ -341,7 +344,8 @@ lora_status lora_shrink(const lora_weights_t* w, const void* x, int64_t ldx, int
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)))
         return LORA_INVALID_ARG;
     if (workspace_bytes < layout_for(w, M).total) return LORA_INVALID_ARG;
-    const LinearArgs a = make_args(w, seg, M);
+    LinearArgs a = make_args(w, seg, M);
+    a.err = ws_error(workspace);
     return from_hip(launch_shrink(a, x, ldx, S, workspace, stream));
 }
 
@@ -375,7 +379,8 @@ lora_status lora_shrink_expand_add(const lora_weights_t* w, const void* x, int64
         return LORA_INVALID_ARG;
     const LinearWs L = layout_for(w, M);
     if (workspace_bytes < L.total) return LORA_INVALID_ARG;
-    const LinearArgs a = make_args(w, seg, M);
+    LinearArgs a = make_args(w, seg, M);
+    a.err = ws_error(workspace);
     if (M <= LORA_DECODE_MAX_M)
         return from_hip(launch_decode_fused(a, nullptr, nullptr, SegOut{}, x, ldx, y, ldy,
                                             workspace, nullptr, stream));
@@ -403,7 +408,8 @@ lora_status lora_linear_fused(const lora_weights_t* w, const void* W, int64_t ld
         return LORA_INVALID_ARG;
     const LinearWs L = layout_for(w, M);
     if (workspace_bytes < L.total) return LORA_INVALID_ARG;
-    const LinearArgs a = make_args(w, seg, M);
+    LinearArgs a = make_args(w, seg, M);
+    a.err = ws_error(workspace);
     float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + L.S);
     hipError_t e = launch_shrink(a, x, ldx, S, workspace, stream);
     if (e != hipSuccess) return LORA_HIP_ERROR;

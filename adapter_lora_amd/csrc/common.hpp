@@ -257,6 +257,23 @@ static_assert(sizeof(WsHeader) == 256, "workspace header size");
 
 constexpr int kErrSpin = LORA_DEVERR_WAIT;
 constexpr int kErrBadId = LORA_DEVERR_BAD_ID;
+
+// Device-side checks of the segment table handed to the table-form calls,
+// compiled in only when the library is built with MLORA_DEBUG.
+#ifdef MLORA_DEBUG
+constexpr bool kTableChecks = true;
+#else
+constexpr bool kTableChecks = false;
+#endif
+
+// Wave-uniform call: true when any lane found a bad entry, which is then
+// reported once in `err` (may be null).
+__device__ __forceinline__ bool table_fault(int* err, bool bad) {
+    if (!kTableChecks) return false;
+    const bool any = __ballot(bad) != 0ull;
+    if (any && err && lane_id() == 0) atomicOr(err, LORA_DEVERR_TABLE);
+    return any;
+}
 constexpr int kMaxSpin = 1 << 20;
 
 }  // namespace mlora

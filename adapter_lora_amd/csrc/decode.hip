@@ -141,7 +141,7 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
     }
     // lane t: token at sorted position p0 + t
     v.tl = __shfl(v.tl, (v.p0 + lane) & (kWave - 1), kWave);
-    const int id = v.id < 0 ? 0 : v.id;
+    const int id = (v.id < 0 || v.id >= L) ? 0 : v.id;   // never index past the table
     if (small) {
         // id is the same in every lane: the entry is read with readlane
         const int q = id / kWave, src = id % kWave;
@@ -163,6 +163,12 @@ __device__ __forceinline__ SegView seg_view(const DecodeParams& p, const ViewArg
     // token id of the segment's t-th token (lane t reads token tl of lane t)
     v.tok = va.tokens ? __shfl(tk, v.tl & (kWave - 1), kWave) : 0;
     v.ms = p1 - v.p0;
+    if (kTableChecks && !va.ids && s < v.nseg) {
+        // a segment of the table must name a slot and lie inside the batch
+        const bool seg_ok = v.id >= 0 && v.id < L && v.p0 >= 0 && v.ms >= 0 && p1 <= M;
+        const bool tok_ok = lane >= v.ms || (v.tl >= 0 && v.tl < M);
+        if (table_fault(p.err, !(seg_ok && tok_ok))) v.id = -1;
+    }
     return v;
 }
 

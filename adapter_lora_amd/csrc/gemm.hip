@@ -105,7 +105,14 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
     const int q_rk = a.rank[lq];
     const int64_t q_bo = a.b_off[lq];
 
-    if (tid < kGM) s_tok[tid] = tid < rows ? a.sorted_idx[p0 + tid] : -1;
+    if (tid < kGM) {
+        int m = tid < rows ? a.sorted_idx[p0 + tid] : -1;
+        // (checked builds) a token index outside the batch is never stored
+        if (table_fault(a.err, tid < rows && (m < 0 || m >= a.M))) {
+            if (tid < rows && (m < 0 || m >= a.M)) m = -1;
+        }
+        s_tok[tid] = m;
+    }
 
     // ---- columns of the unit (one slice)
     int sl = 0;
@@ -117,8 +124,10 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
     const int tr = tid / 8, tc = tid % 8;
     const uint16_t* xrow[kGXL];
 #pragma unroll
-    for (int i = 0; i < kGXL; ++i)
-        xrow[i] = p.x + (int64_t)a.sorted_idx[p0 + min(tr + 32 * i, rows - 1)] * p.ldx;
+    for (int i = 0; i < kGXL; ++i) {
+        const int m = a.sorted_idx[p0 + min(tr + 32 * i, rows - 1)];
+        xrow[i] = p.x + (int64_t)((kTableChecks && (m < 0 || m >= a.M)) ? 0 : m) * p.ldx;
+    }
     const uint16_t* wrow[kGWL];
 #pragma unroll
     for (int i = 0; i < kGWL; ++i)
@@ -362,8 +371,10 @@ __global__ __launch_bounds__(kGThreads, 1) void k_gemm_lora(GemmParams p) {
                 beg = a.seg_indptr[s];
                 end = a.seg_indptr[s + 1];
                 const int id = a.req_to_lora[s];
-                rp = beg < p0 + rows ? a.rank[id] : 0;
-                bo = a.b_off[id];
+                const bool id_ok = id >= 0 && id < L;   // never index past the table
+                table_fault(a.err, beg < p0 + rows && !id_ok);
+                rp = (beg < p0 + rows && id_ok) ? a.rank[id] : 0;
+                bo = id_ok ? a.b_off[id] : 0;
             }
             if (beg >= p0 + rows) break;
             if (rp == 0) continue;

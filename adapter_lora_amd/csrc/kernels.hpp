@@ -34,6 +34,7 @@ struct LinearArgs {
     const int32_t* tile_rows;   // [max_tiles][64]: token index per row, -1 past the rows
     const int32_t* num_tiles;
     int max_tiles;
+    int* err;                   // workspace error word (null: none); table checks report here
 };
 
 // K columns handled by one shrink work unit (fused decode and MFMA shrink).

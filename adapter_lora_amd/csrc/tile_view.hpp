@@ -58,6 +58,14 @@ __device__ __forceinline__ TileView tile_view(const LinearArgs& a, int t, bool a
         v.off = offs[id];
     }
     if (t >= nt) v.seg = -1;
+    if (kTableChecks && t < nt) {
+        // the tile must lie inside the batch and name a slot of the table;
+        // rows past its count are -1
+        const bool head_ok = v.seg >= 0 && v.id >= 0 && v.id < a.L && v.n >= 1 &&
+                             v.n <= kRowTile && v.pbeg >= 0 && v.pbeg <= a.M - v.n;
+        const bool row_ok = lane < v.n ? (v.row >= 0 && v.row < a.M) : v.row == -1;
+        if (table_fault(a.err, !(head_ok && row_ok))) v.seg = -1;
+    }
     return v;
 }
 

@@ -160,9 +160,19 @@ lora_status lora_workspace_init(void* workspace, size_t bytes, hipStream_t strea
  *                       exist, the mixed-up-rows failure of the Ascend
  *                       walkthrough's s4.1 troubleshooting table, so it is
  *                       reported and never followed.
+ *   LORA_DEVERR_TABLE   (libraries built with MLORA_DEBUG only) a
+ *                       table-form call met a segment-table entry that does
+ *                       not fit the batch or the weight table: an adapter
+ *                       id outside [0, L), a token index outside [0, M), or
+ *                       a tile or segment reaching past M.  The tile or
+ *                       segment is skipped, never dereferenced.  Calls
+ *                       without a workspace (lora_expand_add,
+ *                       lora_embedding_shrink) skip such entries without
+ *                       reporting them.  The release library does not check.
  */
 #define LORA_DEVERR_WAIT 1
 #define LORA_DEVERR_BAD_ID 2
+#define LORA_DEVERR_TABLE 4
 
 lora_status lora_read_device_error(void* workspace, int32_t* out, hipStream_t stream);
 

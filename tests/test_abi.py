@@ -39,6 +39,18 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_debug_library_exports_the_same_boundary():
+    """libmlora_debug.so (MLORA_DEBUG: device-side segment-table checks) is
+    built beside the release library and exports the same symbols."""
+    dbg = os.path.join(ROOT, "adapter_lora_amd", "libmlora_debug.so")
+    assert os.path.exists(dbg), "run __graft_entry__.build() first"
+    out = subprocess.run(["nm", "-D", "--defined-only", dbg], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (lora_\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
 def test_binding_signature_table_matches_header():
     from adapter_lora_amd import _abi
     assert sorted(_abi.SIGNATURES) == declared_functions()
