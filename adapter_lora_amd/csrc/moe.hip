@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
                                                               const float* __restrict__ S,
                                                               T* __restrict__ out, int64_t ld_out,
                                                               int N, int n_groups, int tpw,
-                                                              int units) {
+                                                              int units, SChunks sc) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
@@ -337,9 +337,10 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
     const int n_begin = g * tpw * kNTile;
     const int n_end = min(N, n_begin + tpw * kNTile);
     if constexpr (sizeof(T) == 2) {
+        // bf16: S arrives as the shrink's K-chunk partials, summed while staged
         __shared__ uint4 lds[kExpandLds / 16];
-        expand_rows_bf16(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin, n_end,
-                         reinterpret_cast<uint16_t*>(out), ld_out, lds);
+        expand_rows_bf16<true>(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin,
+                               n_end, reinterpret_cast<uint16_t*>(out), ld_out, lds, sc);
     } else {
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
             expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out);
@@ -351,7 +352,8 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4)
                                                                    const float* __restrict__ S,
                                                                    uint16_t* __restrict__ out,
                                                                    int64_t ld_out, int N,
-                                                                   int n_groups, int units) {
+                                                                   int n_groups, int units,
+                                                                   SChunks sc) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
     __shared__ int s_wlast[kWideThreads / kWave];
     __shared__ uint4 lds[kWideLds / 16];
@@ -367,7 +369,8 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4)
         reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int n0 = g * kWideCols;
-    expand_rows_wide(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds);
+    expand_rows_wide<true>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds,
+                           sc);
 }
 
 template <typename T>
@@ -395,13 +398,23 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
-    int rb = (a.max_tokens_padded * a.r / 4 + 255) / 256;
-    if (rb < 1) rb = 1;
-    hipLaunchKernelGGL(k_moe_reduce, dim3((unsigned)rb, (unsigned)a.L), dim3(256), 0, st, P, C,
-                       cstride, S, a.r, a.max_tokens_padded, a.ntpp, a.sorted_token_ids,
-                       a.M * a.topk);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // bf16: the expand sums the partials of its own rows as it stages them (a
+    // workgroup reads 16 S columns x C chunks of its block's rows), which
+    // saves the reduce launch; fp32: a separate reduce into S
+    SChunks sc{1, 0};
+    const float* Sx = S;
+    if (sizeof(T) == 2) {
+        sc = SChunks{C, cstride};
+        Sx = P;
+    } else {
+        int rb = (a.max_tokens_padded * a.r / 4 + 255) / 256;
+        if (rb < 1) rb = 1;
+        hipLaunchKernelGGL(k_moe_reduce, dim3((unsigned)rb, (unsigned)a.L), dim3(256), 0, st, P, C,
+                           cstride, S, a.r, a.max_tokens_padded, a.ntpp, a.sorted_token_ids,
+                           a.M * a.topk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int n_tiles = (N + kNTile - 1) / kNTile;
     // one 256-column tile per workgroup: a workgroup walks its tiles one after
     // another, so spreading them over more workgroups overlaps their latencies
@@ -415,12 +428,12 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
         const int wg = (N + kWideCols - 1) / kWideCols;
         const int wunits = a.L * nblk * wg;
         hipLaunchKernelGGL(k_moe_expand_wide, dim3((unsigned)(wunits > 0 ? wunits : 1)),
-                           dim3(kWideThreads), 0, st, a, which, S,
+                           dim3(kWideThreads), 0, st, a, which, Sx,
                            static_cast<uint16_t*>(out),
-                           ld_out, N, wg, wunits);
+                           ld_out, N, wg, wunits, sc);
     } else {
-        hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, S,
-                           reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2);
+        hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, Sx,
+                           reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2, sc);
     }
     return hipGetLastError();
 }

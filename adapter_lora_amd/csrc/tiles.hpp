@@ -205,13 +205,80 @@ constexpr int kExpandLds = 64 * kYRowBytes + 2 * 64 * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int ypos(int r, int q) { return r * (kYRowBytes / 16) + (q ^ (r & 15)); }
 
+// Partial sums of S handed to the expand instead of S itself: the S value
+// at an offset is the sum of `C` chunk partials `cs` floats apart, added in
+// chunk order (the order of the separate reduce kernel).
+struct SChunks {
+    int C;
+    int64_t cs;
+};
+
+// One float4 of S as the sum of its chunk partials (zero when !ok); the
+// loads of up to kChunkBatch chunks are in flight together.
+constexpr int kChunkBatch = 4;
+
+__device__ __forceinline__ float4 chunk_sum4(const float* p, SChunks sc, bool ok) {
+    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc = *reinterpret_cast<const float4*>(p);
+    for (int c0 = 1; c0 < sc.C; c0 += kChunkBatch) {
+        float4 v[kChunkBatch];
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q)
+            v[q] = *reinterpret_cast<const float4*>(p + (int64_t)min(c0 + q, sc.C - 1) * sc.cs);
+#pragma unroll
+        for (int q = 0; q < kChunkBatch; ++q)
+            if (c0 + q < sc.C) {
+                acc.x += v[q].x; acc.y += v[q].y; acc.z += v[q].z; acc.w += v[q].w;
+            }
+    }
+    return acc;
+}
+
+// Stage `nrows` S rows (rank positions 0..rp-1 summed from their chunk
+// partials, zero past rp and for missing rows) into LDS as bf16 hi / lo
+// pairs.  The (row, float4) pairs below rp are dealt to the threads first,
+// one per thread and pass, so each thread's chunk loads are in flight
+// together; the positions past rp are then cleared.
+__device__ __forceinline__ void stage_s_chunks(const RowSet& rs, int r0, int rows, int nrows,
+                                               const float* __restrict__ S, int sld, int sc0,
+                                               SChunks sc, int rp, int nthreads,
+                                               uint16_t* __restrict__ sHi,
+                                               uint16_t* __restrict__ sLo) {
+    const int wa = rp / 4;                        // float4 per row below rp
+    for (int i = (int)threadIdx.x; i < nrows * wa; i += nthreads) {
+        const int row = i / wa, j = (i % wa) * 4;
+        const int sr = row < rows ? rs.in_row[r0 + row] : -1;
+        const float4 v4 =
+            chunk_sum4(S + (int64_t)(sr < 0 ? 0 : sr) * sld + sc0 + j, sc, sr >= 0);
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        uint32_t h[2], l[2];
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+            const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+            h[q / 2] = h0 | (h1 << 16);
+            l[q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
+                       (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
+        }
+        *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
+        *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
+    }
+    const int wz = LORA_MAX_RANK / 4 - wa;        // float4 per row past rp
+    for (int i = (int)threadIdx.x; i < nrows * wz; i += nthreads) {
+        const int row = i / wz, j = rp + (i % wz) * 4;
+        *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(0u, 0u);
+    }
+}
+
+// kSum: S is given as chunk partials (SChunks), summed while staged.
+template <bool kSum = false>
 __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -245,37 +312,41 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
             bop[nb][st] = ld16(B + (int64_t)min(n, n1 - 1) * rp + min(j, rp - 8));
         }
     }
-    // 1c. S rows: thread t covers row t / 4, rank positions 16 (t % 4) .. +16;
-    //     positions past rp are written as zeros, so the MFMA operand reads
-    //     below need no mask
-    {
-        const int row = tid / 4, qt = tid % 4;
-        const int sr = row < rows ? rs.in_row[r0 + row] : -1;
-        float4 sv[4];
+    if constexpr (kSum) {
+        stage_s_chunks(rs, r0, rows, 64, S, sld, sc0, sc, rp, kTileThreads, sHi, sLo);
+    } else {
+        // 1c. S rows: thread t covers row t / 4, rank positions 16 (t % 4) .. +16;
+        //     positions past rp are written as zeros, so the MFMA operand reads
+        //     below need no mask
+        {
+            const int row = tid / 4, qt = tid % 4;
+            const int sr = row < rows ? rs.in_row[r0 + row] : -1;
+            float4 sv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = qt * 16 + e * 4;
-            sv[e] = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
-        }
-        uint32_t h[8], l[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float v[4] = {sv[e].x, sv[e].y, sv[e].z, sv[e].w};
-#pragma unroll
-            for (int q = 0; q < 4; q += 2) {
-                const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
-                const uint32_t l0 = f32_to_bf16(v[q] - bf16_to_f32(h0));
-                const uint32_t l1 = f32_to_bf16(v[q + 1] - bf16_to_f32(h1));
-                h[e * 2 + q / 2] = h0 | (h1 << 16);
-                l[e * 2 + q / 2] = l0 | (l1 << 16);
+            for (int e = 0; e < 4; ++e) {
+                const int j = qt * 16 + e * 4;
+                sv[e] = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
             }
+            uint32_t h[8], l[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v[4] = {sv[e].x, sv[e].y, sv[e].z, sv[e].w};
+#pragma unroll
+                for (int q = 0; q < 4; q += 2) {
+                    const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+                    const uint32_t l0 = f32_to_bf16(v[q] - bf16_to_f32(h0));
+                    const uint32_t l1 = f32_to_bf16(v[q + 1] - bf16_to_f32(h1));
+                    h[e * 2 + q / 2] = h0 | (h1 << 16);
+                    l[e * 2 + q / 2] = l0 | (l1 << 16);
+                }
+            }
+            uint4* hp = reinterpret_cast<uint4*>(sHi + row * kSLds + qt * 16);
+            uint4* lp = reinterpret_cast<uint4*>(sLo + row * kSLds + qt * 16);
+            hp[0] = make_uint4(h[0], h[1], h[2], h[3]);
+            hp[1] = make_uint4(h[4], h[5], h[6], h[7]);
+            lp[0] = make_uint4(l[0], l[1], l[2], l[3]);
+            lp[1] = make_uint4(l[4], l[5], l[6], l[7]);
         }
-        uint4* hp = reinterpret_cast<uint4*>(sHi + row * kSLds + qt * 16);
-        uint4* lp = reinterpret_cast<uint4*>(sLo + row * kSLds + qt * 16);
-        hp[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        hp[1] = make_uint4(h[4], h[5], h[6], h[7]);
-        lp[0] = make_uint4(l[0], l[1], l[2], l[3]);
-        lp[1] = make_uint4(l[4], l[5], l[6], l[7]);
     }
     __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
     __syncthreads();
@@ -341,18 +412,22 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs over columns [n_begin, n_end), one 64 x 256 tile at a time.
+template <bool kSum = false>
 __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp,
                                                  int n_begin, int n_end,
                                                  uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0}) {
     for (int r0 = 0; r0 < rs.n; r0 += 64) {
         const int rows = min(64, rs.n - r0);
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
-            expand_tile_bf16(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end), y,
-                             ldy_, lds, reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16),
-                             reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16) + 64 * kSLds);
+            expand_tile_bf16<kSum>(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end),
+                                   y, ldy_, lds,
+                                   reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16),
+                                   reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16) +
+                                       64 * kSLds,
+                                   sc);
     }
 }
 
@@ -373,13 +448,14 @@ constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
 
+template <bool kSum = false>
 __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;                 // 0..7
@@ -416,23 +492,27 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
             bop[nb][1] = ld16(B + (int64_t)n * rp + min(32 + lq * 8, rp - 8));
         }
     }
-    // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
-    //     .. +4; positions past rp are written as zeros
-    if (tid < 256) {
-        const int row = tid / 16, j = (tid % 16) * 4;
-        const int sr = row < rows ? rs.in_row[r0 + row] : -1;
-        const float4 v4 = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
-        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-        uint32_t h[2], l[2];
+    if constexpr (kSum) {
+        stage_s_chunks(rs, r0, rows, 16, S, sld, sc0, sc, rp, kWideThreads, sHi, sLo);
+    } else {
+        // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
+        //     .. +4; positions past rp are written as zeros
+        if (tid < 256) {
+            const int row = tid / 16, j = (tid % 16) * 4;
+            const int sr = row < rows ? rs.in_row[r0 + row] : -1;
+            const float4 v4 = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
+            const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+            uint32_t h[2], l[2];
 #pragma unroll
-        for (int q = 0; q < 4; q += 2) {
-            const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
-            h[q / 2] = h0 | (h1 << 16);
-            l[q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
-                       (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
+            for (int q = 0; q < 4; q += 2) {
+                const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+                h[q / 2] = h0 | (h1 << 16);
+                l[q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
+                           (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
+            }
+            *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
+            *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
         }
-        *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
-        *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
     }
     __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
     __syncthreads();
@@ -480,16 +560,17 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
+template <bool kSum = false>
 __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0}) {
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
     uint16_t* sLo = sHi + 16 * kSLds;
     for (int r0 = 0; r0 < rs.n; r0 += 16)
-        expand_wide_bf16(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds, sHi,
-                         sLo);
+        expand_wide_bf16<kSum>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
+                               sHi, sLo, sc);
 }
 
 // ---------------------------------------------------------------------------
