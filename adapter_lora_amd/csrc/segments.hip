@@ -124,13 +124,17 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     for (int i = kCachedPasses; c0 + i * kWave < c1; ++i) count_pass(i, pass_bucket(i));
     __syncthreads();
 
-    // 3a. per bucket: the wavefront rows become exclusive offsets
+    // 3a. per bucket: the wavefront rows become exclusive offsets (all 16
+    //     counts read before any is rewritten, so the reads overlap)
     for (int b = tid; b < NB; b += kSegThreads) {
+        int c[kSegWaves];
+#pragma unroll
+        for (int w = 0; w < kSegWaves; ++w) c[w] = row[w * NB + b];
         int run = 0;
+#pragma unroll
         for (int w = 0; w < kSegWaves; ++w) {
-            const int c = row[w * NB + b];
             row[w * NB + b] = run;
-            run += c;
+            run += c[w];
         }
         total[b] = run;
     }
@@ -180,11 +184,32 @@ __global__ __launch_bounds__(kSegThreads) void k_build_segments(
     // tile schedule: per 64-row tile its segment, adapter, first position and
     // row count; rows past the count are marked -1 in tile_rows.  One
     // wavefront per tile, lane r for row r: the tile's segment is the last s
-    // with stile[s] <= t, found 64 segments at a time by a ballot.
+    // with stile[s] <= t, found by a ballot (64 segments at a time past 64).
     {
         const int segs = s_segs;
         const int tiles = min(s_tiles, max_tiles);
-        for (int t = wave; t < tiles; t += kSegWaves) {
+        // up to 64 segments: lane s holds segment s's first tile, adapter,
+        // first position and size, read once per wavefront, so a tile costs
+        // a ballot and four readlanes instead of a chain of LDS reads
+        const bool in_regs = segs <= kWave;
+        int g_st = 0, g_b = 0, g_beg = 0, g_n = 0;
+        if (in_regs && lane < segs) {
+            g_st = stile[lane];
+            g_b = sbucket[lane];
+            g_beg = bstart[g_b];
+            g_n = total[g_b];
+        }
+        for (int t = wave; in_regs && t < tiles; t += kSegWaves) {
+            const unsigned long long bl = __ballot(lane < segs && g_st <= t);
+            const int s = 63 - __clzll(bl);        // stile[0] = 0 <= t: never empty
+            const int b = __builtin_amdgcn_readlane(g_b, s);
+            const int i = t - __builtin_amdgcn_readlane(g_st, s);
+            const int beg = __builtin_amdgcn_readlane(g_beg, s) + i * kRowTileRows;
+            const int n = min(kRowTileRows, __builtin_amdgcn_readlane(g_n, s) - i * kRowTileRows);
+            if (lane < 4) tile_info[t * 4 + lane] = lane == 0 ? s : lane == 1 ? b : lane == 2 ? beg : n;
+            if (lane >= n) tile_rows[t * kRowTileRows + lane] = -1;
+        }
+        for (int t = wave; !in_regs && t < tiles; t += kSegWaves) {
             int s = 0;
             for (int s0 = 0; s0 < segs; s0 += kWave) {
                 const bool le = s0 + lane < segs && stile[s0 + lane] <= t;
