@@ -316,7 +316,7 @@ __global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride
     }
 }
 
-template <typename T>
+template <typename T, int kSteps>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_moe_expand(MoeArgs a, int which,
                                                               const float* __restrict__ S,
                                                               T* __restrict__ out, int64_t ld_out,
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
     if constexpr (sizeof(T) == 2) {
         // bf16: S arrives as the shrink's K-chunk partials, summed while staged
         __shared__ uint4 lds[kExpandLds / 16];
-        expand_rows_bf16<true>(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin,
+        expand_rows_bf16<true, kSteps>(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin,
                                n_end, reinterpret_cast<uint16_t*>(out), ld_out, lds, sc);
     } else {
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
 }
 
 // bf16 expand over wide tiles: unit = (aligned block, 1024 output columns).
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_moe_expand_wide(MoeArgs a, int which,
+template <int kSteps>
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(kSteps == 1 ? 4 : 2))) void k_moe_expand_wide(MoeArgs a, int which,
                                                                    const float* __restrict__ S,
                                                                    uint16_t* __restrict__ out,
                                                                    int64_t ld_out, int N,
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(4)
         reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
     const int n0 = g * kWideCols;
-    expand_rows_wide<true>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds,
+    expand_rows_wide<true, kSteps>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds,
                            sc);
 }
 
@@ -424,16 +425,27 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
     const unsigned g2 = (unsigned)(units2 > 0 ? units2 : 1);
     // wide 16 x 1024 tiles when the output is wide enough that 64 x 256 tiles
     // would need many rounds of mostly idle workgroups (the gate/up output)
+    // rank <= 32: one 32-wide MFMA step, half the B operands in registers
+    const bool one = a.r <= 32;
     if (sizeof(T) == 2 && N >= 2 * kWideCols * 4) {
         const int wg = (N + kWideCols - 1) / kWideCols;
         const int wunits = a.L * nblk * wg;
-        hipLaunchKernelGGL(k_moe_expand_wide, dim3((unsigned)(wunits > 0 ? wunits : 1)),
-                           dim3(kWideThreads), 0, st, a, which, Sx,
-                           static_cast<uint16_t*>(out),
-                           ld_out, N, wg, wunits, sc);
+        const dim3 grid((unsigned)(wunits > 0 ? wunits : 1));
+        uint16_t* o = static_cast<uint16_t*>(out);
+        if (one)
+            hipLaunchKernelGGL(k_moe_expand_wide<1>, grid, dim3(kWideThreads), 0, st, a, which,
+                               Sx, o, ld_out, N, wg, wunits, sc);
+        else
+            hipLaunchKernelGGL(k_moe_expand_wide<2>, grid, dim3(kWideThreads), 0, st, a, which,
+                               Sx, o, ld_out, N, wg, wunits, sc);
     } else {
-        hipLaunchKernelGGL((k_moe_expand<T>), dim3(g2), dim3(kTileThreads), 0, st, a, which, Sx,
-                           reinterpret_cast<T*>(out), ld_out, N, n_groups, tpw, units2, sc);
+        T* o = reinterpret_cast<T*>(out);
+        if (one)
+            hipLaunchKernelGGL((k_moe_expand<T, 1>), dim3(g2), dim3(kTileThreads), 0, st, a,
+                               which, Sx, o, ld_out, N, n_groups, tpw, units2, sc);
+        else
+            hipLaunchKernelGGL((k_moe_expand<T, 2>), dim3(g2), dim3(kTileThreads), 0, st, a,
+                               which, Sx, o, ld_out, N, n_groups, tpw, units2, sc);
     }
     return hipGetLastError();
 }

@@ -279,7 +279,10 @@ __device__ __forceinline__ void stage_s_chunks(const RowSet& rs, int r0, int row
 }
 
 // kSum: S is given as chunk partials (SChunks), summed while staged.
-template <bool kSum = false>
+// kSteps: 32-wide rank steps the code is built for; 1 needs rp <= 32 and
+// keeps half the B operands out of registers (the MoE launches, whose rank
+// is known at launch, pick it; the dense launches mix ranks up to 64).
+template <bool kSum = false, int kSteps = 2>
 __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
@@ -322,12 +325,12 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
                                          16, 0, 0);
     }
     // 1b. B operands: rows nw + 16*nb + lr, 8 rank values at st*32 + lq*8
-    uint4 bop[4][2];
+    uint4 bop[4][kSteps];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
         const int n = nw + nb * 16 + lr;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < kSteps; ++st) {
             const int j = st * 32 + lq * 8;
             // clamped, not masked: columns past n1 are never written back and
             // rank positions past rp meet zero S values
@@ -337,9 +340,9 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
     if constexpr (kSum) {
         stage_s_chunks(rs, r0, rows, 64, S, sld, sc0, sc, rp, kTileThreads, sHi, sLo);
     } else {
-        // 1c. S rows: thread t covers row t / 4, rank positions 16 (t % 4) .. +16;
-        //     positions past rp are written as zeros, so the MFMA operand reads
-        //     below need no mask
+        // 1c. S rows (loaded at step 0) split into hi / lo in LDS; positions
+        //     past rp are written as zeros, so the MFMA operand reads below
+        //     need no mask
         {
             const int row = srow, qt = sqt;
             float4 sv[4];
@@ -371,9 +374,9 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
     // 2. MFMA; each 16 x 16 result is added into the LDS tile
     if (nw < n1) {
         // S operands of the next row group are read while this one's MFMAs run
-        uint4 shi[2], slo[2], nhi[2], nlo[2];
+        uint4 shi[kSteps], slo[kSteps], nhi[kSteps], nlo[kSteps];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < kSteps; ++st) {
             shi[st] = ld16(sHi + lr * kSLds + st * 32 + lq * 8);
             slo[st] = ld16(sLo + lr * kSLds + st * 32 + lq * 8);
         }
@@ -382,7 +385,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
             if (rg * 16 >= rows) break;
             if (rg < 3) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
+                for (int st = 0; st < kSteps; ++st) {
                     nhi[st] = ld16(sHi + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
                     nlo[st] = ld16(sLo + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
                 }
@@ -392,7 +395,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
             for (int nb = 0; nb < 4; ++nb) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
+                for (int st = 0; st < kSteps; ++st) {
                     if (st < nsteps) {
                         acc = mfma_bf16(bop[nb][st], shi[st], acc);
                         acc = mfma_bf16(bop[nb][st], slo[st], acc);
@@ -410,7 +413,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
                 *yp = nv;
             }
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < kSteps; ++st) {
                 shi[st] = nhi[st];
                 slo[st] = nlo[st];
             }
@@ -433,7 +436,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs over columns [n_begin, n_end), one 64 x 256 tile at a time.
-template <bool kSum = false>
+template <bool kSum = false, int kSteps = 2>
 __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp,
@@ -443,7 +446,7 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
     for (int r0 = 0; r0 < rs.n; r0 += 64) {
         const int rows = min(64, rs.n - r0);
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
-            expand_tile_bf16<kSum>(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end),
+            expand_tile_bf16<kSum, kSteps>(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end),
                                    y, ldy_, lds,
                                    reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16),
                                    reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16) +
@@ -469,7 +472,7 @@ constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
 
-template <bool kSum = false>
+template <bool kSum = false, int kSteps = 2>
 __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
@@ -482,7 +485,7 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
     const int wave = tid / kWave;                 // 0..7
     const int lr = lane % 16;
     const int lq = lane / 16;
-    const int nsteps = (rp + 31) / 32;
+    const int nsteps = kSteps == 1 ? 1 : (rp + 31) / 32;
     const int nw = n0 + wave * 128;
     const int nchunks = (n1 - n0) / 8;            // valid 16-byte chunks per row
     // 1a. y rows -> LDS: 32 wave instructions of 1 KB (half a row); position
@@ -499,18 +502,20 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
                                          0);
     }
     // 1b. B operands: rows nw + 16 nb + lr (clamped; see expand_tile_bf16)
-    uint4 bop[8][2];
+    uint4 bop[8][kSteps];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
         const int n = min(nw + nb * 16 + lr, n1 - 1);
         bop[nb][0] = ld16(B + (int64_t)n * rp + min(lq * 8, rp - 8));
-        bop[nb][1] = make_uint4(0, 0, 0, 0);
+        if constexpr (kSteps > 1) bop[nb][1] = make_uint4(0, 0, 0, 0);
     }
-    if (nsteps > 1) {
+    if constexpr (kSteps > 1) {
+        if (nsteps > 1) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int n = min(nw + nb * 16 + lr, n1 - 1);
-            bop[nb][1] = ld16(B + (int64_t)n * rp + min(32 + lq * 8, rp - 8));
+            for (int nb = 0; nb < 8; ++nb) {
+                const int n = min(nw + nb * 16 + lr, n1 - 1);
+                bop[nb][1] = ld16(B + (int64_t)n * rp + min(32 + lq * 8, rp - 8));
+            }
         }
     }
     if constexpr (kSum) {
@@ -539,13 +544,15 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
     __syncthreads();
     // 2. MFMA: the one 16-row group; each 16 x 16 result is added into the tile
     if (nw < n1) {
-        uint4 shi[2], slo[2];
+        uint4 shi[kSteps], slo[kSteps];
         shi[0] = ld16(sHi + lr * kSLds + lq * 8);
         slo[0] = ld16(sLo + lr * kSLds + lq * 8);
-        shi[1] = slo[1] = make_uint4(0, 0, 0, 0);
-        if (nsteps > 1) {
-            shi[1] = ld16(sHi + lr * kSLds + 32 + lq * 8);
-            slo[1] = ld16(sLo + lr * kSLds + 32 + lq * 8);
+        if constexpr (kSteps > 1) {
+            shi[1] = slo[1] = make_uint4(0, 0, 0, 0);
+            if (nsteps > 1) {
+                shi[1] = ld16(sHi + lr * kSLds + 32 + lq * 8);
+                slo[1] = ld16(sLo + lr * kSLds + 32 + lq * 8);
+            }
         }
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
@@ -557,9 +564,11 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
                            __uint_as_float(old.y << 16), __uint_as_float(old.y & 0xffff0000u)};
             acc = mfma_bf16(bop[nb][0], shi[0], acc);
             acc = mfma_bf16(bop[nb][0], slo[0], acc);
-            if (nsteps > 1) {
-                acc = mfma_bf16(bop[nb][1], shi[1], acc);
-                acc = mfma_bf16(bop[nb][1], slo[1], acc);
+            if constexpr (kSteps > 1) {
+                if (nsteps > 1) {
+                    acc = mfma_bf16(bop[nb][1], shi[1], acc);
+                    acc = mfma_bf16(bop[nb][1], slo[1], acc);
+                }
             }
             uint2 nv;
             nv.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
@@ -581,7 +590,7 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
-template <bool kSum = false>
+template <bool kSum = false, int kSteps = 2>
 __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
@@ -590,7 +599,7 @@ __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* 
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
     uint16_t* sLo = sHi + 16 * kSLds;
     for (int r0 = 0; r0 < rs.n; r0 += 16)
-        expand_wide_bf16<kSum>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
+        expand_wide_bf16<kSum, kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
                                sHi, sLo, sc);
 }
 

@@ -162,11 +162,14 @@ def test_disabled_adapters_leave_caches(ml):
 # with the oracle's single rounding; the activation is checked to the
 # tolerance and its device output is what the oracle's down stage reads, so
 # every later stage is compared bit for bit.  Cases: the narrow expand, the
-# wide (16 x 1024) expand with a ragged last tile, shared outer matrices
+# wide (16 x 1024) expand with a ragged last tile (rank 32: the one-step
+# build; rank 64: the two-step build of both expands), shared outer matrices
 # with a disabled adapter.
 INT_MOE_CASES = [
     ("narrow", lambda: W.integer_moe_case(1, M=90, H=264, I=64)),
     ("wide_ragged", lambda: W.integer_moe_case(2, M=70, H=136, I=4104, rank=32,
+                                               block_size_m=32)),
+    ("wide_rank64", lambda: W.integer_moe_case(4, M=60, H=136, I=4104, rank=64,
                                                block_size_m=32)),
     ("shared_outer_masked", lambda: W.integer_moe_case(3, M=50, H=264, I=136, shared_outer=True,
                                                        enabled=[1, 0, 1])),
