@@ -162,13 +162,16 @@ LinearWs linear_ws_layout(int M, int K, int cols) {
 
 MoeWs moe_ws_layout(int L, int mtp, int r, int Kmax) {
     MoeWs ws{};
+    // partials: fp32 values per K chunk of kKChunk (fp32 path), or 8-byte
+    // tagged exchange slots per K chunk of 1024 (bf16 path)
     const size_t C = (size_t)kchunks(Kmax);
+    const size_t C8 = (size_t)(Kmax + 1023) / 1024;
     const size_t rows = (size_t)L * mtp;
     size_t off = 0;
     ws.header = off;
     off += up(sizeof(WsHeader));
     ws.partial = off;
-    off += up(C * rows * r * sizeof(float));
+    off += up(std::max(C * sizeof(float), C8 * sizeof(uint64_t)) * rows * r);
     ws.S = off;
     off += up(rows * r * sizeof(float));
     ws.total = off;

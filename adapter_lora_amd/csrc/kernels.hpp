@@ -165,7 +165,7 @@ struct MoeArgs {
 
 struct MoeWs {
     size_t header;
-    size_t partial;     // float[C][L*max_tokens_padded][r]
+    size_t partial;     // fp32 [C][L*max_tokens_padded][r], or (bf16) tagged slots [C1024][...][r]
     size_t S;           // float[L*max_tokens_padded][r]
     size_t total;
 };

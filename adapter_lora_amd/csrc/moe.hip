@@ -219,24 +219,24 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink(MoeArgs a, int whic
 }
 
 // bf16 shrink for sparse blocks: unit = (aligned block, K chunk of 1024, 16
-// S columns).  Wave w takes K values [256 w, 256 w + 256) of the chunk in 8
-// steps of v_mfma_f32_16x16x32_bf16 with 16 of the block's rows as the first
-// operand and the unit's 16 A rows (kept in registers for every row group)
-// as the second; the four waves' partials are added in LDS in a fixed order.
-// Only real rows are visited, 16 at a time, so a block of ~16 real rows costs
-// one MFMA chain per wave instead of a 64-row tile.
+// S columns).  With kNW waves, wave w takes K values [w 1024 / kNW, (w + 1)
+// 1024 / kNW) of the chunk in 32 / kNW steps of v_mfma_f32_16x16x32_bf16,
+// with 16 of the block's rows as the first operand and the unit's 16 A rows
+// (kept in registers for every row group) as the second; the waves'
+// partials are added in LDS in a fixed order.  Only real rows are visited,
+// 16 at a time, so a block of ~16 real rows costs one MFMA chain per wave
+// instead of a 64-row tile.  The partial goes to P (float) or, with a
+// nonzero tag, into P's tagged exchange slot for the expand units of the
+// same launch.  red: kNW * 256 floats of LDS.
 constexpr int kNarrowK = 1024;
 
-__global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, int which,
-                                                                     const uint16_t* __restrict__ in,
-                                                                     int64_t ld_in,
-                                                                     float* __restrict__ P, int C,
-                                                                     int G, int K, int units) {
-    __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
-    __shared__ int s_wlast[kTileWaves];
-    __shared__ float red[kTileWaves * 16 * 16];
-    const int unit = (int)blockIdx.x;
-    if (unit >= units) return;
+template <int kNW>
+__device__ __forceinline__ void moe_shrink_unit(const MoeArgs& a, int which,
+                                                const uint16_t* __restrict__ in, int64_t ld_in,
+                                                float* __restrict__ P, int C, int G, int K,
+                                                int unit, int* s_in, int* s_out, int* s_wlast,
+                                                float* red, uint32_t tag) {
+    constexpr int kNS = 32 / kNW;                 // MFMA steps per wave
     const int blk = unit / (C * G);
     const int c = (unit / G) % C;
     const int cb = unit % G;
@@ -249,33 +249,44 @@ __global__ __launch_bounds__(kTileThreads) void k_moe_shrink_narrow(MoeArgs a, i
     const int64_t ew = moe_slot(a, which == 0, l, mu.e);
     const uint16_t* A = reinterpret_cast<const uint16_t*>(which == 0 ? a.A_gu : a.A_d) +
                         (ew * a.r + cb * 16 + lr) * K;
-    const int kw = c * kNarrowK + wave * 256 + lq * 8;     // this lane's first K value
-    uint4 av[8];
+    const int kw = c * kNarrowK + wave * (32 * kNS) + lq * 8;   // this lane's first K value
+    uint4 av[kNS];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < K, A);
-    float* Pc = P + (int64_t)c * a.L * a.max_tokens_padded * a.r;
+    for (int kk = 0; kk < kNS; ++kk) av[kk] = ld16_if(A + kw + kk * 32, kw + kk * 32 < K, A);
+    const int64_t cs = (int64_t)a.L * a.max_tokens_padded * a.r;
     for (int r0 = 0; r0 < mu.n; r0 += 16) {
         const int i = r0 + lr;
         const int xr = i < mu.n ? s_in[i] : -1;
         const uint16_t* xp = in + (int64_t)(xr < 0 ? 0 : xr) * ld_in;
-        uint4 xv[8];
+        uint4 xv[kNS];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
+        for (int kk = 0; kk < kNS; ++kk)
             xv[kk] = ld16_if(xp + kw + kk * 32, xr >= 0 && kw + kk * 32 < K, in);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) acc = mfma_bf16(xv[kk], av[kk], acc);
+        for (int kk = 0; kk < kNS; ++kk) acc = mfma_bf16(xv[kk], av[kk], acc);
         // acc[q]: block row r0 + 4 lq + q, S column cb*16 + lr
 #pragma unroll
         for (int q = 0; q < 4; ++q) red[(wave * 16 + lq * 4 + q) * 16 + lr] = acc[q];
         __syncthreads();
-        {
+        if (threadIdx.x < 256) {
             const int row = threadIdx.x / 16, col = threadIdx.x % 16;
             const int orow = r0 + row < mu.n ? s_out[r0 + row] : -1;
-            if (orow >= 0)
-                Pc[(int64_t)orow * a.r + cb * 16 + col] =
-                    (red[(0 * 16 + row) * 16 + col] + red[(1 * 16 + row) * 16 + col]) +
-                    (red[(2 * 16 + row) * 16 + col] + red[(3 * 16 + row) * 16 + col]);
+            if (orow >= 0) {
+                float sum[kNW];
+#pragma unroll
+                for (int w = 0; w < kNW; ++w) sum[w] = red[(w * 16 + row) * 16 + col];
+                // pairwise, in a fixed order
+#pragma unroll
+                for (int h = 1; h < kNW; h *= 2)
+#pragma unroll
+                    for (int w = 0; w + h < kNW; w += 2 * h) sum[w] += sum[w + h];
+                const int64_t at = (int64_t)c * cs + (int64_t)orow * a.r + cb * 16 + col;
+                if (tag != 0u)
+                    slot_put(reinterpret_cast<slot_t*>(P) + at, sum[0], tag);
+                else
+                    P[at] = sum[0];
+            }
         }
         __syncthreads();     // red is rewritten by the next row group
     }
@@ -316,49 +327,47 @@ __global__ void k_moe_reduce(const float* __restrict__ P, int C, int64_t cstride
     }
 }
 
-template <typename T, int kSteps>
-__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_moe_expand(MoeArgs a, int which,
+// fp32 expand: unit = (aligned block, 256 output columns), S from the reduce.
+template <typename T>
+__global__ __launch_bounds__(kTileThreads) void k_moe_expand(MoeArgs a, int which,
                                                               const float* __restrict__ S,
                                                               T* __restrict__ out, int64_t ld_out,
-                                                              int N, int n_groups, int tpw,
-                                                              int units, SChunks sc) {
+                                                              int N, int n_groups, int units) {
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
+    __shared__ int s_wlast[kTileWaves];
     const int unit = (int)blockIdx.x;
     if (unit >= units) return;
     const int blk = unit / n_groups;
     const int g = unit % n_groups;
     const int l = blk % a.L, b = blk / a.L;
-    __shared__ int s_wlast[kTileWaves];
     const MoeUnit mu = moe_unit(a, which, false, l, b, s_in, s_out, s_wlast);
     if (!mu.ok) return;
     const int64_t ew = moe_slot(a, which == 1, l, mu.e);
     const T* B = reinterpret_cast<const T*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
-    const int n_begin = g * tpw * kNTile;
-    const int n_end = min(N, n_begin + tpw * kNTile);
-    if constexpr (sizeof(T) == 2) {
-        // bf16: S arrives as the shrink's K-chunk partials, summed while staged
-        __shared__ uint4 lds[kExpandLds / 16];
-        expand_rows_bf16<true, kSteps>(rs, S, a.r, 0, reinterpret_cast<const uint16_t*>(B), a.r, n_begin,
-                               n_end, reinterpret_cast<uint16_t*>(out), ld_out, lds, sc);
-    } else {
-        for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
-            expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out);
-    }
+    const int n0 = g * kNTile;
+    expand_tile_simple<T>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out);
 }
 
-// bf16 expand over wide tiles: unit = (aligned block, 1024 output columns).
-template <int kSteps>
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(kSteps == 1 ? 4 : 2))) void k_moe_expand_wide(MoeArgs a, int which,
-                                                                   const float* __restrict__ S,
-                                                                   uint16_t* __restrict__ out,
-                                                                   int64_t ld_out, int N,
-                                                                   int n_groups, int units,
-                                                                   SChunks sc) {
+template <int kSteps, bool kWide>
+__global__ __launch_bounds__(kWide ? kWideThreads : kTileThreads)
+__attribute__((amdgpu_waves_per_eu(kWide ? (kSteps == 1 ? 4 : 2) : 3))) void k_moe_delta(
+    MoeArgs a, int which, const uint16_t* __restrict__ in, int64_t ld_in, float* __restrict__ P,
+    int C, int G, int K, int nprod, uint16_t* __restrict__ out, int64_t ld_out, int N,
+    int n_groups, int units, int* err) {
+    constexpr int kThreads = kWide ? kWideThreads : kTileThreads;
+    constexpr int kNW = kThreads / kWave;
+    static_assert(kNW * 256 * 4 <= (kWide ? kWideLds : kExpandLds), "shrink scratch must fit");
     __shared__ int s_in[kMaxRowTile], s_out[kMaxRowTile];
-    __shared__ int s_wlast[kWideThreads / kWave];
-    __shared__ uint4 lds[kWideLds / 16];
-    const int unit = (int)blockIdx.x;
+    __shared__ int s_wlast[kNW];
+    __shared__ uint4 lds[(kWide ? kWideLds : kExpandLds) / 16];
+    const uint32_t tag = launch_tag();
+    if ((int)blockIdx.x < nprod) {
+        moe_shrink_unit<kNW>(a, which, in, ld_in, P, C, G, K, (int)blockIdx.x, s_in, s_out,
+                             s_wlast, reinterpret_cast<float*>(lds), tag);
+        return;
+    }
+    const int unit = (int)blockIdx.x - nprod;
     if (unit >= units) return;
     const int blk = unit / n_groups;
     const int g = unit % n_groups;
@@ -369,9 +378,37 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(kS
     const uint16_t* B =
         reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
-    const int n0 = g * kWideCols;
-    expand_rows_wide<true, kSteps>(rs, S, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out, ld_out, lds,
-                           sc);
+    const SChunks sc{C, (int64_t)a.L * a.max_tokens_padded * a.r, tag, err};
+    if constexpr (kWide) {
+        const int n0 = g * kWideCols;
+        expand_rows_wide<true, kSteps>(rs, P, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out,
+                                    ld_out, lds, sc);
+    } else {
+        const int n0 = g * kNTile;
+        expand_rows_bf16<true, kSteps>(rs, P, a.r, 0, B, a.r, n0, min(N, n0 + kNTile), out, ld_out,
+                                    lds, sc);
+    }
+}
+
+template <int kSteps>
+static void launch_moe_delta_bf16(const MoeArgs& a, int which, const uint16_t* in, int64_t ld_in,
+                                  float* P, int C, int G, int K, int nprod, uint16_t* out,
+                                  int64_t ld_out, int N, int nblk, int* err, hipStream_t st) {
+    // wide 16 x 1024 tiles when the output is wide enough that 64 x 256 tiles
+    // would need many rounds of mostly idle workgroups (the gate/up output)
+    if (N >= 2 * kWideCols * 4) {
+        const int wg = (N + kWideCols - 1) / kWideCols;
+        const int units = a.L * nblk * wg;
+        hipLaunchKernelGGL((k_moe_delta<kSteps, true>), dim3((unsigned)(nprod + units)),
+                           dim3(kWideThreads), 0, st, a, which, in, ld_in, P, C, G, K, nprod, out,
+                           ld_out, N, wg, units, err);
+    } else {
+        const int ng = (N + kNTile - 1) / kNTile;
+        const int units = a.L * nblk * ng;
+        hipLaunchKernelGGL((k_moe_delta<kSteps, false>), dim3((unsigned)(nprod + units)),
+                           dim3(kTileThreads), 0, st, a, which, in, ld_in, P, C, G, K, nprod, out,
+                           ld_out, N, ng, units, err);
+    }
 }
 
 template <typename T>
@@ -379,35 +416,36 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
                               void* out, int64_t ld_out, void* ws, hipStream_t st) {
     const int K = which == 0 ? a.H : a.I;
     const int N = which == 0 ? 2 * a.I : a.H;
-    const int C = sizeof(T) == 2 ? (K + kNarrowK - 1) / kNarrowK : kchunks(K);
     const int nblk = a.max_tokens_padded / a.block_size_m;
     const MoeWs W = moe_ws_layout(a.L, a.max_tokens_padded, a.r, a.H > a.I ? a.H : a.I);
     float* P = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.partial);
-    float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
     if constexpr (sizeof(T) == 2) {
+        // one launch; P holds the partials as tagged exchange slots (8 bytes each)
+        const int C = (K + kNarrowK - 1) / kNarrowK;
         const int G = a.r / 16;
-        const int units = a.L * nblk * C * G;
-        hipLaunchKernelGGL(k_moe_shrink_narrow, dim3((unsigned)(units > 0 ? units : 1)),
-                           dim3(kTileThreads), 0, st, a, which,
-                           reinterpret_cast<const uint16_t*>(in), ld_in, P, C, G, K, units);
+        const int nprod = a.L * nblk * C * G;
+        int* err = &reinterpret_cast<WsHeader*>(reinterpret_cast<char*>(ws) + W.header)->error;
+        const uint16_t* xin = reinterpret_cast<const uint16_t*>(in);
+        uint16_t* o = static_cast<uint16_t*>(out);
+        // rank <= 32: one 32-wide MFMA step, half the B operands in registers
+        if (a.r <= 32)
+            launch_moe_delta_bf16<1>(a, which, xin, ld_in, P, C, G, K, nprod, o, ld_out, N, nblk,
+                                     err, st);
+        else
+            launch_moe_delta_bf16<2>(a, which, xin, ld_in, P, C, G, K, nprod, o, ld_out, N, nblk,
+                                     err, st);
+        return hipGetLastError();
     } else {
+        // fp32: shrink into K-chunk partials, reduce into S, expand
+        const int C = kchunks(K);
+        float* S = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + W.S);
         const int units = a.L * nblk * C;
         hipLaunchKernelGGL((k_moe_shrink<T>), dim3((unsigned)(units > 0 ? units : 1)),
                            dim3(kTileThreads), 0, st, a, which, reinterpret_cast<const T*>(in),
                            ld_in, P, C, K, units);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
-    // bf16: the expand sums the partials of its own rows as it stages them (a
-    // workgroup reads 16 S columns x C chunks of its block's rows), which
-    // saves the reduce launch; fp32: a separate reduce into S
-    SChunks sc{1, 0};
-    const float* Sx = S;
-    if (sizeof(T) == 2) {
-        sc = SChunks{C, cstride};
-        Sx = P;
-    } else {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t cstride = (int64_t)a.L * a.max_tokens_padded * a.r;
         int rb = (a.max_tokens_padded * a.r / 4 + 255) / 256;
         if (rb < 1) rb = 1;
         hipLaunchKernelGGL(k_moe_reduce, dim3((unsigned)rb, (unsigned)a.L), dim3(256), 0, st, P, C,
@@ -415,39 +453,13 @@ static hipError_t moe_delta_t(const MoeArgs& a, int which, const void* in, int64
                            a.M * a.topk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        const int n_groups = (N + kNTile - 1) / kNTile;
+        const int units2 = a.L * nblk * n_groups;
+        hipLaunchKernelGGL((k_moe_expand<T>), dim3((unsigned)(units2 > 0 ? units2 : 1)),
+                           dim3(kTileThreads), 0, st, a, which, S, reinterpret_cast<T*>(out),
+                           ld_out, N, n_groups, units2);
+        return hipGetLastError();
     }
-    const int n_tiles = (N + kNTile - 1) / kNTile;
-    // one 256-column tile per workgroup: a workgroup walks its tiles one after
-    // another, so spreading them over more workgroups overlaps their latencies
-    const int tpw = 1;
-    const int n_groups = (n_tiles + tpw - 1) / tpw;
-    const int units2 = a.L * nblk * n_groups;
-    const unsigned g2 = (unsigned)(units2 > 0 ? units2 : 1);
-    // wide 16 x 1024 tiles when the output is wide enough that 64 x 256 tiles
-    // would need many rounds of mostly idle workgroups (the gate/up output)
-    // rank <= 32: one 32-wide MFMA step, half the B operands in registers
-    const bool one = a.r <= 32;
-    if (sizeof(T) == 2 && N >= 2 * kWideCols * 4) {
-        const int wg = (N + kWideCols - 1) / kWideCols;
-        const int wunits = a.L * nblk * wg;
-        const dim3 grid((unsigned)(wunits > 0 ? wunits : 1));
-        uint16_t* o = static_cast<uint16_t*>(out);
-        if (one)
-            hipLaunchKernelGGL(k_moe_expand_wide<1>, grid, dim3(kWideThreads), 0, st, a, which,
-                               Sx, o, ld_out, N, wg, wunits, sc);
-        else
-            hipLaunchKernelGGL(k_moe_expand_wide<2>, grid, dim3(kWideThreads), 0, st, a, which,
-                               Sx, o, ld_out, N, wg, wunits, sc);
-    } else {
-        T* o = reinterpret_cast<T*>(out);
-        if (one)
-            hipLaunchKernelGGL((k_moe_expand<T, 1>), dim3(g2), dim3(kTileThreads), 0, st, a,
-                               which, Sx, o, ld_out, N, n_groups, tpw, units2, sc);
-        else
-            hipLaunchKernelGGL((k_moe_expand<T, 2>), dim3(g2), dim3(kTileThreads), 0, st, a,
-                               which, Sx, o, ld_out, N, n_groups, tpw, units2, sc);
-    }
-    return hipGetLastError();
 }
 
 hipError_t launch_moe_delta(const MoeArgs& a, int which, const void* in, int64_t ld_in,

@@ -214,50 +214,75 @@ constexpr int kExpandLds = 64 * kYRowBytes + 2 * 64 * kSLds * 2;   // bytes
 __device__ __forceinline__ int ypos(int r, int q) { return r * (kYRowBytes / 16) + (q ^ (r & 15)); }
 
 // Partial sums of S handed to the expand instead of S itself: the S value
-// at an offset is the sum of `C` chunk partials `cs` floats apart, added in
-// chunk order (the order of the separate reduce kernel).
+// at an offset is the sum of `C` chunk partials `cs` slots apart, added in
+// chunk order, each a tagged exchange slot of the launch with tag `tag`.
 struct SChunks {
     int C;
     int64_t cs;
+    uint32_t tag;
+    int* err;         // sticky error word for a wait that runs out (may be null)
 };
 
-// One float4 of S as the sum of its chunk partials (zero when !ok); the
-// loads of up to kChunkBatch chunks are in flight together.
-constexpr int kChunkBatch = 4;
+// One float4 of S from tagged exchange slots: the sum of its C chunk
+// partials in chunk order, each chunk's four slots polled (kSlotBatch
+// chunks together) until they carry the launch's tag.  A wait that runs
+// out sets `timeout` and leaves the missing partials out.
+constexpr int kSlotBatch = 4;
 
-__device__ __forceinline__ float4 chunk_sum4(const float* p, SChunks sc, bool ok) {
-    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 acc = *reinterpret_cast<const float4*>(p);
-    for (int c0 = 1; c0 < sc.C; c0 += kChunkBatch) {
-        float4 v[kChunkBatch];
+__device__ __forceinline__ float4 slot_sum4(const slot_t* p, SChunks sc, bool ok, bool& timeout) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!ok) return acc;
+    for (int c0 = 0; c0 < sc.C; c0 += kSlotBatch) {
+        slot_t w[kSlotBatch][4];
+        for (int spin = 0;; ++spin) {
+            bool all = true;
 #pragma unroll
-        for (int q = 0; q < kChunkBatch; ++q)
-            v[q] = *reinterpret_cast<const float4*>(p + (int64_t)min(c0 + q, sc.C - 1) * sc.cs);
+            for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
-        for (int q = 0; q < kChunkBatch; ++q)
-            if (c0 + q < sc.C) {
-                acc.x += v[q].x; acc.y += v[q].y; acc.z += v[q].z; acc.w += v[q].w;
+                for (int e = 0; e < 4; ++e)
+                    w[q][e] = c0 + q < sc.C ? slot_load(p + (int64_t)(c0 + q) * sc.cs + e)
+                                            : ((slot_t)sc.tag << 32);
+#pragma unroll
+            for (int q = 0; q < kSlotBatch; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) all = all && slot_full(w[q][e], sc.tag);
+            if (all) break;
+            if (timeout || spin >= kMaxSpin) {
+                timeout = true;
+                break;
             }
+            __builtin_amdgcn_s_sleep(2);
+        }
+#pragma unroll
+        for (int q = 0; q < kSlotBatch; ++q) {
+            if (c0 + q >= sc.C) continue;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = slot_full(w[q][e], sc.tag) ? __uint_as_float((uint32_t)w[q][e]) : 0.f;
+            acc.x += v[0]; acc.y += v[1]; acc.z += v[2]; acc.w += v[3];
+        }
     }
     return acc;
 }
 
-// Stage `nrows` S rows (rank positions 0..rp-1 summed from their chunk
-// partials, zero past rp and for missing rows) into LDS as bf16 hi / lo
-// pairs.  The (row, float4) pairs below rp are dealt to the threads first,
-// one per thread and pass, so each thread's chunk loads are in flight
-// together; the positions past rp are then cleared.
-__device__ __forceinline__ void stage_s_chunks(const RowSet& rs, int r0, int rows, int nrows,
-                                               const float* __restrict__ S, int sld, int sc0,
-                                               SChunks sc, int rp, int nthreads,
-                                               uint16_t* __restrict__ sHi,
-                                               uint16_t* __restrict__ sLo) {
+// Stage `nrows` S rows into LDS as bf16 hi / lo pairs: rank positions
+// 0..rp-1 summed from their chunk partials in tagged exchange slots, zero
+// past rp and for missing rows.  The (row, float4) pairs below rp are dealt
+// to the threads, one per thread and pass, so each thread's slot loads are
+// in flight together; the positions past rp are then cleared.
+__device__ __forceinline__ void stage_s_slots(const RowSet& rs, int r0, int rows, int nrows,
+                                              const slot_t* __restrict__ S, int sld, int sc0,
+                                              SChunks sc, int rp, int nthreads,
+                                              uint16_t* __restrict__ sHi,
+                                              uint16_t* __restrict__ sLo) {
     const int wa = rp / 4;                        // float4 per row below rp
+    bool timeout = false;
     for (int i = (int)threadIdx.x; i < nrows * wa; i += nthreads) {
         const int row = i / wa, j = (i % wa) * 4;
         const int sr = row < rows ? rs.in_row[r0 + row] : -1;
         const float4 v4 =
-            chunk_sum4(S + (int64_t)(sr < 0 ? 0 : sr) * sld + sc0 + j, sc, sr >= 0);
+            slot_sum4(S + (int64_t)(sr < 0 ? 0 : sr) * sld + sc0 + j, sc, sr >= 0, timeout);
         const float v[4] = {v4.x, v4.y, v4.z, v4.w};
         uint32_t h[2], l[2];
 #pragma unroll
@@ -270,6 +295,7 @@ __device__ __forceinline__ void stage_s_chunks(const RowSet& rs, int r0, int row
         *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
         *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
     }
+    if (timeout && sc.err != nullptr) atomicOr(sc.err, kErrSpin);
     const int wz = LORA_MAX_RANK / 4 - wa;        // float4 per row past rp
     for (int i = (int)threadIdx.x; i < nrows * wz; i += nthreads) {
         const int row = i / wz, j = rp + (i % wz) * 4;
@@ -278,18 +304,19 @@ __device__ __forceinline__ void stage_s_chunks(const RowSet& rs, int r0, int row
     }
 }
 
-// kSum: S is given as chunk partials (SChunks), summed while staged.
+// kSlots: S arrives as chunk partials in tagged exchange slots written by
+// the same launch, polled until they carry its tag (stage_s_slots).
 // kSteps: 32-wide rank steps the code is built for; 1 needs rp <= 32 and
 // keeps half the B operands out of registers (the MoE launches, whose rank
 // is known at launch, pick it; the dense launches mix ranks up to 64).
-template <bool kSum = false, int kSteps = 2>
+template <bool kSlots = false, int kSteps = 2>
 __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0}) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -304,7 +331,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
     //    order; measured 0.1-0.5 us per launch on the dense workloads)
     const int srow = tid / 4, sqt = tid % 4;
     float4 sv_early[4];
-    if constexpr (!kSum) {
+    if constexpr (!kSlots) {
         const int sr = srow < rows ? rs.in_row[r0 + srow] : -1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -337,8 +364,9 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
             bop[nb][st] = ld16(B + (int64_t)min(n, n1 - 1) * rp + min(j, rp - 8));
         }
     }
-    if constexpr (kSum) {
-        stage_s_chunks(rs, r0, rows, 64, S, sld, sc0, sc, rp, kTileThreads, sHi, sLo);
+    if constexpr (kSlots) {
+        stage_s_slots(rs, r0, rows, 64, reinterpret_cast<const slot_t*>(S), sld, sc0, sc, rp,
+                      kTileThreads, sHi, sLo);
     } else {
         // 1c. S rows (loaded at step 0) split into hi / lo in LDS; positions
         //     past rp are written as zeros, so the MFMA operand reads below
@@ -436,17 +464,17 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs over columns [n_begin, n_end), one 64 x 256 tile at a time.
-template <bool kSum = false, int kSteps = 2>
+template <bool kSlots = false, int kSteps = 2>
 __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp,
                                                  int n_begin, int n_end,
                                                  uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds, SChunks sc = {1, 0}) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr}) {
     for (int r0 = 0; r0 < rs.n; r0 += 64) {
         const int rows = min(64, rs.n - r0);
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
-            expand_tile_bf16<kSum, kSteps>(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end),
+            expand_tile_bf16<kSlots, kSteps>(rs, r0, rows, S, sld, sc0, B, rp, n0, min(n0 + kNTile, n_end),
                                    y, ldy_, lds,
                                    reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16),
                                    reinterpret_cast<uint16_t*>(lds + 64 * kYRowBytes / 16) +
@@ -472,14 +500,14 @@ constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
 
-template <bool kSum = false, int kSteps = 2>
+template <bool kSlots = false, int kSteps = 2>
 __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int rows,
                                                  const float* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0}) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;                 // 0..7
@@ -518,8 +546,9 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
             }
         }
     }
-    if constexpr (kSum) {
-        stage_s_chunks(rs, r0, rows, 16, S, sld, sc0, sc, rp, kWideThreads, sHi, sLo);
+    if constexpr (kSlots) {
+        stage_s_slots(rs, r0, rows, 16, reinterpret_cast<const slot_t*>(S), sld, sc0, sc, rp,
+                      kWideThreads, sHi, sLo);
     } else {
         // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
         //     .. +4; positions past rp are written as zeros
@@ -590,16 +619,16 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
-template <bool kSum = false, int kSteps = 2>
+template <bool kSlots = false, int kSteps = 2>
 __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds, SChunks sc = {1, 0}) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr}) {
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
     uint16_t* sLo = sHi + 16 * kSLds;
     for (int r0 = 0; r0 < rs.n; r0 += 16)
-        expand_wide_bf16<kSum, kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
+        expand_wide_bf16<kSlots, kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
                                sHi, sLo, sc);
 }
 

@@ -480,7 +480,14 @@ lora_status lora_moe_align(const int32_t* topk_ids, const int32_t* ids,
                            int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* ntpp,
                            hipStream_t stream);
 
-/* Bytes of device workspace needed by the two MoE delta calls. */
+/*
+ * Bytes of device workspace needed by the two MoE delta calls.  As for
+ * lora_workspace_size: zero it once (lora_workspace_init) before its first
+ * use and order the calls that share it on one stream.  With bf16 weights a
+ * delta call is one launch whose expand workgroups wait (bounded) for the
+ * shrink workgroups' partials in the workspace; a wait that runs out sets
+ * LORA_DEVERR_WAIT in the workspace's error word (lora_read_device_error).
+ */
 size_t lora_moe_workspace_size(const lora_moe_weights_t* w, int32_t max_tokens_padded);
 
 /*

@@ -142,6 +142,7 @@ def test_moe_stages_and_chain(ml, name, mk):
                         case.B_d.values, case.shared_outer)
     r4 = O.topk_reduce(r3, case.topk_weights.astype(np.float64))
     assert_close(to_f64(out), r4, dt, None, "chain")
+    assert ml.lora_read_device_error(ws.buf) == 0
 
 
 def test_disabled_adapters_leave_caches(ml):
@@ -205,3 +206,4 @@ def test_moe_chain_integer_bit_exact(ml, name, mk):
     assert np.array_equal(got3, bf(r3)), "down"
     r4 = O.topk_reduce(got3, case.topk_weights.astype(np.float64))
     assert np.array_equal(to_f64(out), bf(r4)), "top-k reduce"
+    assert ml.lora_read_device_error(ws.buf) == 0
