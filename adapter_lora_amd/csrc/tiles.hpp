@@ -223,16 +223,15 @@ struct SChunks {
     int* err;         // sticky error word for a wait that runs out (may be null)
 };
 
-// One float4 of S from tagged exchange slots: the sum of its C chunk
-// partials in chunk order, each chunk's four slots polled (kSlotBatch
-// chunks together) until they carry the launch's tag.  A wait that runs
-// out sets `timeout` and leaves the missing partials out.
-constexpr int kSlotBatch = 4;
-
-__device__ __forceinline__ float4 slot_sum4(const slot_t* p, SChunks sc, bool ok, bool& timeout) {
+// Sum of chunks [c0, c1) of one float4 of S held in tagged exchange slots,
+// in chunk order; each chunk's four slots are polled (kSlotBatch chunks
+// together) until they carry the launch's tag.  A wait that runs out sets
+// `timeout` and leaves the missing partials out.
+template <int kSlotBatch>
+__device__ __forceinline__ float4 slot_range_sum(const slot_t* p, SChunks sc, int c0, int c1,
+                                                 bool& timeout) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!ok) return acc;
-    for (int c0 = 0; c0 < sc.C; c0 += kSlotBatch) {
+    for (int cb = c0; cb < c1; cb += kSlotBatch) {
         slot_t w[kSlotBatch][4];
         for (int spin = 0;; ++spin) {
             bool all = true;
@@ -240,8 +239,8 @@ __device__ __forceinline__ float4 slot_sum4(const slot_t* p, SChunks sc, bool ok
             for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[q][e] = c0 + q < sc.C ? slot_load(p + (int64_t)(c0 + q) * sc.cs + e)
-                                            : ((slot_t)sc.tag << 32);
+                    w[q][e] = cb + q < c1 ? slot_load(p + (int64_t)(cb + q) * sc.cs + e)
+                                          : ((slot_t)sc.tag << 32);
 #pragma unroll
             for (int q = 0; q < kSlotBatch; ++q)
 #pragma unroll
@@ -255,7 +254,7 @@ __device__ __forceinline__ float4 slot_sum4(const slot_t* p, SChunks sc, bool ok
         }
 #pragma unroll
         for (int q = 0; q < kSlotBatch; ++q) {
-            if (c0 + q >= sc.C) continue;
+            if (cb + q >= c1) continue;
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -268,22 +267,66 @@ __device__ __forceinline__ float4 slot_sum4(const slot_t* p, SChunks sc, bool ok
 
 // Stage `nrows` S rows into LDS as bf16 hi / lo pairs: rank positions
 // 0..rp-1 summed from their chunk partials in tagged exchange slots, zero
-// past rp and for missing rows.  The (row, float4) pairs below rp are dealt
-// to the threads, one per thread and pass, so each thread's slot loads are
-// in flight together; the positions past rp are then cleared.
-__device__ __forceinline__ void stage_s_slots(const RowSet& rs, int r0, int rows, int nrows,
+// past rp and for missing rows.  Called by every thread of the block; at
+// most 4 nthreads (row, float4) pairs (nrows * rp / 4).
+//
+// A poll is a round trip to the point where the workgroups of all XCDs
+// meet, so the chunks are split over the threads rather than walked by one:
+// with `items` (row, float4) pairs for the tile's rows, G = threads / items
+// groups of consecutive chunks (at least 1, at most C, and no more than the
+// scratch holds) are polled at once,
+// task (g, item) adding group g's chunks.  The task sums meet in LDS (sHi /
+// sLo serve as the scratch) and are added in group order.  The positions
+// past rp are then cleared.  kNRows rows, kThreads threads; a thread polls
+// kBatch chunks at a time (fewer registers for the wide tile).
+template <int kNRows, int kThreads, int kBatch>
+__device__ __forceinline__ void stage_s_slots(const RowSet& rs, int r0, int rows,
                                               const slot_t* __restrict__ S, int sld, int sc0,
-                                              SChunks sc, int rp, int nthreads,
-                                              uint16_t* __restrict__ sHi,
+                                              SChunks sc, int rp, uint16_t* __restrict__ sHi,
                                               uint16_t* __restrict__ sLo) {
+    constexpr int nrows = kNRows, nthreads = kThreads;
+    constexpr int kPer = (kNRows * LORA_MAX_RANK / 4 + kThreads - 1) / kThreads;  // items per thread
+    constexpr int kCap = kNRows * kSLds / 4;      // float4 that sHi and sLo hold together
+    static_assert(kNRows * LORA_MAX_RANK / 4 <= kCap, "one task per item must fit");
     const int wa = rp / 4;                        // float4 per row below rp
+    const int tid = (int)threadIdx.x;
+    const int items = rows * wa;
+    const int G = max(1, min(sc.C, min(nthreads, kCap) / max(items, 1)));
+    const int per = (sc.C + G - 1) / G;
+    float4* part = reinterpret_cast<float4*>(sHi);   // G * items <= kCap float4
     bool timeout = false;
-    for (int i = (int)threadIdx.x; i < nrows * wa; i += nthreads) {
+    for (int t = tid; t < G * items; t += nthreads) {
+        const int g = t / items, it = t % items;
+        const int row = it / wa, j = (it % wa) * 4;
+        const int sr = rs.in_row[r0 + row];
+        const int c0 = g * per, c1 = min(sc.C, c0 + per);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sr >= 0 && c0 < c1)
+            acc = slot_range_sum<kBatch>(S + (int64_t)sr * sld + sc0 + j, sc, c0, c1, timeout);
+        part[t] = acc;
+    }
+    if (timeout && sc.err != nullptr) atomicOr(sc.err, kErrSpin);
+    __syncthreads();
+    float4 sum[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * nthreads;
+        sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < items) {
+            sum[k] = part[i];
+            for (int g = 1; g < G; ++g) {
+                const float4 v = part[g * items + i];
+                sum[k].x += v.x; sum[k].y += v.y; sum[k].z += v.z; sum[k].w += v.w;
+            }
+        }
+    }
+    __syncthreads();                              // the scratch is overwritten below
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * nthreads;
+        if (i >= nrows * wa) break;
         const int row = i / wa, j = (i % wa) * 4;
-        const int sr = row < rows ? rs.in_row[r0 + row] : -1;
-        const float4 v4 =
-            slot_sum4(S + (int64_t)(sr < 0 ? 0 : sr) * sld + sc0 + j, sc, sr >= 0, timeout);
-        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        const float v[4] = {sum[k].x, sum[k].y, sum[k].z, sum[k].w};   // zero past `items`
         uint32_t h[2], l[2];
 #pragma unroll
         for (int q = 0; q < 4; q += 2) {
@@ -295,9 +338,8 @@ __device__ __forceinline__ void stage_s_slots(const RowSet& rs, int r0, int rows
         *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
         *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
     }
-    if (timeout && sc.err != nullptr) atomicOr(sc.err, kErrSpin);
     const int wz = LORA_MAX_RANK / 4 - wa;        // float4 per row past rp
-    for (int i = (int)threadIdx.x; i < nrows * wz; i += nthreads) {
+    for (int i = tid; i < nrows * wz; i += nthreads) {
         const int row = i / wz, j = rp + (i % wz) * 4;
         *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(0u, 0u);
         *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(0u, 0u);
@@ -365,8 +407,8 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
         }
     }
     if constexpr (kSlots) {
-        stage_s_slots(rs, r0, rows, 64, reinterpret_cast<const slot_t*>(S), sld, sc0, sc, rp,
-                      kTileThreads, sHi, sLo);
+        stage_s_slots<64, kTileThreads, 4>(rs, r0, rows, reinterpret_cast<const slot_t*>(S),
+                                           sld, sc0, sc, rp, sHi, sLo);
     } else {
         // 1c. S rows (loaded at step 0) split into hi / lo in LDS; positions
         //     past rp are written as zeros, so the MFMA operand reads below
@@ -547,8 +589,8 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
         }
     }
     if constexpr (kSlots) {
-        stage_s_slots(rs, r0, rows, 16, reinterpret_cast<const slot_t*>(S), sld, sc0, sc, rp,
-                      kWideThreads, sHi, sLo);
+        stage_s_slots<16, kWideThreads, 2>(rs, r0, rows, reinterpret_cast<const slot_t*>(S),
+                                           sld, sc0, sc, rp, sHi, sLo);
     } else {
         // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
         //     .. +4; positions past rp are written as zeros
