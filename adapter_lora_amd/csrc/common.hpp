@@ -276,4 +276,15 @@ __device__ __forceinline__ bool table_fault(int* err, bool bad) {
 }
 constexpr int kMaxSpin = 1 << 20;
 
+// Control of the bounded waits on exchange slots: a poll expects the
+// launch's tag XOR poll_xor, and a wait gives up after max_spin polls.  The
+// launches pass {0, kMaxSpin}, except in the checked library (MLORA_DEBUG)
+// run with MLORA_DEBUG_WAIT_FAULT=1 in the environment: then every poll
+// misses and gives up after 64 tries, which exercises the LORA_DEVERR_WAIT
+// path with kernels that still end normally.
+struct WaitCtl {
+    uint32_t poll_xor;
+    int max_spin;
+};
+
 }  // namespace mlora

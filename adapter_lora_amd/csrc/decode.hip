@@ -23,7 +23,7 @@
 //              cross-lane reduction is needed on this side.
 // Consumers only wait on producers, which never wait, and producers have the
 // lower workgroup ids, so they are dispatched first; every wait is also
-// bounded (kMaxSpin) and reports a device error instead of hanging.
+// bounded (kMaxSpin polls) and reports a device error instead of hanging.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "wave_groups.hpp"
@@ -56,6 +56,7 @@ struct DecodeParams {
     int by_slot;             // ids mode with L <= M: producers numbered over the used slots
     const int32_t* tokens;   // non-null: embedding lookup, S rows read from the
                              // transposed A table by token id (a.K = vocab); no producers
+    WaitCtl wc;              // the consumers' bounded waits
 };
 
 // ---------------------------------------------------------------- shared view
@@ -483,6 +484,7 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
     float* sS = reinterpret_cast<float*>(lds);
     const int64_t cstride = (int64_t)LORA_DECODE_MAX_M * p.a.cols;
     bool ok = true;
+    const uint32_t want = tag ^ p.wc.poll_xor;
     for (int e = threadIdx.x; e < v.ms * rp; e += kDecThreads) {
         const int t = e / rp, j = e % rp;
         const slot_t* sp = slot_at(p, 0, v.p0 + t, sl * p.a.r_max + j);
@@ -493,11 +495,11 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
                 bool all = true;
 #pragma unroll
                 for (int q = 0; q < kPollBatch; ++q)
-                    w[q] = c0 + q < p.C ? slot_load(sp + (c0 + q) * cstride) : ((slot_t)tag << 32);
+                    w[q] = c0 + q < p.C ? slot_load(sp + (c0 + q) * cstride) : ((slot_t)want << 32);
 #pragma unroll
-                for (int q = 0; q < kPollBatch; ++q) all = all && slot_full(w[q], tag);
+                for (int q = 0; q < kPollBatch; ++q) all = all && slot_full(w[q], want);
                 if (all) break;
-                if (!ok || spin >= kMaxSpin) {
+                if (!ok || spin >= p.wc.max_spin) {
                     ok = false;
                     break;
                 }
@@ -505,7 +507,7 @@ __device__ __forceinline__ bool collect_S(const DecodeParams& p, const SegView& 
             }
 #pragma unroll
             for (int q = 0; q < kPollBatch; ++q)
-                if (c0 + q < p.C && slot_full(w[q], tag)) acc += __uint_as_float((uint32_t)w[q]);
+                if (c0 + q < p.C && slot_full(w[q], want)) acc += __uint_as_float((uint32_t)w[q]);
         }
         if constexpr (sizeof(T) == 2) {
             const uint32_t h = f32_to_bf16(acc);
@@ -856,6 +858,7 @@ hipError_t launch_embedding_decode(const LinearArgs& a, const int32_t* ids,
                                    const int32_t* enabled, const int32_t* tokens,
                                    const SegOut& out, void* y, int64_t ldy, hipStream_t st) {
     DecodeParams p{};
+    p.wc = wait_ctl();
     p.a = a;
     p.y = y;
     p.ldy = ldy;
@@ -882,6 +885,7 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
                                const SegOut& out, const void* x, int64_t ldx, void* y,
                                int64_t ldy, void* ws, int32_t* err, hipStream_t st) {
     DecodeParams p{};
+    p.wc = wait_ctl();
     p.a = a;
     p.ids = ids;
     p.enabled = ids ? enabled : nullptr;

@@ -7,8 +7,24 @@
 #include <stdint.h>
 
 #include "../../include/mlora.h"
+#include "common.hpp"
+#include <cstdlib>
 
 namespace mlora {
+
+// The wait control the launches pass (see WaitCtl): the checked library
+// reads MLORA_DEBUG_WAIT_FAULT once.
+inline WaitCtl wait_ctl() {
+#ifdef MLORA_DEBUG
+    static const bool fault = [] {
+        const char* e = std::getenv("MLORA_DEBUG_WAIT_FAULT");
+        return e != nullptr && e[0] == '1';
+    }();
+    if (fault) return WaitCtl{0x80000000u, 64};
+#endif
+    return WaitCtl{0u, kMaxSpin};
+}
+
 
 // Dense multi-LoRA call description (validated by api.cpp).
 struct LinearArgs {

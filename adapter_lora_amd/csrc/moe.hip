@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWide ? kWideThreads : kTileThreads)
 __attribute__((amdgpu_waves_per_eu(kWide ? (kSteps == 1 ? 4 : 2) : 3))) void k_moe_delta(
     MoeArgs a, int which, const uint16_t* __restrict__ in, int64_t ld_in, float* __restrict__ P,
     int C, int G, int K, int nprod, uint16_t* __restrict__ out, int64_t ld_out, int N,
-    int n_groups, int units, int* err) {
+    int n_groups, int units, int* err, WaitCtl wc) {
     constexpr int kThreads = kWide ? kWideThreads : kTileThreads;
     constexpr int kNW = kThreads / kWave;
     static_assert(kNW * 256 * 4 <= (kWide ? kWideLds : kExpandLds), "shrink scratch must fit");
@@ -378,7 +378,8 @@ __attribute__((amdgpu_waves_per_eu(kWide ? (kSteps == 1 ? 4 : 2) : 3))) void k_m
     const uint16_t* B =
         reinterpret_cast<const uint16_t*>(which == 0 ? a.B_gu : a.B_d) + ew * (int64_t)N * a.r;
     const RowSet rs{mu.n, a.block_size_m, s_in, s_out};
-    const SChunks sc{C, (int64_t)a.L * a.max_tokens_padded * a.r, tag, err};
+    const SChunks sc{C, (int64_t)a.L * a.max_tokens_padded * a.r, tag ^ wc.poll_xor, err,
+                     wc.max_spin};
     if constexpr (kWide) {
         const int n0 = g * kWideCols;
         expand_rows_wide<true, kSteps>(rs, P, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out,
@@ -401,13 +402,13 @@ static void launch_moe_delta_bf16(const MoeArgs& a, int which, const uint16_t* i
         const int units = a.L * nblk * wg;
         hipLaunchKernelGGL((k_moe_delta<kSteps, true>), dim3((unsigned)(nprod + units)),
                            dim3(kWideThreads), 0, st, a, which, in, ld_in, P, C, G, K, nprod, out,
-                           ld_out, N, wg, units, err);
+                           ld_out, N, wg, units, err, wait_ctl());
     } else {
         const int ng = (N + kNTile - 1) / kNTile;
         const int units = a.L * nblk * ng;
         hipLaunchKernelGGL((k_moe_delta<kSteps, false>), dim3((unsigned)(nprod + units)),
                            dim3(kTileThreads), 0, st, a, which, in, ld_in, P, C, G, K, nprod, out,
-                           ld_out, N, ng, units, err);
+                           ld_out, N, ng, units, err, wait_ctl());
     }
 }
 

@@ -219,8 +219,9 @@ __device__ __forceinline__ int ypos(int r, int q) { return r * (kYRowBytes / 16)
 struct SChunks {
     int C;
     int64_t cs;
-    uint32_t tag;
+    uint32_t tag;     // what a full slot carries (the launch's tag, XOR the wait control's)
     int* err;         // sticky error word for a wait that runs out (may be null)
+    int max_spin;     // polls before a wait gives up
 };
 
 // Sum of chunks [c0, c1) of one float4 of S held in tagged exchange slots,
@@ -246,7 +247,7 @@ __device__ __forceinline__ float4 slot_range_sum(const slot_t* p, SChunks sc, in
 #pragma unroll
                 for (int e = 0; e < 4; ++e) all = all && slot_full(w[q][e], sc.tag);
             if (all) break;
-            if (timeout || spin >= kMaxSpin) {
+            if (timeout || spin >= sc.max_spin) {
                 timeout = true;
                 break;
             }
@@ -358,7 +359,7 @@ __device__ __forceinline__ void expand_tile_bf16(const RowSet& rs, int r0, int r
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr}) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr, kMaxSpin}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -521,7 +522,7 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
                                                  const uint16_t* __restrict__ B, int rp,
                                                  int n_begin, int n_end,
                                                  uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr}) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr, kMaxSpin}) {
     for (int r0 = 0; r0 < rs.n; r0 += 64) {
         const int rows = min(64, rs.n - r0);
         for (int n0 = n_begin; n0 < n_end; n0 += kNTile)
@@ -558,7 +559,7 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
                                                  uint16_t* __restrict__ sHi,
-                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr}) {
+                                                 uint16_t* __restrict__ sLo, SChunks sc = {1, 0, 0u, nullptr, kMaxSpin}) {
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;                 // 0..7
@@ -675,7 +676,7 @@ __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* 
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
-                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr}) {
+                                                 uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr, kMaxSpin}) {
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
     uint16_t* sLo = sHi + 16 * kSLds;
     for (int r0 = 0; r0 < rs.n; r0 += 16)
