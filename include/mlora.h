@@ -153,7 +153,11 @@ lora_status lora_workspace_init(void* workspace, size_t bytes, hipStream_t strea
  * `stream`.  *out receives 0 when no kernel reported an error, else an OR of
  *   LORA_DEVERR_WAIT    a kernel gave up waiting on data from another
  *                       workgroup; the results of that call are not valid
- *                       (the workspace itself stays usable);
+ *                       (the workspace itself stays usable).  A library
+ *                       built with MLORA_DEBUG and run with
+ *                       MLORA_DEBUG_WAIT_FAULT=1 in the environment makes
+ *                       every such wait give up after a few polls, to test
+ *                       this path;
  *   LORA_DEVERR_BAD_ID  lora_fused_decode met a token id outside [-1, L); the
  *                       token was treated as one without an adapter.  An id
  *                       past the table would index a slot that does not
