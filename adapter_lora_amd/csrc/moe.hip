@@ -382,7 +382,7 @@ __attribute__((amdgpu_waves_per_eu(kWide ? (kSteps == 1 ? 4 : 2) : 3))) void k_m
                      wc.max_spin};
     if constexpr (kWide) {
         const int n0 = g * kWideCols;
-        expand_rows_wide<true, kSteps>(rs, P, a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out,
+        expand_rows_wide<kSteps>(rs, reinterpret_cast<const slot_t*>(P), a.r, 0, B, a.r, n0, min(N, n0 + kWideCols), out,
                                     ld_out, lds, sc);
     } else {
         const int n0 = g * kNTile;

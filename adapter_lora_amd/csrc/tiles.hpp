@@ -552,9 +552,9 @@ constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
 
-template <bool kSlots = false, int kSteps = 2>
+template <int kSteps>
 __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int rows,
-                                                 const float* __restrict__ S, int sld, int sc0,
+                                                 const slot_t* __restrict__ S, int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ ytile,
@@ -598,29 +598,8 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
             }
         }
     }
-    if constexpr (kSlots) {
-        stage_s_slots<16, kWideThreads, 2>(rs, r0, rows, reinterpret_cast<const slot_t*>(S),
-                                           sld, sc0, sc, rp, sHi, sLo);
-    } else {
-        // 1c. S rows: thread t < 256 covers row t / 16, rank positions 4 (t % 16)
-        //     .. +4; positions past rp are written as zeros
-        if (tid < 256) {
-            const int row = tid / 16, j = (tid % 16) * 4;
-            const int sr = row < rows ? rs.in_row[r0 + row] : -1;
-            const float4 v4 = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
-            const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-            uint32_t h[2], l[2];
-#pragma unroll
-            for (int q = 0; q < 4; q += 2) {
-                const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
-                h[q / 2] = h0 | (h1 << 16);
-                l[q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
-                           (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
-            }
-            *reinterpret_cast<uint2*>(sHi + row * kSLds + j) = make_uint2(h[0], h[1]);
-            *reinterpret_cast<uint2*>(sLo + row * kSLds + j) = make_uint2(l[0], l[1]);
-        }
-    }
+    // 1c. S rows summed from the shrink part's tagged slots
+    stage_s_slots<16, kWideThreads, 2>(rs, r0, rows, S, sld, sc0, sc, rp, sHi, sLo);
     __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
     __syncthreads();
     // 2. MFMA: the one 16-row group; each 16 x 16 result is added into the tile
@@ -671,8 +650,8 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
 }
 
 // All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
-template <bool kSlots = false, int kSteps = 2>
-__device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* __restrict__ S,
+template <int kSteps>
+__device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const slot_t* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
@@ -680,7 +659,7 @@ __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const float* 
     uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
     uint16_t* sLo = sHi + 16 * kSLds;
     for (int r0 = 0; r0 < rs.n; r0 += 16)
-        expand_wide_bf16<kSlots, kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
+        expand_wide_bf16<kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
                                sHi, sLo, sc);
 }
 
