@@ -505,15 +505,19 @@ __global__ void k_silu_mul_f32(const float* __restrict__ c1, int64_t ld1, float*
 
 hipError_t launch_silu_and_mul(int dtype, const void* c1, int64_t ld1, void* c2, int64_t ld2,
                                int P, int I, hipStream_t st) {
+    // bf16: one 16-byte piece per thread, 512-thread workgroups (9.2 against
+    // 9.5 us with 256 for the 512 x 14336 activation; more pieces per thread
+    // and non-temporal loads were slower)
+    const int threads = dtype == LORA_BF16 ? 512 : 256;
     const int64_t work = dtype == LORA_BF16 ? (int64_t)P * I / 8 : (int64_t)P * I;
-    int64_t blocks = (work + 255) / 256;
+    int64_t blocks = (work + threads - 1) / threads;
     if (blocks > 16384) blocks = 16384;
     if (blocks < 1) blocks = 1;
     if (dtype == LORA_BF16)
-        hipLaunchKernelGGL(k_silu_mul_bf16, dim3((unsigned)blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_silu_mul_bf16, dim3((unsigned)blocks), dim3(threads), 0, st,
                            (const uint16_t*)c1, ld1, (uint16_t*)c2, ld2, P, I);
     else
-        hipLaunchKernelGGL(k_silu_mul_f32, dim3((unsigned)blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_silu_mul_f32, dim3((unsigned)blocks), dim3(threads), 0, st,
                            (const float*)c1, ld1, (float*)c2, ld2, P, I);
     return hipGetLastError();
 }
