@@ -538,17 +538,19 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
 // ---------------------------------------------------------------------------
 // plain vector-ALU versions (any storage type); used for fp32 storage
 // ---------------------------------------------------------------------------
-// Wide expand tile for sparse row blocks (MoE): 16 rows x 1024 columns, 512
-// threads.  Wave w owns columns n0 + 128w .. +128 as 8 blocks of 16.  The
-// same three phases as the 64 x 256 tile (y tile straight into LDS, MFMA
-// results folded into it, row-major write-back), but a unit with few rows
-// carries four times the columns, so an MoE block of about 16 real rows
-// needs a quarter of the workgroups.
+// Wide expand tile for sparse row blocks (MoE): up to 32 rows (two groups of
+// 16) x 1024 columns, 512 threads.  Wave w owns columns n0 + 128w .. +128 as
+// 8 blocks of 16.  The same three phases as the 64 x 256 tile (y tile
+// straight into LDS, MFMA results folded into it, row-major write-back), but
+// a unit with few rows carries four times the columns, so an MoE block of
+// about 16 real rows needs a quarter of the workgroups; a block of 17-32
+// rows is one pass (its y rows, S rows and B operands loaded once).
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 512;
 constexpr int kWideCols = 1024;
+constexpr int kWideRows = 32;                                       // rows per pass (2 groups of 16)
 constexpr int kWideRowChunks = kWideCols / 8;                       // 128 chunks of 16 bytes
-constexpr int kWideLds = 16 * kWideCols * 2 + 2 * 16 * kSLds * 2;   // bytes
+constexpr int kWideLds = kWideRows * kWideCols * 2 + 2 * kWideRows * kSLds * 2;   // bytes
 
 __device__ __forceinline__ int wpos(int r, int q) { return r * kWideRowChunks + (q ^ r); }
 
@@ -568,14 +570,16 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
     const int nsteps = kSteps == 1 ? 1 : (rp + 31) / 32;
     const int nw = n0 + wave * 128;
     const int nchunks = (n1 - n0) / 8;            // valid 16-byte chunks per row
-    // 1a. y rows -> LDS: 32 wave instructions of 1 KB (half a row); position
-    //     p of row r holds chunk p ^ r
+    // 1a. y rows -> LDS: one wave instruction per half row (1 KB), rows past
+    //     `rows` skipped; position p of row r holds chunk p ^ r
+    constexpr int kHalves = kWideRows * 2 / (kWideThreads / kWave);   // per wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int k = wave * 4 + i;
+    for (int i = 0; i < kHalves; ++i) {
+        const int k = wave * kHalves + i;
         const int r = k / 2, h = k % 2;
+        if (r >= rows) break;                     // wave-uniform
         const int q = (h * 64 + lane) ^ r;
-        const int yr = r < rows ? rs.out_row[r0 + r] : -1;
+        const int yr = rs.out_row[r0 + r];
         const bool ok = yr >= 0 && q < nchunks;
         const uint16_t* src = ok ? y + (int64_t)yr * ldy_ + n0 + q * 8 : y;
         __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(ytile + r * kWideRowChunks + h * 64), 16, 0,
@@ -599,26 +603,30 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
         }
     }
     // 1c. S rows summed from the shrink part's tagged slots
-    stage_s_slots<16, kWideThreads, 2>(rs, r0, rows, S, sld, sc0, sc, rp, sHi, sLo);
+    stage_s_slots<kWideRows, kWideThreads, 2>(rs, r0, rows, S, sld, sc0, sc, rp, sHi, sLo);
     __builtin_amdgcn_s_waitcnt(0);    // direct-to-LDS loads are tracked by vmcnt only
     __syncthreads();
-    // 2. MFMA: the one 16-row group; each 16 x 16 result is added into the tile
-    if (nw < n1) {
+    // 2. MFMA, one 16-row group after the other; each 16 x 16 result is
+    //    added into the tile
+#pragma unroll 1
+    for (int rg = 0; rg < kWideRows / 16; ++rg) {
+        if (rg * 16 >= rows || nw >= n1) break;
+        const int row = rg * 16 + lr;
         uint4 shi[kSteps], slo[kSteps];
-        shi[0] = ld16(sHi + lr * kSLds + lq * 8);
-        slo[0] = ld16(sLo + lr * kSLds + lq * 8);
+        shi[0] = ld16(sHi + row * kSLds + lq * 8);
+        slo[0] = ld16(sLo + row * kSLds + lq * 8);
         if constexpr (kSteps > 1) {
             shi[1] = slo[1] = make_uint4(0, 0, 0, 0);
             if (nsteps > 1) {
-                shi[1] = ld16(sHi + lr * kSLds + 32 + lq * 8);
-                slo[1] = ld16(sLo + lr * kSLds + 32 + lq * 8);
+                shi[1] = ld16(sHi + row * kSLds + 32 + lq * 8);
+                slo[1] = ld16(sLo + row * kSLds + 32 + lq * 8);
             }
         }
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-            // acc[e]: column c + e of row lr, where c = 128 wave + 16 nb + 4 lq
+            // acc[e]: column c + e of row `row`, where c = 128 wave + 16 nb + 4 lq
             const int c = wave * 128 + nb * 16 + lq * 4;
-            uint2* yp = reinterpret_cast<uint2*>(ytile + wpos(lr, c / 8)) + ((c / 4) & 1);
+            uint2* yp = reinterpret_cast<uint2*>(ytile + wpos(row, c / 8)) + ((c / 4) & 1);
             const uint2 old = *yp;
             f32x4_t acc = {__uint_as_float(old.x << 16), __uint_as_float(old.x & 0xffff0000u),
                            __uint_as_float(old.y << 16), __uint_as_float(old.y & 0xffff0000u)};
@@ -638,8 +646,8 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
     }
     __syncthreads();
     // 3. row-major write-back: a wave instruction stores 64 chunks of one row
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+#pragma unroll 2
+    for (int i = 0; i < kWideRows * kWideRowChunks / kWideThreads; ++i) {
         const int idx = i * kWideThreads + tid;
         const int r = idx / kWideRowChunks, q = idx % kWideRowChunks;
         const int yr = r < rows ? rs.out_row[r0 + r] : -1;
@@ -649,18 +657,18 @@ __device__ __forceinline__ void expand_wide_bf16(const RowSet& rs, int r0, int r
     __syncthreads();     // the LDS tile is reused by the next row group
 }
 
-// All rows of rs (16 at a time) over columns [n0, min(n0 + 1024, n_end)).
+// All rows of rs (kWideRows at a time) over columns [n0, min(n0 + 1024, n_end)).
 template <int kSteps>
 __device__ __forceinline__ void expand_rows_wide(const RowSet& rs, const slot_t* __restrict__ S,
                                                  int sld, int sc0,
                                                  const uint16_t* __restrict__ B, int rp, int n0,
                                                  int n1, uint16_t* __restrict__ y, int64_t ldy_,
                                                  uint4* __restrict__ lds, SChunks sc = {1, 0, 0u, nullptr, kMaxSpin}) {
-    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 16 * kWideRowChunks);
-    uint16_t* sLo = sHi + 16 * kSLds;
-    for (int r0 = 0; r0 < rs.n; r0 += 16)
-        expand_wide_bf16<kSteps>(rs, r0, min(16, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y, ldy_, lds,
-                               sHi, sLo, sc);
+    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + kWideRows * kWideRowChunks);
+    uint16_t* sLo = sHi + kWideRows * kSLds;
+    for (int r0 = 0; r0 < rs.n; r0 += kWideRows)
+        expand_wide_bf16<kSteps>(rs, r0, min(kWideRows, rs.n - r0), S, sld, sc0, B, rp, n0, n1, y,
+                                 ldy_, lds, sHi, sLo, sc);
 }
 
 // ---------------------------------------------------------------------------

@@ -80,6 +80,10 @@ MOE_CASES = [
     # 32 rows with up to 2 row groups of 16
     ("wide_ragged_bf16", lambda: W.moe_case(7, M=150, H=264, I=4104, E=3, topk=2, L=2, rank=64,
                                             block_size_m=32)),
+    # full 64-row blocks (two experts, one adapter): the wide expand's blocks
+    # take two passes of 32 rows, the 64 x 256 tiles all their rows
+    ("wide_full_blocks", lambda: W.moe_case(10, M=160, H=264, I=4104, E=2, topk=2, L=1, rank=16,
+                                            block_size_m=64)),
     # experts_shared_outer_loras: gate_up A and down B with one expert slot
     ("cfg5_shared_outer", lambda: W.moe_case(0, shared_outer=True)),
     ("shared_outer_fp32", lambda: W.moe_case(8, M=40, H=128, I=96, E=4, topk=2, L=3, rank=16,
@@ -172,6 +176,8 @@ INT_MOE_CASES = [
                                                block_size_m=32)),
     ("wide_rank64", lambda: W.integer_moe_case(4, M=60, H=136, I=4104, rank=64,
                                                block_size_m=32)),
+    ("wide_full_blocks", lambda: W.integer_moe_case(5, M=120, H=136, I=4104, E=2, L=1,
+                                                    block_size_m=64, p_none=0.0)),
     ("shared_outer_masked", lambda: W.integer_moe_case(3, M=50, H=264, I=136, shared_outer=True,
                                                        enabled=[1, 0, 1])),
 ]
