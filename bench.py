@@ -606,7 +606,7 @@ def cpu_baseline_moe(case, seconds, tokens=32):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import workloads as W

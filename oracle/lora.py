@@ -22,7 +22,7 @@ Sources (the pages, by title and section):
   * SGLang "LoRA + MoE" page, CUDA-graph section: an adapter_enabled mask
     switches adapters off without changing the captured shapes.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * segment order: ascending adapter id; stable inside a segment;
   * -1 tokens are placed after every segment and belong to none;
   * adapters without tokens get no segment; buffer tails are filled

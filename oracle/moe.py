@@ -16,7 +16,7 @@ Source: SGLang "LoRA + MoE" page —
   * design rationale: adding the delta before the nonlinearity keeps
     (W + BA) x equivalence.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
   * a (token, expert) pair is flattened as f = m*topk + k (row f of cache1 /
     cache2 / cache3);
   * inside an adapter's list: experts ascending, pairs ascending; each

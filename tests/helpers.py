@@ -8,7 +8,7 @@ import torch
 
 import workloads as W
 
-# the benchmark spec gates
+# parity gates: normwise error against the largest oracle value
 TOL_BF16 = 2e-2          # max|y - y_or| <= 2e-2 * max|y_or|
 TOL_F32 = 1e-4           # max|y - y_or| <= 1e-4 * max|y_or|
 
@@ -37,7 +37,7 @@ def table_for(case: W.LinearCase, device="cuda"):
 
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, base: np.ndarray = None,
                  what: str = "", roundings: int = 1):
-    """The benchmark spec gate, plus a tighter element-wise gate derived from the
+    """The normwise gate above, plus a tighter element-wise gate derived from the
     arithmetic: each output rounding costs at most half an ulp (<= 2^-8 |y|
     for bf16, counted `roundings` times for repeated in-place updates, whose
     intermediate values lie between y_base and y) plus fp32 accumulation
