@@ -135,6 +135,40 @@ __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3)
     }
 }
 
+// Pipelined bf16 expand: unit = (tile, run of gm.tpw 128-column tiles of one
+// slice); see expand_pipe_bf16.
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_expand_pipe(
+    LinearArgs a, GroupMap gm, const float* __restrict__ S, uint16_t* __restrict__ y, int64_t ldy,
+    int units) {
+    __shared__ int s_in[kRowTile], s_out[kRowTile];
+    const int u = (int)blockIdx.x;
+    if (u >= units) return;
+    const int tile = u / gm.n_groups;
+    const int g = u % gm.n_groups;
+    const TileView v = tile_view(a, tile, false);
+    if (v.seg < 0 || v.rp == 0) return;
+    if (threadIdx.x < kRowTile) {
+        s_in[threadIdx.x] = (int)threadIdx.x < v.n ? v.pbeg + (int)threadIdx.x : -1;
+        s_out[threadIdx.x] = v.row;
+    }
+    __syncthreads();
+    int sl = 0;
+    while (sl + 1 < a.n_sl && g >= gm.group_start[sl + 1]) ++sl;
+    const int64_t nb = a.slice_off[sl] + (int64_t)(g - gm.group_start[sl]) * gm.tpw * kPCols;
+    const int n_begin = (int)nb;
+    const int n_end = (int)min(nb + (int64_t)gm.tpw * kPCols, a.slice_off[sl + 1]);
+    const RowSet rs{v.n, kRowTile, s_in, s_out};
+    // the rank and the B block are the same for every lane (buffer resources
+    // are built from scalar registers)
+    const int rp = __builtin_amdgcn_readfirstlane(v.rp);
+    const int64_t off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v.off >> 32)) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane((int)v.off));
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(a.B) + off;
+    __shared__ uint4 lds[kPipeLds / 16];
+    expand_pipe_bf16(rs, v.n, S, a.cols, sl * a.r_max, B, (int)a.slice_off[a.n_sl], rp, n_begin,
+                     n_end, y, ldy, lds);
+}
+
 // ---------------------------------------------------------------------------
 // embedding lookup (SGLang "LoRA Layers" page, the embedding's A side):
 // S[p][j] = A_i[j, t] for the token t at sorted position p, read from the
@@ -211,15 +245,15 @@ hipError_t launch_shrink(const LinearArgs& a, const void* x, int64_t ldx, float*
 
 // One 256-column tile per workgroup: a workgroup walks its tiles one after
 // another without overlapping them, so spreading tiles over more workgroups
-// (three resident per CU) hides more latency.
-static GroupMap make_group_map(const LinearArgs& a) {
-    const int tpw = 1;
+// (three resident per CU) hides more latency.  The pipelined expand takes
+// runs of `tpw` 128-column tiles.
+static GroupMap make_group_map(const LinearArgs& a, int tpw = 1, int tile_cols = kNTile) {
     GroupMap gm{};
     gm.tpw = tpw;
     int g = 0;
     for (int s = 0; s < a.n_sl; ++s) {
         gm.group_start[s] = g;
-        const int t = (int)((a.slice_off[s + 1] - a.slice_off[s] + kNTile - 1) / kNTile);
+        const int t = (int)((a.slice_off[s + 1] - a.slice_off[s] + tile_cols - 1) / tile_cols);
         g += (t + tpw - 1) / tpw;
     }
     gm.group_start[a.n_sl] = g;
@@ -239,8 +273,30 @@ hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, f
     return hipGetLastError();
 }
 
+// The pipelined bf16 expand addresses y through a buffer resource with
+// 32-bit byte offsets from the first column of a run, so it serves outputs
+// whose rows span less than 2 GiB (M * ldy * 2 bytes); larger ones take the
+// one-tile-per-workgroup kernel.  Its runs are as short as keeps every unit
+// resident at once (three workgroups per CU on 256 CUs): a second, partial
+// round of workgroups costs more than shorter pipelines save (2048-token
+// prefill: 29.4 us for the delta kernels with runs of 2 tiles against 30.9
+// us unpipelined; stacked QKV 24.3 against 26.1; stacked gate/up, runs of
+// 6, 39.4 against 44.2, where runs of 5 (920 units) took 43.6).
+constexpr int kResidentExpandUnits = 3 * 256;
+
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st) {
+    if (a.dtype == LORA_BF16 && (int64_t)a.M * ldy * 2 <= 0x7fffffff) {
+        const int budget = max(1, kResidentExpandUnits / max(1, a.max_tiles));   // runs per tile
+        const int tiles = make_group_map(a, 1, kPCols).n_groups;                  // 128-column tiles
+        int t = (tiles + budget - 1) / budget;
+        GroupMap gp = make_group_map(a, t, kPCols);
+        while (gp.n_groups > budget && gp.n_groups > a.n_sl) gp = make_group_map(a, ++t, kPCols);
+        const int units = a.max_tiles * gp.n_groups;
+        hipLaunchKernelGGL(k_expand_pipe, dim3(grid_of(units)), dim3(kTileThreads), 0, st, a, gp, S,
+                           reinterpret_cast<uint16_t*>(y), ldy, units);
+        return hipGetLastError();
+    }
     const GroupMap gm = make_group_map(a);
     const int units = a.max_tiles * gm.n_groups;
     if (a.dtype == LORA_BF16) {

@@ -536,6 +536,208 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer access (gfx9 buffer resource, stride 0): an access at a byte
+// offset at or past the resource's size reads zeros and writes nothing, so
+// rows and columns outside a tile need neither a branch nor a mask.  With
+// every load and store of a loop issued unconditionally the compiler's
+// memory counter waits are exact: waiting for one load does not wait for the
+// stores and loads issued after it.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_vt __attribute__((ext_vector_type(4)));
+constexpr uint32_t kBufOff = 0x80000000u;         // an offset past every resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_vt v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// non-temporal (the cache policy's nt bit)
+__device__ __forceinline__ void buf_st16_nt(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_vt w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 2);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined expand over a run of 64-row x 128-column tiles of one row tile:
+// S is staged once for the whole run, and while tile k's products are folded
+// into LDS and written back, tile k+1's y values and B operands are already
+// on their way into registers, so a workgroup's loads, matrix work and stores
+// overlap instead of running as three phases one after another.  The y tiles
+// alternate between two LDS buffers (a buffer is refilled two tiles after its
+// write-back read it out, with two barriers in between).
+//   thread t: y rows t/16 + 16 i (i = 0..3), 16-byte chunk t % 16 of the tile
+//   wave w:   columns 32w .. 32w+31 of the tile (two 16-column blocks)
+// y and B go through buffer resources: y based at y_tile0 (byte offsets of
+// the rows below 2^31, checked by the launcher), B at the adapter's block of
+// nb_rows x rp values.
+// ---------------------------------------------------------------------------
+constexpr int kPCols = 128;
+constexpr int kPRowChunks = kPCols / 8;                              // 16
+constexpr int kPipeLds = 2 * 64 * kPCols * 2 + 2 * 64 * kSLds * 2;   // bytes
+
+__device__ __forceinline__ int ppos(int r, int q) { return r * kPRowChunks + (q ^ (r & 15)); }
+
+__device__ __forceinline__ void expand_pipe_bf16(const RowSet& rs, int rows,
+                                                 const float* __restrict__ S, int sld, int sc0,
+                                                 const uint16_t* __restrict__ B, int nb_rows,
+                                                 int rp, int n_begin, int n_end,
+                                                 uint16_t* __restrict__ y, int64_t ldy_,
+                                                 uint4* __restrict__ lds) {
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int lr = lane % 16;
+    const int lq = lane / 16;
+    const int nsteps = (rp + 31) / 32;
+    uint4* ybuf = lds;                                           // [2][64 * kPRowChunks]
+    uint16_t* sHi = reinterpret_cast<uint16_t*>(lds + 2 * 64 * kPRowChunks);
+    uint16_t* sLo = sHi + 64 * kSLds;
+    // S rows first (thread t: row t / 4, rank positions 16 (t % 4) .. +16)
+    const int srow = tid / 4, sqt = tid % 4;
+    float4 sv[4];
+    {
+        const int sr = srow < rows ? rs.in_row[srow] : -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = sqt * 16 + e * 4;
+            sv[e] = ldf4_if(S + (int64_t)sr * sld + sc0 + j, sr >= 0 && j < rp, S);
+        }
+    }
+    const int wq = tid % 16;
+    const __amdgpu_buffer_rsrc_t yr = buf_rsrc(y + n_begin, 0x7fffffffu);
+    const __amdgpu_buffer_rsrc_t br = buf_rsrc(B, (uint32_t)nb_rows * (uint32_t)rp * 2u);
+    uint32_t yoff[4];                                             // row byte offsets, kBufOff if none
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = tid / 16 + 16 * i;
+        const int row = r < rows ? rs.out_row[r] : -1;
+        yoff[i] = row >= 0 ? (uint32_t)((int64_t)row * ldy_ * 2) : kBufOff;
+    }
+    // the loads of the tile at column n0 (none past n_end)
+    auto load_y = [&](int n0, uint4 (&yv)[4]) {
+        const int nch = (min(n0 + kPCols, n_end) - n0) / 8;
+        const uint32_t c = (uint32_t)(n0 - n_begin) * 2u + (uint32_t)wq * 16u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yv[i] = buf_ld16(yr, wq < nch ? yoff[i] + c : kBufOff);
+    };
+    auto load_b = [&](int n0, uint4 (&bv)[2][2]) {
+        const int n1 = min(n0 + kPCols, n_end);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int n = min(n0 + wave * 32 + nb * 16 + lr, n1 - 1);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int j = st * 32 + lq * 8;
+                // rank positions past rp read zeros (their S values are zero
+                // too, and 0 * NaN would not be)
+                bv[nb][st] = buf_ld16(br, (j < rp && n0 < n_end) ? (uint32_t)(n * rp + j) * 2u
+                                                                  : kBufOff);
+            }
+        }
+    };
+    uint4 yv[4], bA[2][2], bB[2][2];
+    load_y(n_begin, yv);
+    load_b(n_begin, bA);
+    // S split into bf16 hi / lo in LDS, zero past rp
+    {
+        uint32_t h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v[4] = {sv[e].x, sv[e].y, sv[e].z, sv[e].w};
+#pragma unroll
+            for (int q = 0; q < 4; q += 2) {
+                const uint32_t h0 = f32_to_bf16(v[q]), h1 = f32_to_bf16(v[q + 1]);
+                h[e * 2 + q / 2] = h0 | (h1 << 16);
+                l[e * 2 + q / 2] = f32_to_bf16(v[q] - bf16_to_f32(h0)) |
+                                   (f32_to_bf16(v[q + 1] - bf16_to_f32(h1)) << 16);
+            }
+        }
+        uint4* hp = reinterpret_cast<uint4*>(sHi + srow * kSLds + sqt * 16);
+        uint4* lp = reinterpret_cast<uint4*>(sLo + srow * kSLds + sqt * 16);
+        hp[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        hp[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        lp[0] = make_uint4(l[0], l[1], l[2], l[3]);
+        lp[1] = make_uint4(l[4], l[5], l[6], l[7]);
+    }
+    // one tile: its y values (in yv) into LDS buffer `buf`, the next tile's
+    // loads issued (y into the freed yv, B into bn; past the run they read
+    // nothing), products folded in with bc, write-back
+    auto tile = [&](int n0, int buf, const uint4 (&bc)[2][2], uint4 (&bn)[2][2]) {
+        const int n1 = min(n0 + kPCols, n_end);
+        const int nch = (n1 - n0) / 8;
+        uint4* yt = ybuf + buf * (64 * kPRowChunks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yt[ppos(tid / 16 + 16 * i, wq)] = yv[i];
+        load_y(n0 + kPCols, yv);
+        load_b(n0 + kPCols, bn);
+        __syncthreads();
+        const int cw = wave * 32;
+        if (n0 + cw < n1) {
+            uint4 shi[2], slo[2], nhi[2], nlo[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                shi[st] = ld16(sHi + lr * kSLds + st * 32 + lq * 8);
+                slo[st] = ld16(sLo + lr * kSLds + st * 32 + lq * 8);
+            }
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                if (rg * 16 >= rows) break;
+                if (rg < 3) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        nhi[st] = ld16(sHi + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
+                        nlo[st] = ld16(sLo + ((rg + 1) * 16 + lr) * kSLds + st * 32 + lq * 8);
+                    }
+                }
+                const int r = rg * 16 + lr;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        if (st < nsteps) {
+                            acc = mfma_bf16(bc[nb][st], shi[st], acc);
+                            acc = mfma_bf16(bc[nb][st], slo[st], acc);
+                        }
+                    }
+                    // acc[e]: tile column c + e, row r
+                    const int c = cw + nb * 16 + lq * 4;
+                    uint2* yp = reinterpret_cast<uint2*>(yt + ppos(r, c / 8)) + ((c / 4) & 1);
+                    const uint2 old = *yp;
+                    uint2 nv;
+                    nv.x = f32_to_bf16(__uint_as_float(old.x << 16) + acc[0]) |
+                           (f32_to_bf16(__uint_as_float(old.x & 0xffff0000u) + acc[1]) << 16);
+                    nv.y = f32_to_bf16(__uint_as_float(old.y << 16) + acc[2]) |
+                           (f32_to_bf16(__uint_as_float(old.y & 0xffff0000u) + acc[3]) << 16);
+                    *yp = nv;
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    shi[st] = nhi[st];
+                    slo[st] = nlo[st];
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t c = (uint32_t)(n0 - n_begin) * 2u + (uint32_t)wq * 16u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            buf_st16_nt(yt[ppos(tid / 16 + 16 * i, wq)], yr, wq < nch ? yoff[i] + c : kBufOff);
+    };
+    // two tiles per trip so the B register sets alternate without copies
+    for (int n0 = n_begin;;) {
+        tile(n0, 0, bA, bB);
+        n0 += kPCols;
+        if (n0 >= n_end) break;
+        tile(n0, 1, bB, bA);
+        n0 += kPCols;
+        if (n0 >= n_end) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // plain vector-ALU versions (any storage type); used for fp32 storage
 // ---------------------------------------------------------------------------
 // Wide expand tile for sparse row blocks (MoE): up to 32 rows (two groups of

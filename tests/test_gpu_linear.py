@@ -224,6 +224,60 @@ def test_expand_from_oracle_S(ml):
     assert_close(to_f64(y), ref, case.dtype, case.y_base.values, "expand")
 
 
+def run_with(ml, case, seg_cap=None, y_stride=None, sentinel=-7.0):
+    """lora_shrink_expand_add with a segment table of capacity seg_cap tokens
+    (more tiles than the batch needs: longer runs of output tiles per
+    workgroup in the bf16 expand) and y as the first N columns of a
+    [M, y_stride] buffer filled with a sentinel.  Returns y and the columns
+    past N (which must keep the sentinel)."""
+    table = table_for(case)
+    seg = ml.Segments(seg_cap or case.M, case.L)
+    ml.lora_build_segments(torch.from_numpy(case.ids).cuda(), seg)
+    N = table.N
+    dt = torch.bfloat16 if case.dtype == W.BF16 else torch.float32
+    if y_stride is None:
+        y = to_dev(case.y_base)
+        pad = None
+    else:
+        big = torch.full((case.M, y_stride), sentinel, dtype=dt, device="cuda")
+        big[:, :N] = to_dev(case.y_base)
+        y, pad = big[:, :N], big[:, N:N + 64]
+    ws = ml.Workspace.for_table(table, case.M)
+    ml.lora_shrink_expand_add(table, to_dev(case.x), seg, y, ws)
+    torch.cuda.synchronize()
+    assert ml.lora_read_device_error(ws.buf) == 0
+    return to_f64(y), (None if pad is None else pad.float().cpu().numpy())
+
+
+@pytest.mark.parametrize("seg_cap", [20000, 60000])
+def test_expand_long_tile_runs(ml, seg_cap):
+    """Slices of 5 and 4 128-column tiles, each ending in a ragged tile (24
+    and 8 columns): with a large schedule capacity the expand's units take
+    runs of several tiles (one run per slice at 60000), odd and even
+    lengths, so the two LDS buffers and register sets alternate across a
+    run and its last tile loads nothing further."""
+    case = W.random_linear(31, 150, 264, [536, 392], [16, 64, 32, 0, 48], W.BF16)
+    log(f"long runs cap={seg_cap}")
+    got, _ = run_with(ml, case, seg_cap=seg_cap)
+    ref = oracle_y(case)
+    keep = ~O.delta_rows(case.ids, case.ranks)
+    assert np.array_equal(got[keep], case.y_base.values[keep])
+    assert_close(got, ref, case.dtype, case.y_base.values, "long runs")
+
+
+@pytest.mark.parametrize("stride", [4096, 1 << 24])
+def test_expand_strided_y(ml, stride):
+    """y inside a wider buffer: rows 4096 columns apart (the pipelined bf16
+    expand) and 2^24 columns apart, 70 rows spanning 2.3 GB, past the 2 GiB
+    that its 32-bit buffer offsets reach (the one-tile-per-workgroup
+    expand).  The columns past N keep their sentinel."""
+    case = W.random_linear(32, 70, 200, [328], [16, 32, 64], W.BF16, p_none=0.1)
+    log(f"strided y stride={stride}")
+    got, pad = run_with(ml, case, y_stride=stride)
+    assert np.all(pad == -7.0), "columns past N were written"
+    assert_close(got, oracle_y(case), case.dtype, case.y_base.values, f"stride {stride}")
+
+
 def test_full_size_table_form_repeated(ml):
     """Full decode workload through the table form (lora_shrink_expand_add on
     a prebuilt table), 8 back-to-back calls on one workspace; every row is

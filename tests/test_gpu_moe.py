@@ -84,6 +84,11 @@ MOE_CASES = [
     # take two passes of 32 rows, the 64 x 256 tiles all their rows
     ("wide_full_blocks", lambda: W.moe_case(10, M=160, H=264, I=4104, E=2, topk=2, L=1, rank=16,
                                             block_size_m=64)),
+    # the largest block size (256 rows): eight 32-row passes of the wide
+    # expand, four 64-row passes of the narrow one, sixteen 16-row groups
+    # in the shrink part; rank 32
+    ("max_block_256", lambda: W.moe_case(11, M=300, H=264, I=4104, E=2, topk=2, L=1, rank=32,
+                                         block_size_m=256)),
     # experts_shared_outer_loras: gate_up A and down B with one expert slot
     ("cfg5_shared_outer", lambda: W.moe_case(0, shared_outer=True)),
     ("shared_outer_fp32", lambda: W.moe_case(8, M=40, H=128, I=96, E=4, topk=2, L=3, rank=16,
