@@ -93,6 +93,30 @@ __device__ __forceinline__ float4 ldf4_if(const float* p, bool ok, const float* 
 }
 
 // ----------------------------------------------------------------------------
+// Raw buffer access (gfx9 buffer resource, stride 0): an access at a byte
+// offset at or past the resource's size reads zeros and writes nothing, so
+// rows and columns outside a tile need neither a branch nor a mask.  With
+// every load and store of a loop issued unconditionally the compiler's
+// memory counter waits are exact: waiting for one load does not wait for the
+// stores and loads issued after it.
+// ----------------------------------------------------------------------------
+typedef unsigned int u32x4_vt __attribute__((ext_vector_type(4)));
+constexpr uint32_t kBufOff = 0x80000000u;         // an offset past every resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_vt v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// non-temporal (the cache policy's nt bit)
+__device__ __forceinline__ void buf_st16_nt(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_vt w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 2);
+}
+
+// ----------------------------------------------------------------------------
 // bf16 MFMA, 16 x 16 output, K = 32 (v_mfma_f32_16x16x32_bf16).  Lane l
 // supplies row (l % 16) of the first operand and column (l % 16) of the
 // second, eight consecutive K values starting at 8 * (l / 16) for both; it
