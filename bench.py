@@ -624,7 +624,7 @@ def main():
     if want("prefill"):
         cases["prefill_bf16"] = (W.prefill_bf16(0), 64)
         results["prefill_bf16"] = bench_linear(cases["prefill_bf16"][0], args.steps, args.warmup,
-                                               "k_shrink_dense + k_reduce_partials + k_expand_dense")
+                                               "k_shrink_dense + k_reduce_partials + k_expand_pipe")
     if want("qkv"):
         cases["stacked_qkv_bf16"] = (W.stacked_bf16("qkv", 0), 64)
         results["stacked_qkv_bf16"] = bench_linear(cases["stacked_qkv_bf16"][0], args.steps,
