@@ -110,6 +110,12 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
     const u32x4_vt v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint16_t buf_ld_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st_u16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
 // non-temporal (the cache policy's nt bit)
 __device__ __forceinline__ void buf_st16_nt(const uint4& v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4_vt w = {v.x, v.y, v.z, v.w};

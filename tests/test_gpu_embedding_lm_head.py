@@ -178,6 +178,33 @@ def test_lm_head_consumers_over_tile_groups(ml, dtype):
     assert_close(got, oracle_y(case), case.dtype, case.y_base.values, case.name)
 
 
+@pytest.mark.parametrize("form", ["ids", "table"])
+def test_lm_head_many_tokens_per_adapter(ml, form):
+    """64 tokens over three adapters (ranks 16, 64, 48: about 20 tokens
+    each, past the 16 token rows of the matrix-core consumers' first block
+    and the 4 of the dot-product consumers' registers) at 150008 columns,
+    so each consumer walks two tiles pipelined and the last tile is
+    ragged; through the ids form and the table form."""
+    case = W.random_linear(28, 64, 512, [150008], [16, 64, 48], W.BF16, p_none=0.05)
+    log(f"lm_head many tokens {form} M={case.M} K={case.K} N={case.N}")
+    table = table_for(case)
+    ids = torch.from_numpy(case.ids).cuda()
+    y = to_dev(case.y_base)
+    seg = ml.Segments(case.M, case.L)
+    ws = ml.Workspace.for_table(table, case.M)
+    if form == "ids":
+        ml.lora_fused_decode(table, ids, to_dev(case.x), y, ws, seg=seg)
+    else:
+        ml.lora_build_segments(ids, seg)
+        ml.lora_shrink_expand_add(table, to_dev(case.x), seg, y, ws)
+    torch.cuda.synchronize()
+    assert ml.lora_read_device_error(ws.buf) == 0
+    got = to_f64(y)
+    keep = ~O.delta_rows(case.ids, case.ranks)
+    assert np.array_equal(got[keep], case.y_base.values[keep])
+    assert_close(got, oracle_y(case), case.dtype, case.y_base.values, case.name)
+
+
 def test_lm_head_larger_batch(ml):
     """More than 64 rows (the segmented shrink + expand) at vocabulary width."""
     case = W.random_linear(26, 160, 1024, [32000], [16, 64, 32, 0, 48], W.BF16)
