@@ -740,7 +740,8 @@ __device__ __forceinline__ void dec_consume_mfma(const DecodeParams& p, SegView&
 // register sets take what one 256-column set did.  Tokens past the first 16
 // (MFMA form) or kTokGroup (dot-product form) of a segment take ordinary
 // loads and stores after the pipelined part.  Requires y rows within 2 GiB
-// of p.y (M * ldy * 2 bytes, checked by the launcher).
+// of p.y (M * ldy * 2 bytes) and B blocks under 2 GiB (checked by the
+// launcher).
 struct DecBuf {
     __amdgpu_buffer_rsrc_t b, y;
     int rp, ldy;
@@ -1180,7 +1181,8 @@ hipError_t launch_decode_fused(const LinearArgs& a, const int32_t* ids, const in
     // three tiles per consumer: 18.2 against 20.7 µs); one-tile consumers keep
     // the branchy form, which issues only the stores of real tokens (decode:
     // 8.95 against 9.5 µs pipelined).
-    p.pipe = (p.G > 1 && (int64_t)a.M * ldy * 2 <= 0x7fffffff) ? 1 : 0;
+    p.pipe = (p.G > 1 && (int64_t)a.M * ldy * 2 <= 0x7fffffff &&
+              a.slice_off[a.n_sl] * a.r_max * 2 <= 0x7fffffff) ? 1 : 0;
     return launch_decode(p, (unsigned)(p.grid1 + a.s_max * p.n_groups + p.writer), st);
 }
 

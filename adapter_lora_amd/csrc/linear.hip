@@ -273,9 +273,9 @@ hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, f
     return hipGetLastError();
 }
 
-// The pipelined bf16 expand addresses y through a buffer resource with
-// 32-bit byte offsets from the first column of a run, so it serves outputs
-// whose rows span less than 2 GiB (M * ldy * 2 bytes); larger ones take the
+// The pipelined bf16 expand addresses y and B through buffer resources with
+// 32-bit byte offsets, so it serves outputs whose rows span less than 2 GiB
+// (M * ldy * 2 bytes) and B blocks under 2 GiB; larger ones take the
 // one-tile-per-workgroup kernel.  Its runs are as short as keeps every unit
 // resident at once (three workgroups per CU on 256 CUs): a second, partial
 // round of workgroups costs more than shorter pipelines save (2048-token
@@ -286,7 +286,8 @@ constexpr int kResidentExpandUnits = 3 * 256;
 
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st) {
-    if (a.dtype == LORA_BF16 && (int64_t)a.M * ldy * 2 <= 0x7fffffff) {
+    if (a.dtype == LORA_BF16 && (int64_t)a.M * ldy * 2 <= 0x7fffffff &&
+        a.slice_off[a.n_sl] * a.r_max * 2 <= 0x7fffffff) {
         const int budget = max(1, kResidentExpandUnits / max(1, a.max_tiles));   // runs per tile
         const int tiles = make_group_map(a, 1, kPCols).n_groups;                  // 128-column tiles
         int t = (tiles + budget - 1) / budget;
