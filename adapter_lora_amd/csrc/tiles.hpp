@@ -545,9 +545,9 @@ __device__ __forceinline__ void expand_rows_bf16(const RowSet& rs, const float* 
 // write-back read it out, with two barriers in between).
 //   thread t: y rows t/16 + 16 i (i = 0..3), 16-byte chunk t % 16 of the tile
 //   wave w:   columns 32w .. 32w+31 of the tile (two 16-column blocks)
-// y and B go through buffer resources: y based at y_tile0 (byte offsets of
-// the rows below 2^31, checked by the launcher), B at the adapter's block of
-// nb_rows x rp values.
+// y and B go through buffer resources: y based at the run's first column
+// (row byte offsets below 2^31), B at the adapter's block of nb_rows x rp
+// values (under 2 GiB); the launcher checks both bounds.
 // ---------------------------------------------------------------------------
 constexpr int kPCols = 128;
 constexpr int kPRowChunks = kPCols / 8;                              // 16
