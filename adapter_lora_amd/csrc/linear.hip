@@ -278,17 +278,24 @@ hipError_t launch_embedding_shrink(const LinearArgs& a, const int32_t* tokens, f
 // (M * ldy * 2 bytes) and B blocks under 2 GiB; larger ones take the
 // one-tile-per-workgroup kernel.  Its runs are as short as keeps every unit
 // resident at once (three workgroups per CU on 256 CUs): a second, partial
-// round of workgroups costs more than shorter pipelines save (2048-token
-// prefill: 29.4 us for the delta kernels with runs of 2 tiles against 30.9
-// us unpipelined; stacked QKV 24.3 against 26.1; stacked gate/up, runs of
-// 6, 39.4 against 44.2, where runs of 5 (920 units) took 43.6).
+// round of workgroups costs more than shorter pipelines save (stacked QKV:
+// 24.3 us for the delta kernels with runs of 2 tiles against 26.1 us
+// unpipelined; stacked gate/up, runs of 6, 39.4 against 44.2, where runs of
+// 5, 920 units, took 43.6).  When the schedule's tiles are nearly full (at
+// least 48 rows on average) a unit carries enough traffic that two per CU
+// keep the memory system as busy, and longer runs win (2048-token prefill:
+// runs of 3, 440 units, 28.6 us against 29.4 with runs of 2 and 30.9
+// unpipelined).
 constexpr int kResidentExpandUnits = 3 * 256;
+constexpr int kFullTileExpandUnits = 2 * 256;
 
 hipError_t launch_expand(const LinearArgs& a, const float* S, void* y, int64_t ldy,
                          hipStream_t st) {
     if (a.dtype == LORA_BF16 && (int64_t)a.M * ldy * 2 <= 0x7fffffff &&
         a.slice_off[a.n_sl] * a.r_max * 2 <= 0x7fffffff) {
-        const int budget = max(1, kResidentExpandUnits / max(1, a.max_tiles));   // runs per tile
+        const bool full = (int64_t)a.M >= (int64_t)48 * a.max_tiles;
+        const int budget = max(1, (full ? kFullTileExpandUnits : kResidentExpandUnits) /
+                                      max(1, a.max_tiles));                      // runs per tile
         const int tiles = make_group_map(a, 1, kPCols).n_groups;                  // 128-column tiles
         int t = (tiles + budget - 1) / budget;
         GroupMap gp = make_group_map(a, t, kPCols);
